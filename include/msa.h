@@ -1,0 +1,260 @@
+/*
+ * msa.h -- C ABI of libmsa.so, the MI355X (gfx950) hot path of Memory Sparse
+ * Attention (MSA).
+ *
+ * The method (sources are web pages; each call cites the passage that
+ * defines what it computes):
+ *   - "MSA架构：突破大模型记忆瓶颈的稀疏注意力技术" (intelliparadigm.com),
+ *     sections 2.1 and 3.1: a router picks documents by cosine top-k over
+ *     routing keys made by 256-token chunk-mean pooling.
+ *   - "MSA" card (robocikowo.com), sections "Komponenty", "Pułapki
+ *     implementacyjne", "Równoległość": the MSA layer appends the top-k
+ *     documents' K/V to the local context; document-wise RoPE restarts
+ *     positions at every document, global RoPE with an offset covers the
+ *     active context; routing keys live in GPU memory and full K/V may live
+ *     in host memory (pinned, copied asynchronously); top-k and the
+ *     following K/V fetch are sequential within a decode step; Memory
+ *     Interleave alternates document selection and context expansion.
+ *   - the MLA/CSA attention article (mlqm.cn), section 6.2: 1/sqrt(d) scale.
+ *
+ * Conventions for every call
+ *   - Every pointer is caller-owned.  "device" pointers are HIP device
+ *     memory on the current device; "host" pointers are ordinary CPU memory.
+ *     The library allocates only in msa_bank_create (small per-bank tables)
+ *     and frees them in msa_bank_destroy.  No hot-path call allocates.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls are asynchronous on that stream unless stated; results are valid
+ *     once the stream has completed the work.
+ *   - Return value: msa_status.  Argument and shape errors are detected on
+ *     the host before anything is launched (MSA_EINVAL / MSA_EUNSUPPORTED,
+ *     nothing written).  A failed HIP launch or copy returns MSA_EHIP.
+ *     msa_last_error() gives a human-readable reason for the last failure
+ *     on the calling thread.
+ *   - Head size d and routing-key size d_r are 128.  Routing chunks are 256
+ *     tokens; every document length is a positive multiple of 256.
+ *   - dtype: MSA_F32 or MSA_BF16, the storage type of routing keys, document
+ *     K/V, local K/V and attention queries.  Router queries and attention
+ *     outputs are always float32.  Arithmetic accumulates in float32 (the
+ *     routing-key pooling and norms in float64).
+ *   - A bank handle is immutable after msa_bank_create; calls on one bank may
+ *     run concurrently on different streams if their workspaces differ.
+ *
+ * Layouts (row-major; the last index is contiguous)
+ *   Routing keys      kr       [h_r][C][d_r]        (C = total chunks)
+ *   Key norms         inv_norm [h_r][C] float32     (1/||key||, 0 for a zero key)
+ *   Document K store  per document n at token offset kv_off[n]:
+ *                     k_store + kv_off[n]*h_kv*d  ->  [h_kv][L_n][d]
+ *                     (rotated at document-local positions 0..L_n-1)
+ *   Document V store  v_store + kv_off[n]*h_kv*d  ->  [h_kv][d][L_n]
+ *                     (d-major: one row of L_n tokens per channel)
+ *   Local K           [n_seq][h_kv][L][d]           (rotated at pos0 + j)
+ *   Local V           [n_seq][h_kv][d][loc_stride]  (loc_stride >= L, % 8 == 0)
+ *   Raw per-token inputs (what a model emits): [tokens][heads][128].
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_EINVAL = 1,        /* bad argument, shape or pointer */
+  MSA_ENOMEM = 2,        /* workspace/staging too small, or bank tables could not be allocated */
+  MSA_EHIP = 3,          /* a HIP launch, copy or synchronisation failed */
+  MSA_EUNSUPPORTED = 4   /* valid request outside what this build supports */
+} msa_status;
+
+typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype;
+typedef enum { MSA_KV_DEVICE = 0, MSA_KV_HOST = 1 } msa_kv_loc;
+typedef enum { MSA_DECODE = 0, MSA_PREFILL = 1 } msa_mode;
+
+typedef struct msa_bank msa_bank;
+
+/* Description of a memory bank ("MSA" card, robocikowo.com, "Komponenty":
+ * the KV-cache memory store keeps the routing keys Kr in GPU memory and the
+ * full K/V of every document, possibly in CPU memory). */
+typedef struct {
+  msa_dtype dtype;
+  int32_t n_docs;            /* N >= 1 */
+  const int64_t* doc_len;    /* host [N]: tokens per document, > 0, % 256 == 0 */
+  const int64_t* kv_off;     /* host [N] or NULL: token offset of each document in the
+                                K/V stores (NULL = documents packed in order).  Several
+                                documents may share storage. */
+  int64_t kv_tokens;         /* tokens the K/V stores hold: >= max(kv_off[n] + doc_len[n]) */
+  int32_t h_r;               /* router heads, 1..16 */
+  int32_t d_r;               /* 128 */
+  int32_t h_kv;              /* KV heads, 1..64 */
+  int32_t d;                 /* 128 */
+  double rope_base;          /* RoPE base (10000) */
+  msa_kv_loc kv_loc;         /* where k_store / v_store live */
+  void* kr;                  /* device [h_r][C][d_r], dtype */
+  float* inv_norm;           /* device [h_r][C] */
+  void* k_store;             /* device or pinned host, kv_tokens*h_kv*d elements */
+  void* v_store;             /* device or pinned host, kv_tokens*h_kv*d elements */
+} msa_bank_desc;
+
+typedef struct {
+  int64_t n_chunks;          /* C */
+  int64_t n_tokens;          /* sum of doc_len */
+  int64_t max_doc_len;
+  int32_t n_docs;
+  int32_t n_pieces;          /* routing partial slots per (query, head) */
+} msa_bank_info;
+
+/* Per-call knobs of the attention kernels. */
+typedef struct {
+  int32_t mode;              /* MSA_DECODE or MSA_PREFILL */
+  int32_t n_q;               /* decode: queries B; prefill: query tokens L_q */
+  int32_t h_q;               /* query heads, a multiple of h_kv with h_q/h_kv in {1,2,4,8} */
+  const void* q;             /* device [n_q][h_q][d], dtype, before RoPE */
+  int32_t q_pos;             /* decode: position of every query;
+                                prefill: position of query 0 (query i at q_pos + i) */
+  const int32_t* ids;        /* device [n_groups][k]: selected document ids (or source ids
+                                when src_len is set); ids outside [0, N) (resp. [0, n_src))
+                                are skipped, so -1 marks an empty slot.
+                                decode: n_groups = n_q; prefill: n_groups = n_q / block */
+  int32_t k;                 /* documents per group, >= 0 */
+  int32_t block;             /* prefill: queries per routing group (n_q % block == 0) */
+  const void* k_loc;         /* device local K [n_seq][h_kv][L_loc][d] (prepared) */
+  const void* v_loc;         /* device local V [n_seq][h_kv][d][loc_stride] (prepared) */
+  int32_t L_loc;             /* local tokens, >= 0 (decode: n_seq = n_q; prefill: n_seq = 1) */
+  int32_t loc_stride;        /* >= L_loc, % 8 == 0 */
+  float* out;                /* device [n_q][h_q][d] float32 */
+  void* ws;                  /* device workspace */
+  size_t ws_bytes;
+  int32_t splits;            /* decode: work splits per (query, KV head); 0 = automatic */
+  /* Optional source override (host-resident banks copy selected documents
+   * into a staging area; ids then index this table).  All NULL = the bank. */
+  const void* src_k;         /* device K store of the sources, layout as the bank's */
+  const void* src_v;         /* device V store of the sources */
+  const int64_t* src_off;    /* device [n_src] token offsets */
+  const int32_t* src_len;    /* device [n_src] token lengths */
+  int32_t n_src;             /* entries in src_off / src_len */
+} msa_attend_args;
+
+/* One step of the path: route -> top-k -> gather -> attend, repeated for
+ * `hops` hops (Memory Interleave). */
+typedef struct {
+  int32_t mode;              /* MSA_DECODE or MSA_PREFILL */
+  int32_t n_q;               /* decode: B; prefill: L_q */
+  int32_t h_q;
+  int32_t k;                 /* top-k documents, 1 <= k <= N */
+  const void* q;             /* device [n_q][h_q][d] dtype, before RoPE */
+  int32_t q_pos;             /* as in msa_attend_args */
+  const float* q_route;      /* decode: device [n_q][h_r][d_r] float32, hop-1 router query */
+  const void* route_tokens;  /* prefill: device [n_q][h_r][d_r] dtype per-token router vectors */
+  int32_t block;             /* prefill routing block (64) */
+  const void* k_loc;         /* prepared local context, as in msa_attend_args */
+  const void* v_loc;
+  int32_t L_loc;
+  int32_t loc_stride;
+  int32_t hops;              /* >= 1; > 1 needs h_r == 1 and w_proj (decode only) */
+  const float* w_proj;       /* device [d_r][h_q*d] float32: next hop's router query is
+                                w_proj times the concatenated per-head outputs */
+  int32_t exclude_selected;  /* nonzero: documents selected in earlier hops are excluded */
+  uint32_t* exclude;         /* device [n_groups][ceil(N/32)] bit mask of excluded documents
+                                (bit n%32 of word n/32), or NULL.  With exclude_selected the
+                                call ORs each hop's selections into it. */
+  int32_t* ids;              /* device [hops][n_groups][k] */
+  float* scores;             /* device [hops][n_groups][k] */
+  float* out;                /* device [hops][n_q][h_q][d] float32 */
+  void* ws;
+  size_t ws_bytes;
+  void* staging;             /* host banks: device staging for copied documents */
+  size_t staging_bytes;
+  int32_t splits;
+} msa_step_args;
+
+typedef struct {
+  int64_t docs_copied;       /* host banks: distinct documents copied host->device */
+  int64_t bytes_copied;      /* host banks: bytes copied host->device */
+} msa_step_stats;
+
+const char* msa_status_string(int status);
+const char* msa_last_error(void);
+int msa_version(void);
+
+/* Validate `desc`, build the bank's routing tables (document and chunk
+ * offsets, the chunk->document map, RoPE frequencies) and upload them.
+ * Does not touch kr / inv_norm / the K/V stores.  Synchronous. */
+int msa_bank_create(const msa_bank_desc* desc, msa_bank** out);
+int msa_bank_destroy(msa_bank* bank);
+int msa_bank_get_info(const msa_bank* bank, msa_bank_info* info);
+
+/* Offline bank build for documents [doc_begin, doc_end) ("MSA" card,
+ * robocikowo.com, "Pułapki implementacyjne", cold start: encode documents
+ * ahead of time, store routing keys and K/V, pool by chunk means).
+ *   route_vec: device [T_s][h_r][d_r] dtype, the per-token routing vectors of
+ *     those documents in order (T_s = their total length).  Writes kr rows
+ *     as the mean of each 256-token chunk (intelliparadigm.com, section 3.1),
+ *     rounded to dtype, and inv_norm from the rounded keys.  NULL: kr is
+ *     taken as given and only inv_norm of those chunks is computed.
+ *   k_raw, v_raw: device [T_s][h_kv][d] dtype, or both NULL.  K is rotated at
+ *     document-local positions (document-wise RoPE, "MSA" card,
+ *     "Komponenty") and both are written into the device K/V stores in the
+ *     layouts above.  Host-resident stores are not written (MSA_EUNSUPPORTED).
+ */
+int msa_build_bank(const msa_bank* bank, int32_t doc_begin, int32_t doc_end,
+                   const void* route_vec, const void* k_raw, const void* v_raw, void* stream);
+
+/* Local (active) context: rotate raw K at global positions pos0 + j ("MSA"
+ * card, "Pułapki implementacyjne": global RoPE with an offset for the
+ * active context) and lay K and V out for the attention kernels.
+ *   k_raw, v_raw: device [n_seq][L][h_kv][d] dtype.
+ *   k_loc: device [n_seq][h_kv][L][d]; v_loc: device [n_seq][h_kv][d][loc_stride],
+ *   columns L..loc_stride-1 are zero-filled. */
+int msa_prepare_local(const msa_bank* bank, const void* k_raw, const void* v_raw,
+                      int32_t n_seq, int32_t L, int32_t pos0,
+                      void* k_loc, void* v_loc, int32_t loc_stride, void* stream);
+
+/* Workspace bytes msa_route / msa_attend / msa_step need for these sizes.
+ * mode: MSA_DECODE or MSA_PREFILL; n_q, h_q, k as in the args; hops >= 1. */
+size_t msa_workspace_bytes(const msa_bank* bank, int32_t mode, int32_t n_q, int32_t h_q,
+                           int32_t k, int32_t block, int32_t hops, int32_t splits);
+
+/* Staging bytes msa_step needs for a host-resident bank. */
+size_t msa_staging_bytes(const msa_bank* bank, int32_t n_groups, int32_t k);
+
+/* Routing ("MSA" card, "Komponenty", router; intelliparadigm.com, 2.1):
+ *   cos[b,h,c] = q_route[b,h] . kr[h,c] * inv_norm[h,c] / ||q_route[b,h]||
+ *   score[b,n] = mean over h of max over document n's chunks of cos
+ * then the k best documents per query, ordered by score (descending) with
+ * ties to the lower id.  Excluded documents (bit set in `exclude`, may be
+ * NULL) are never chosen; if fewer than k remain, the tail is id -1, score
+ * -inf.
+ *   q_route: device [B][h_r][d_r] float32.  ids: device [B][k] int32;
+ *   scores: device [B][k] float32 (the document scores).  1 <= k <= N. */
+int msa_route(const msa_bank* bank, const float* q_route, int32_t B, int32_t k,
+              const uint32_t* exclude, int32_t* ids, float* scores,
+              void* ws, size_t ws_bytes, void* stream);
+
+/* GQA softmax attention of each query over the union of its selected
+ * documents' K/V (rank order) and the local context ("MSA" card,
+ * "Komponenty", the MSA layer; "Paradygmat wykonania": only the selected
+ * blocks take part), scale 1/sqrt(d) (mlqm.cn article, 6.2).  Query head
+ * hq reads KV head hq / (h_q/h_kv).  Queries are rotated at their global
+ * positions.  Decode: each query sees all L_loc local tokens.  Prefill:
+ * query i of group g = i / block sees group g's documents and local tokens
+ * j <= L_loc - n_q + i (the queries are the last n_q local tokens). */
+int msa_attend(const msa_bank* bank, const msa_attend_args* args, void* stream);
+
+/* Route + top-k + gather + attend for one batch, `hops` times ("MSA" card,
+ * "Równoległość": top-k then K/V fetch, sequential in each decode step;
+ * "Komponenty": Memory Interleave).  Prefill: each block of `block` query
+ * tokens routes with the mean of its router vectors and shares one top-k set.
+ * Host-resident banks: after top-k the ids are read back (the call blocks
+ * once per hop on `stream`), each distinct selected document is copied into
+ * `staging` on `copy_stream` (NULL = `stream`), and attention waits for the
+ * copies.  `stats` (host, may be NULL) receives copy counts. */
+int msa_step(const msa_bank* bank, const msa_step_args* args, void* stream,
+             void* copy_stream, msa_step_stats* stats);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MSA_H */

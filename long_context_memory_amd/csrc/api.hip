@@ -1,0 +1,523 @@
+// C ABI entry points: argument validation, bank tables, workspace layout and
+// the orchestration of msa_step (route -> top-k -> gather -> attend, hops,
+// host-resident banks).  See include/msa.h for the contract of each call.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "msa_internal.h"
+
+namespace msa {
+
+static thread_local std::string g_last_error;
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+namespace {
+
+int fail(int code, const std::string& msg) {
+  set_error(msg);
+  return code;
+}
+
+#define MSA_CHECK_HIP(expr)                                                          \
+  do {                                                                               \
+    hipError_t e_ = (expr);                                                          \
+    if (e_ != hipSuccess)                                                            \
+      return fail(MSA_EHIP, std::string(#expr) + ": " + hipGetErrorString(e_));      \
+  } while (0)
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+// Workspace layout shared by msa_workspace_bytes and the entry points.
+struct WsLayout {
+  size_t piecemax = 0, keys = 0, qroute = 0, qrot = 0, part = 0, srcids = 0, srcoff = 0,
+         srclen = 0, excl = 0, total = 0;
+};
+
+WsLayout ws_layout(const Bank& bk, int mode, int n_q, int h_q, int k, int block, int hops,
+                   int splits) {
+  WsLayout L;
+  const int n_groups = mode == MSA_PREFILL ? n_q / std::max(block, 1) : n_q;
+  const size_t esz = dtype_size(bk.desc.dtype);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  L.piecemax = take((size_t)bk.desc.h_r * bk.n_pieces * n_groups * sizeof(float));
+  L.keys = take((size_t)n_groups * bk.desc.n_docs * sizeof(uint64_t));
+  L.qroute = take((size_t)n_groups * bk.desc.h_r * kD * sizeof(float));
+  L.qrot = take((size_t)n_q * h_q * kD * esz);
+  const int G = std::max(1, h_q / bk.desc.h_kv);
+  L.part = take(decode_partial_floats(n_q, bk.desc.h_kv, G, splits) * sizeof(float));
+  L.srcids = take((size_t)n_groups * k * sizeof(int32_t));
+  L.srcoff = take((size_t)n_groups * k * sizeof(int64_t));
+  L.srclen = take((size_t)n_groups * k * sizeof(int32_t));
+  L.excl = take((size_t)n_groups * ((bk.desc.n_docs + 31) / 32) * sizeof(uint32_t));
+  (void)hops;
+  L.total = off;
+  return L;
+}
+
+int resolve_splits(const Bank& bk, int splits, int n_q, int k, int L_loc) {
+  if (splits > 0) return ((splits + 3) / 4) * 4;
+  return decode_auto_splits(bk, n_q, k, L_loc);
+}
+
+const Bank* as_bank(const msa_bank* b) { return reinterpret_cast<const Bank*>(b); }
+
+int check_attend_common(const Bank& bk, int mode, int n_q, int h_q, int k, int block, int L_loc,
+                        int loc_stride, const void* k_loc, const void* v_loc) {
+  if (mode != MSA_DECODE && mode != MSA_PREFILL) return fail(MSA_EINVAL, "mode");
+  if (n_q < 0) return fail(MSA_EINVAL, "n_q < 0");
+  if (h_q <= 0 || h_q % bk.desc.h_kv) return fail(MSA_EINVAL, "h_q must be a multiple of h_kv");
+  const int G = h_q / bk.desc.h_kv;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(MSA_EUNSUPPORTED, "h_q / h_kv must be 1, 2, 4 or 8");
+  if (k < 0 || k > kMaxK) return fail(MSA_EUNSUPPORTED, "k must be in [0, 64]");
+  if (mode == MSA_PREFILL && (block <= 0 || n_q % block))
+    return fail(MSA_EINVAL, "prefill: n_q must be a positive multiple of block");
+  if (L_loc < 0) return fail(MSA_EINVAL, "L_loc < 0");
+  if (L_loc > 0) {
+    if (!k_loc || !v_loc) return fail(MSA_EINVAL, "local K/V pointers are NULL");
+    if (loc_stride < L_loc || loc_stride % 8) return fail(MSA_EINVAL, "loc_stride");
+  }
+  if (mode == MSA_PREFILL && L_loc < n_q)
+    return fail(MSA_EINVAL, "prefill: the queries are the last n_q local tokens (L_loc >= n_q)");
+  return MSA_OK;
+}
+
+}  // namespace
+}  // namespace msa
+
+using namespace msa;
+
+extern "C" {
+
+const char* msa_status_string(int status) {
+  switch (status) {
+    case MSA_OK: return "ok";
+    case MSA_EINVAL: return "invalid argument";
+    case MSA_ENOMEM: return "not enough memory (workspace, staging or tables)";
+    case MSA_EHIP: return "HIP runtime error";
+    case MSA_EUNSUPPORTED: return "unsupported configuration";
+    default: return "unknown status";
+  }
+}
+
+const char* msa_last_error(void) { return g_last_error.c_str(); }
+
+int msa_version(void) { return 10000; }
+
+int msa_bank_create(const msa_bank_desc* d, msa_bank** out) {
+  if (!d || !out) return fail(MSA_EINVAL, "NULL descriptor or output");
+  *out = nullptr;
+  if (d->dtype != MSA_F32 && d->dtype != MSA_BF16) return fail(MSA_EINVAL, "dtype");
+  if (d->n_docs <= 0 || !d->doc_len) return fail(MSA_EINVAL, "n_docs / doc_len");
+  if (d->d_r != kD || d->d != kD) return fail(MSA_EUNSUPPORTED, "d and d_r must be 128");
+  const int vmax = d->dtype == MSA_BF16 ? 16 : 8;
+  if (!is_pow2(d->h_r) || d->h_r > vmax)
+    return fail(MSA_EUNSUPPORTED, "h_r must be a power of two <= 16 (bf16) or 8 (f32)");
+  if (d->h_kv <= 0 || d->h_kv > 64) return fail(MSA_EUNSUPPORTED, "h_kv must be in [1, 64]");
+  if (!(d->rope_base > 1.0)) return fail(MSA_EINVAL, "rope_base must be > 1");
+  if (d->kv_loc != MSA_KV_DEVICE && d->kv_loc != MSA_KV_HOST) return fail(MSA_EINVAL, "kv_loc");
+  if (!d->kr || !d->inv_norm) return fail(MSA_EINVAL, "kr / inv_norm are NULL");
+  if (!d->k_store || !d->v_store) return fail(MSA_EINVAL, "k_store / v_store are NULL");
+
+  Bank* bk = new Bank();
+  bk->desc = *d;
+  bk->desc.doc_len = nullptr;
+  bk->desc.kv_off = nullptr;
+  const int N = d->n_docs;
+  bk->doc_len.resize(N);
+  bk->kv_off.resize(N);
+  bk->tok_off.resize(N + 1);
+  bk->chunk_off.resize(N + 1);
+  bk->tok_off[0] = 0;
+  bk->chunk_off[0] = 0;
+  for (int n = 0; n < N; ++n) {
+    const int64_t L = d->doc_len[n];
+    if (L <= 0 || L % kChunk || L > (int64_t)1 << 30) {
+      delete bk;
+      return fail(MSA_EINVAL, "doc_len[" + std::to_string(n) + "] must be a positive multiple of 256");
+    }
+    bk->doc_len[n] = L;
+    bk->tok_off[n + 1] = bk->tok_off[n] + L;
+    bk->chunk_off[n + 1] = (int32_t)(bk->tok_off[n + 1] / kChunk);
+    bk->max_doc_len = std::max(bk->max_doc_len, L);
+  }
+  bk->n_tokens = bk->tok_off[N];
+  bk->n_chunks = bk->n_tokens / kChunk;
+  if (bk->n_chunks >= ((int64_t)1 << 31)) {
+    delete bk;
+    return fail(MSA_EUNSUPPORTED, "too many chunks");
+  }
+  for (int n = 0; n < N; ++n) {
+    const int64_t o = d->kv_off ? d->kv_off[n] : bk->tok_off[n];
+    if (o < 0 || o + bk->doc_len[n] > d->kv_tokens) {
+      delete bk;
+      return fail(MSA_EINVAL, "kv_off[" + std::to_string(n) + "] + doc_len exceeds kv_tokens");
+    }
+    bk->kv_off[n] = o;
+  }
+  // routing tiles (64 chunks) and pieces (document x tile overlaps)
+  const int64_t C = bk->n_chunks;
+  bk->n_tiles = (int32_t)((C + kRouteTile - 1) / kRouteTile);
+  std::vector<int32_t> chunk_doc(C), tile_piece0(bk->n_tiles + 1), doc_piece0(N + 1);
+  for (int n = 0; n < N; ++n)
+    for (int64_t c = bk->chunk_off[n]; c < bk->chunk_off[n + 1]; ++c) chunk_doc[c] = n;
+  int32_t piece = 0;
+  int last_doc = -1;
+  for (int t = 0; t < bk->n_tiles; ++t) {
+    tile_piece0[t] = piece;
+    const int64_t c0 = (int64_t)t * kRouteTile, c1 = std::min(C, c0 + kRouteTile);
+    for (int64_t c = c0; c < c1; ++c) {
+      const int n = chunk_doc[c];
+      if (c == c0 || n != chunk_doc[c - 1]) {
+        if (n != last_doc) {
+          for (int m = last_doc + 1; m <= n; ++m) doc_piece0[m] = piece;
+          last_doc = n;
+        }
+        ++piece;
+      }
+    }
+  }
+  tile_piece0[bk->n_tiles] = piece;
+  for (int m = last_doc + 1; m <= N; ++m) doc_piece0[m] = piece;
+  bk->n_pieces = piece;
+  std::vector<int32_t> dl32(N);
+  for (int n = 0; n < N; ++n) dl32[n] = (int32_t)bk->doc_len[n];
+  double inv_freq[kD / 2];
+  for (int i = 0; i < kD / 2; ++i) inv_freq[i] = std::pow(d->rope_base, -2.0 * i / kD);
+
+  // one device allocation for every table
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const size_t o_dl = take(N * 4), o_kv = take(N * 8), o_tok = take((N + 1) * 8),
+               o_cd = take(C * 4), o_tp = take((bk->n_tiles + 1) * 4),
+               o_dp = take((N + 1) * 4), o_if = take(sizeof(inv_freq));
+  if (hipGetDevice(&bk->device) != hipSuccess || hipMalloc(&bk->dev_mem, off) != hipSuccess) {
+    delete bk;
+    return fail(MSA_ENOMEM, "hipMalloc of bank tables failed");
+  }
+  char* base = (char*)bk->dev_mem;
+  bk->d_doc_len = (int32_t*)(base + o_dl);
+  bk->d_kv_off = (int64_t*)(base + o_kv);
+  bk->d_tok_off = (int64_t*)(base + o_tok);
+  bk->d_chunk_doc = (int32_t*)(base + o_cd);
+  bk->d_tile_piece0 = (int32_t*)(base + o_tp);
+  bk->d_doc_piece0 = (int32_t*)(base + o_dp);
+  bk->d_inv_freq = (double*)(base + o_if);
+  hipError_t e = hipSuccess;
+  if (e == hipSuccess) e = hipMemcpy(bk->d_doc_len, dl32.data(), N * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(bk->d_kv_off, bk->kv_off.data(), N * 8, hipMemcpyHostToDevice);
+  if (e == hipSuccess)
+    e = hipMemcpy(bk->d_tok_off, bk->tok_off.data(), (N + 1) * 8, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(bk->d_chunk_doc, chunk_doc.data(), C * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess)
+    e = hipMemcpy(bk->d_tile_piece0, tile_piece0.data(), (bk->n_tiles + 1) * 4,
+                  hipMemcpyHostToDevice);
+  if (e == hipSuccess)
+    e = hipMemcpy(bk->d_doc_piece0, doc_piece0.data(), (N + 1) * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess)
+    e = hipMemcpy(bk->d_inv_freq, inv_freq, sizeof(inv_freq), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(bk->dev_mem);
+    delete bk;
+    return fail(MSA_EHIP, std::string("uploading bank tables: ") + hipGetErrorString(e));
+  }
+  *out = reinterpret_cast<msa_bank*>(bk);
+  return MSA_OK;
+}
+
+int msa_bank_destroy(msa_bank* b) {
+  if (!b) return MSA_OK;
+  Bank* bk = reinterpret_cast<Bank*>(b);
+  if (bk->dev_mem) (void)hipFree(bk->dev_mem);
+  if (bk->h_ids) (void)hipHostFree(bk->h_ids);
+  if (bk->h_src) (void)hipHostFree(bk->h_src);
+  if (bk->h_src_off) (void)hipHostFree(bk->h_src_off);
+  delete bk;
+  return MSA_OK;
+}
+
+int msa_bank_get_info(const msa_bank* b, msa_bank_info* info) {
+  if (!b || !info) return fail(MSA_EINVAL, "NULL bank or info");
+  const Bank& bk = *as_bank(b);
+  info->n_chunks = bk.n_chunks;
+  info->n_tokens = bk.n_tokens;
+  info->max_doc_len = bk.max_doc_len;
+  info->n_docs = bk.desc.n_docs;
+  info->n_pieces = bk.n_pieces;
+  return MSA_OK;
+}
+
+int msa_build_bank(const msa_bank* b, int32_t doc0, int32_t doc1, const void* route_vec,
+                   const void* k_raw, const void* v_raw, void* stream) {
+  if (!b) return fail(MSA_EINVAL, "NULL bank");
+  const Bank& bk = *as_bank(b);
+  if (doc0 < 0 || doc1 > bk.desc.n_docs || doc0 > doc1) return fail(MSA_EINVAL, "document range");
+  if ((k_raw == nullptr) != (v_raw == nullptr))
+    return fail(MSA_EINVAL, "k_raw and v_raw must both be given or both be NULL");
+  if (k_raw && bk.desc.kv_loc != MSA_KV_DEVICE)
+    return fail(MSA_EUNSUPPORTED, "K/V of a host-resident store are not written by the library");
+  hipStream_t s = (hipStream_t)stream;
+  if (route_vec) MSA_CHECK_HIP(launch_pool_keys(bk, doc0, doc1, route_vec, s));
+  else MSA_CHECK_HIP(launch_key_norms(bk, doc0, doc1, s));
+  if (k_raw) MSA_CHECK_HIP(launch_store_kv(bk, doc0, doc1, k_raw, v_raw, s));
+  return MSA_OK;
+}
+
+int msa_prepare_local(const msa_bank* b, const void* k_raw, const void* v_raw, int32_t n_seq,
+                      int32_t L, int32_t pos0, void* k_loc, void* v_loc, int32_t loc_stride,
+                      void* stream) {
+  if (!b) return fail(MSA_EINVAL, "NULL bank");
+  if (n_seq < 0 || L < 0) return fail(MSA_EINVAL, "n_seq / L");
+  if (pos0 < 0) return fail(MSA_EINVAL, "pos0 < 0");
+  if (loc_stride < L || loc_stride % 8) return fail(MSA_EINVAL, "loc_stride must be >= L and % 8 == 0");
+  if (n_seq == 0 || loc_stride == 0) return MSA_OK;
+  if (!v_loc || (L > 0 && (!k_loc || !k_raw || !v_raw))) return fail(MSA_EINVAL, "NULL pointer");
+  MSA_CHECK_HIP(launch_prepare_local(*as_bank(b), k_raw, v_raw, n_seq, L, pos0, k_loc, v_loc,
+                                     loc_stride, (hipStream_t)stream));
+  return MSA_OK;
+}
+
+size_t msa_workspace_bytes(const msa_bank* b, int32_t mode, int32_t n_q, int32_t h_q, int32_t k,
+                           int32_t block, int32_t hops, int32_t splits) {
+  if (!b || n_q < 0 || h_q <= 0 || k < 0) return 0;
+  const Bank& bk = *as_bank(b);
+  if (splits <= 0) splits = 256;  // covers any automatic choice
+  splits = ((splits + 3) / 4) * 4;
+  return ws_layout(bk, mode, n_q, h_q, k, block, hops, splits).total;
+}
+
+size_t msa_staging_bytes(const msa_bank* b, int32_t n_groups, int32_t k) {
+  if (!b || n_groups < 0 || k < 0) return 0;
+  const Bank& bk = *as_bank(b);
+  return (size_t)2 * n_groups * k * bk.max_doc_len * bk.desc.h_kv * kD *
+         dtype_size(bk.desc.dtype);
+}
+
+int msa_route(const msa_bank* b, const float* q_route, int32_t B, int32_t k,
+              const uint32_t* exclude, int32_t* ids, float* scores, void* ws, size_t ws_bytes,
+              void* stream) {
+  if (!b) return fail(MSA_EINVAL, "NULL bank");
+  const Bank& bk = *as_bank(b);
+  if (B < 0) return fail(MSA_EINVAL, "B < 0");
+  if (k < 1 || k > bk.desc.n_docs) return fail(MSA_EINVAL, "k must be in [1, n_docs]");
+  if (B == 0) return MSA_OK;
+  if (!q_route || !ids || !scores || !ws) return fail(MSA_EINVAL, "NULL pointer");
+  const WsLayout L = ws_layout(bk, MSA_DECODE, B, bk.desc.h_kv, k, 1, 1, 4);
+  const size_t need = L.keys + align256((size_t)B * bk.desc.n_docs * 8);
+  if (ws_bytes < need) return fail(MSA_ENOMEM, "workspace too small for msa_route");
+  char* w = (char*)ws;
+  hipStream_t s = (hipStream_t)stream;
+  MSA_CHECK_HIP(launch_route_scan(bk, q_route, B, (float*)(w + L.piecemax), s));
+  MSA_CHECK_HIP(launch_topk(bk, (const float*)(w + L.piecemax), B, k, exclude, nullptr, ids,
+                            scores, (uint64_t*)(w + L.keys), s));
+  return MSA_OK;
+}
+
+int msa_attend(const msa_bank* b, const msa_attend_args* a, void* stream) {
+  if (!b || !a) return fail(MSA_EINVAL, "NULL bank or args");
+  const Bank& bk = *as_bank(b);
+  int st = check_attend_common(bk, a->mode, a->n_q, a->h_q, a->k, a->block, a->L_loc,
+                               a->loc_stride, a->k_loc, a->v_loc);
+  if (st) return st;
+  if (a->n_q == 0) return MSA_OK;
+  if (!a->q || !a->out || !a->ws || (a->k > 0 && !a->ids)) return fail(MSA_EINVAL, "NULL pointer");
+  if (a->q_pos < 0) return fail(MSA_EINVAL, "q_pos < 0");
+  AttnSources src{bk.desc.k_store, bk.desc.v_store, bk.d_kv_off, bk.d_doc_len, bk.desc.n_docs};
+  if (a->src_len || a->src_off || a->src_k || a->src_v) {
+    if (!a->src_len || !a->src_off || !a->src_k || !a->src_v || a->n_src < 0)
+      return fail(MSA_EINVAL, "source override needs src_k, src_v, src_off, src_len and n_src");
+    src = AttnSources{a->src_k, a->src_v, a->src_off, a->src_len, a->n_src};
+  } else if (bk.desc.kv_loc != MSA_KV_DEVICE && a->k > 0) {
+    return fail(MSA_EUNSUPPORTED, "host-resident bank: use msa_step or a source override");
+  }
+  const int splits = resolve_splits(bk, a->splits, a->n_q, a->k, a->L_loc);
+  const WsLayout L = ws_layout(bk, a->mode, a->n_q, a->h_q, a->k, a->block, 1, splits);
+  if (a->ws_bytes < L.total) return fail(MSA_ENOMEM, "workspace too small for msa_attend");
+  char* w = (char*)a->ws;
+  hipStream_t s = (hipStream_t)stream;
+  const bool prefill = a->mode == MSA_PREFILL;
+  MSA_CHECK_HIP(launch_rope_queries(bk, a->q, a->n_q, a->h_q, a->q_pos, prefill ? 1 : 0,
+                                    w + L.qrot, s));
+  if (prefill)
+    MSA_CHECK_HIP(launch_prefill(bk, w + L.qrot, a->n_q, a->h_q, a->ids, a->k, a->block, src,
+                                 a->k_loc, a->v_loc, a->L_loc, a->loc_stride, splits,
+                                 (float*)(w + L.part), a->out, s));
+  else
+    MSA_CHECK_HIP(launch_decode(bk, w + L.qrot, a->n_q, a->h_q, a->ids, a->k, src, a->k_loc,
+                                a->v_loc, a->L_loc, a->loc_stride, splits, (float*)(w + L.part),
+                                a->out, s));
+  return MSA_OK;
+}
+
+int msa_step(const msa_bank* b, const msa_step_args* a, void* stream, void* copy_stream,
+             msa_step_stats* stats) {
+  if (!b || !a) return fail(MSA_EINVAL, "NULL bank or args");
+  Bank& bk = *const_cast<Bank*>(as_bank(b));
+  const int N = bk.desc.n_docs;
+  int st = check_attend_common(bk, a->mode, a->n_q, a->h_q, a->k, a->block, a->L_loc,
+                               a->loc_stride, a->k_loc, a->v_loc);
+  if (st) return st;
+  if (a->k < 1 || a->k > N) return fail(MSA_EINVAL, "k must be in [1, n_docs]");
+  if (a->hops < 1) return fail(MSA_EINVAL, "hops must be >= 1");
+  const bool prefill = a->mode == MSA_PREFILL;
+  if (a->hops > 1 && (prefill || bk.desc.h_r != 1 || !a->w_proj))
+    return fail(MSA_EINVAL, "hops > 1 needs decode mode, h_r == 1 and w_proj");
+  if (stats) {
+    stats->docs_copied = 0;
+    stats->bytes_copied = 0;
+  }
+  if (a->n_q == 0) return MSA_OK;
+  if (!a->q || !a->ids || !a->scores || !a->out || !a->ws) return fail(MSA_EINVAL, "NULL pointer");
+  if (prefill ? !a->route_tokens : !a->q_route) return fail(MSA_EINVAL, "router input is NULL");
+  if (a->q_pos < 0) return fail(MSA_EINVAL, "q_pos < 0");
+  const bool host = bk.desc.kv_loc == MSA_KV_HOST;
+  const int n_groups = prefill ? a->n_q / a->block : a->n_q;
+  const int k = a->k;
+  const int splits = resolve_splits(bk, a->splits, a->n_q, k, a->L_loc);
+  const WsLayout L = ws_layout(bk, a->mode, a->n_q, a->h_q, k, a->block, a->hops, splits);
+  if (a->ws_bytes < L.total) return fail(MSA_ENOMEM, "workspace too small for msa_step");
+  const size_t esz = dtype_size(bk.desc.dtype);
+  const size_t tok_bytes = (size_t)bk.desc.h_kv * kD * esz;
+  if (host) {
+    if (!a->staging) return fail(MSA_EINVAL, "host-resident bank needs a staging buffer");
+    if (a->staging_bytes < msa_staging_bytes(b, n_groups, k))
+      return fail(MSA_ENOMEM, "staging buffer too small");
+    const size_t cap = (size_t)n_groups * k;
+    if (bk.h_ids_cap < cap) {
+      if (bk.h_ids) (void)hipHostFree(bk.h_ids);
+      if (bk.h_src) (void)hipHostFree(bk.h_src);
+      if (bk.h_src_off) (void)hipHostFree(bk.h_src_off);
+      bk.h_ids = nullptr;
+      bk.h_src = nullptr;
+      bk.h_src_off = nullptr;
+      bk.h_ids_cap = 0;
+      if (hipHostMalloc((void**)&bk.h_ids, cap * 4, 0) != hipSuccess ||
+          hipHostMalloc((void**)&bk.h_src, cap * 8, 0) != hipSuccess ||
+          hipHostMalloc((void**)&bk.h_src_off, cap * 8, 0) != hipSuccess)
+        return fail(MSA_ENOMEM, "pinned id buffers");
+      bk.h_ids_cap = cap;
+    }
+  }
+  char* w = (char*)a->ws;
+  hipStream_t s = (hipStream_t)stream;
+  hipStream_t cs = copy_stream ? (hipStream_t)copy_stream : s;
+  const int W = (N + 31) / 32;
+  uint32_t* excl = a->exclude;
+  if (a->exclude_selected && !excl) {
+    excl = (uint32_t*)(w + L.excl);
+    MSA_CHECK_HIP(hipMemsetAsync(excl, 0, (size_t)n_groups * W * 4, s));
+  }
+  float* q_route = (float*)(w + L.qroute);
+  if (prefill) {
+    MSA_CHECK_HIP(launch_block_mean(bk, a->route_tokens, a->n_q, a->block, q_route, s));
+  }
+  const float* qr = prefill ? q_route : a->q_route;
+  const size_t out_stride = (size_t)a->n_q * a->h_q * kD;
+  MSA_CHECK_HIP(launch_rope_queries(bk, a->q, a->n_q, a->h_q, a->q_pos, prefill ? 1 : 0,
+                                    w + L.qrot, s));
+  for (int hop = 0; hop < a->hops; ++hop) {
+    int32_t* ids = a->ids + (size_t)hop * n_groups * k;
+    float* scores = a->scores + (size_t)hop * n_groups * k;
+    float* out = a->out + (size_t)hop * out_stride;
+    MSA_CHECK_HIP(launch_route_scan(bk, qr, n_groups, (float*)(w + L.piecemax), s));
+    MSA_CHECK_HIP(launch_topk(bk, (const float*)(w + L.piecemax), n_groups, k, excl,
+                              a->exclude_selected ? excl : nullptr, ids, scores,
+                              (uint64_t*)(w + L.keys), s));
+    AttnSources src{bk.desc.k_store, bk.desc.v_store, bk.d_kv_off, bk.d_doc_len, N};
+    const int32_t* att_ids = ids;
+    if (host) {
+      // top-k -> K/V fetch is sequential: read the ids back, copy each
+      // distinct selected document into staging, remap ids to staging slots
+      MSA_CHECK_HIP(hipMemcpyAsync(bk.h_ids, ids, (size_t)n_groups * k * 4,
+                                   hipMemcpyDeviceToHost, s));
+      MSA_CHECK_HIP(hipStreamSynchronize(s));
+      std::unordered_map<int32_t, int32_t> slot_of;
+      int32_t* slot_ids = bk.h_src;                       // [n_groups*k]
+      int32_t* slot_len = bk.h_src + (size_t)n_groups * k; // [n_slots]
+      int64_t* slot_off = bk.h_src_off;                   // [n_slots]
+      int64_t tok = 0;
+      int32_t n_slots = 0;
+      char* stg = (char*)a->staging;
+      const size_t half = a->staging_bytes / 2;
+      for (size_t i = 0; i < (size_t)n_groups * k; ++i) {
+        const int32_t id = bk.h_ids[i];
+        if (id < 0 || id >= N) {
+          slot_ids[i] = -1;
+          continue;
+        }
+        auto it = slot_of.find(id);
+        if (it == slot_of.end()) {
+          const int64_t Ld = bk.doc_len[id];
+          slot_of.emplace(id, n_slots);
+          slot_off[n_slots] = tok;
+          slot_len[n_slots] = (int32_t)Ld;
+          const size_t bytes = (size_t)Ld * tok_bytes;
+          const size_t src_o = (size_t)bk.kv_off[id] * tok_bytes;
+          MSA_CHECK_HIP(hipMemcpyAsync(stg + (size_t)tok * tok_bytes,
+                                       (const char*)bk.desc.k_store + src_o, bytes,
+                                       hipMemcpyHostToDevice, cs));
+          MSA_CHECK_HIP(hipMemcpyAsync(stg + half + (size_t)tok * tok_bytes,
+                                       (const char*)bk.desc.v_store + src_o, bytes,
+                                       hipMemcpyHostToDevice, cs));
+          if (stats) {
+            stats->docs_copied += 1;
+            stats->bytes_copied += (int64_t)(2 * bytes);
+          }
+          slot_ids[i] = n_slots++;
+          tok += Ld;
+        } else {
+          slot_ids[i] = it->second;
+        }
+      }
+      int32_t* d_ids = (int32_t*)(w + L.srcids);
+      int64_t* d_off = (int64_t*)(w + L.srcoff);
+      int32_t* d_len = (int32_t*)(w + L.srclen);
+      MSA_CHECK_HIP(hipMemcpyAsync(d_ids, slot_ids, (size_t)n_groups * k * 4,
+                                   hipMemcpyHostToDevice, s));
+      if (n_slots > 0) {
+        MSA_CHECK_HIP(hipMemcpyAsync(d_off, slot_off, (size_t)n_slots * 8, hipMemcpyHostToDevice, s));
+        MSA_CHECK_HIP(hipMemcpyAsync(d_len, slot_len, (size_t)n_slots * 4, hipMemcpyHostToDevice, s));
+      }
+      if (cs != s) {
+        hipEvent_t ev;
+        MSA_CHECK_HIP(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+        MSA_CHECK_HIP(hipEventRecord(ev, cs));
+        MSA_CHECK_HIP(hipStreamWaitEvent(s, ev, 0));
+        MSA_CHECK_HIP(hipEventDestroy(ev));
+      }
+      src = AttnSources{stg, stg + half, d_off, d_len, n_slots};
+      att_ids = d_ids;
+    }
+    if (prefill)
+      MSA_CHECK_HIP(launch_prefill(bk, w + L.qrot, a->n_q, a->h_q, att_ids, k, a->block, src,
+                                   a->k_loc, a->v_loc, a->L_loc, a->loc_stride, splits,
+                                   (float*)(w + L.part), out, s));
+    else
+      MSA_CHECK_HIP(launch_decode(bk, w + L.qrot, a->n_q, a->h_q, att_ids, k, src, a->k_loc,
+                                  a->v_loc, a->L_loc, a->loc_stride, splits, (float*)(w + L.part),
+                                  out, s));
+    if (hop + 1 < a->hops) {
+      MSA_CHECK_HIP(launch_project(out, a->w_proj, a->n_q, a->h_q * kD, kD, q_route, s));
+      qr = q_route;
+    }
+  }
+  if (host) MSA_CHECK_HIP(hipStreamSynchronize(s));  // pinned remap tables are reused next call
+  return MSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,343 @@
+// Bank build and position handling:
+//   - routing keys: mean of every 256-token chunk of the per-token routing
+//     vectors ("MSA架构" article, intelliparadigm.com, sections 2.1 and 3.1),
+//     accumulated in float64, rounded once to the storage type, plus the
+//     inverse norm of the rounded key;
+//   - document K/V store: K rotated at document-local positions (document-wise
+//     RoPE, "MSA" card, robocikowo.com, "Komponenty"), V transposed to the
+//     channel-major layout the attention kernels stream;
+//   - local context: K rotated at global positions pos0 + j (global RoPE with
+//     an offset, same card, "Pułapki implementacyjne");
+//   - queries: rotated at their positions and pre-scaled by log2(e)/sqrt(d) so
+//     the attention kernels can use exp2.
+// RoPE is rotate-half: channel pairs (i, i + 64), angle pos * base^(-2i/128);
+// angles and rotations are computed in float64.
+#include "msa_internal.h"
+
+namespace msa {
+namespace {
+
+template <typename T> struct St;
+template <> struct St<float> {
+  static __device__ __forceinline__ float store(double x) { return (float)x; }
+  static __device__ __forceinline__ double load(float x) { return (double)x; }
+};
+template <> struct St<uint16_t> {
+  static __device__ __forceinline__ uint16_t store(double x) { return f64_to_bf16(x); }
+  static __device__ __forceinline__ double load(uint16_t x) { return (double)bf16_to_f32(x); }
+};
+
+// ---------------------------------------------------------------- pooling
+// One workgroup per chunk.  Thread t owns 16-byte vector (t % NV) of every
+// token row (NV vectors per row of h_r*128 elements) and tokens t/NV,
+// t/NV + S, ... (S = 256/NV streams); float64 partial sums are combined in a
+// fixed order through LDS.
+template <typename T>
+__global__ __launch_bounds__(256) void pool_keys_kernel(
+    const T* __restrict__ rv, int64_t chunk_first, int h_r, int64_t C,
+    T* __restrict__ kr, float* __restrict__ inv_norm) {
+  constexpr int VE = 16 / sizeof(T);
+  const int E = h_r * kD;
+  const int NV = E / VE;
+  const int S = 256 / NV;
+  const int tid = threadIdx.x;
+  const int v = tid % NV, stream = tid / NV;
+  const int64_t c = chunk_first + blockIdx.x;
+  const T* base = rv + (size_t)blockIdx.x * kChunk * E;
+
+  double acc[VE];
+#pragma unroll
+  for (int i = 0; i < VE; ++i) acc[i] = 0.0;
+  for (int t = stream; t < kChunk; t += S) {
+    const T* p = base + (size_t)t * E + v * VE;
+    T buf[VE];
+    *reinterpret_cast<uint4*>(buf) = *reinterpret_cast<const uint4*>(p);
+#pragma unroll
+    for (int i = 0; i < VE; ++i) acc[i] += St<T>::load(buf[i]);
+  }
+  __shared__ double sums[256 * (16 / sizeof(uint16_t))];  // S * E <= 256 * VE doubles
+  __shared__ double rnd[16 * kD];                          // rounded keys, h_r <= 16
+#pragma unroll
+  for (int i = 0; i < VE; ++i) sums[stream * E + v * VE + i] = acc[i];
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) {
+    double tot = 0.0;
+    for (int s = 0; s < S; ++s) tot += sums[s * E + e];
+    const T q = St<T>::store(tot / (double)kChunk);
+    const int h = e / kD, i = e % kD;
+    kr[((size_t)h * C + c) * kD + i] = q;
+    rnd[e] = St<T>::load(q);
+  }
+  __syncthreads();
+  const int wave = tid >> 6, lane = tid & 63;
+  for (int h = wave; h < h_r; h += 4) {
+    const double a = rnd[h * kD + lane], b = rnd[h * kD + 64 + lane];
+    double ss = a * a + b * b;
+    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    if (lane == 0) inv_norm[(size_t)h * C + c] = ss > 0.0 ? (float)(1.0 / sqrt(ss)) : 0.0f;
+  }
+}
+
+// inverse norms of given keys: one thread per (head, chunk) row
+template <typename T>
+__global__ __launch_bounds__(256) void key_norms_kernel(const T* __restrict__ kr, int64_t c0,
+                                                        int64_t nc, int h_r, int64_t C,
+                                                        float* __restrict__ inv_norm) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= nc * h_r) return;
+  const int h = (int)(idx / nc);
+  const int64_t c = c0 + idx % nc;
+  const T* row = kr + ((size_t)h * C + c) * kD;
+  double ss = 0.0;
+  for (int i = 0; i < kD; ++i) {
+    const double x = St<T>::load(row[i]);
+    ss += x * x;
+  }
+  inv_norm[(size_t)h * C + c] = ss > 0.0 ? (float)(1.0 / sqrt(ss)) : 0.0f;
+}
+
+// ---------------------------------------------------------------- K rotation
+// Tiles of 64 tokens.  Bank mode: the input slice starts at a document start
+// and documents are multiples of 256 tokens, so a tile lies inside one
+// document; its document is found by binary search.  Local mode: tile ->
+// (sequence, offset) with sequences of L tokens.
+struct KLayout {
+  int mode;                 // 0 bank, 1 local
+  // bank
+  const int64_t* tok_off;   // device [N+1]
+  const int64_t* kv_off;    // device [N]
+  const int32_t* doc_len;   // device [N]
+  int doc0, doc1;
+  int64_t slice_tok0;       // tok_off[doc0]
+  // local
+  int L, pos0, tiles_per_seq;
+  int h_kv;
+};
+
+struct TileInfo {
+  int64_t in_row0;   // first input row of the tile
+  int64_t out_base;  // element offset of [0][0][0] of the segment in the output
+  int seg_len;       // tokens in the segment (output row length)
+  int t0;            // token offset of the tile inside the segment
+  int pos_base;      // position of token 0 of the segment
+  int n_valid;       // valid tokens in this tile
+};
+
+__device__ __forceinline__ TileInfo tile_info(const KLayout& ly, int tile) {
+  TileInfo ti;
+  if (ly.mode == 0) {
+    const int64_t tok = ly.slice_tok0 + (int64_t)tile * kAttnTile;
+    int lo = ly.doc0, hi = ly.doc1 - 1;  // last doc with tok_off <= tok
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (ly.tok_off[mid] <= tok) lo = mid; else hi = mid - 1;
+    }
+    ti.in_row0 = tok - ly.slice_tok0;
+    ti.seg_len = ly.doc_len[lo];
+    ti.t0 = (int)(tok - ly.tok_off[lo]);
+    ti.out_base = ly.kv_off[lo] * ly.h_kv * kD;
+    ti.pos_base = 0;
+    ti.n_valid = kAttnTile;
+  } else {
+    const int s = tile / ly.tiles_per_seq;
+    ti.t0 = (tile % ly.tiles_per_seq) * kAttnTile;
+    ti.seg_len = ly.L;
+    ti.in_row0 = (int64_t)s * ly.L + ti.t0;
+    ti.out_base = (int64_t)s * ly.h_kv * ly.L * kD;
+    ti.pos_base = ly.pos0;
+    ti.n_valid = min(kAttnTile, ly.L - ti.t0);
+  }
+  return ti;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void rotate_k_kernel(const T* __restrict__ in,
+                                                       T* __restrict__ out, KLayout ly,
+                                                       const double* __restrict__ inv_freq) {
+  const TileInfo ti = tile_info(ly, blockIdx.x);
+  const int pair = threadIdx.x & 63, sub = threadIdx.x >> 6;
+  const double f = inv_freq[pair];
+  for (int tt = sub; tt < ti.n_valid; tt += 4) {
+    const int t = ti.t0 + tt;
+    const double ang = (double)(ti.pos_base + t) * f;
+    double sn, cs;
+    sincos(ang, &sn, &cs);
+    const T* src = in + (size_t)(ti.in_row0 + tt) * ly.h_kv * kD;
+    for (int h = 0; h < ly.h_kv; ++h) {
+      const double x1 = St<T>::load(src[h * kD + pair]);
+      const double x2 = St<T>::load(src[h * kD + 64 + pair]);
+      T* dst = out + ti.out_base + ((size_t)h * ti.seg_len + t) * kD;
+      dst[pair] = St<T>::store(x1 * cs - x2 * sn);
+      dst[64 + pair] = St<T>::store(x2 * cs + x1 * sn);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- V transpose
+// One workgroup per (tile of 64 tokens, head): [64 tokens][128] -> rows of the
+// channel-major output.  Local mode tiles cover loc_stride columns and write
+// zeros past L.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_v_kernel(const T* __restrict__ in,
+                                                          T* __restrict__ out, KLayout ly,
+                                                          int out_stride_local) {
+  const int h = blockIdx.y;
+  TileInfo ti;
+  int row_stride;
+  if (ly.mode == 0) {
+    ti = tile_info(ly, blockIdx.x);
+    row_stride = ti.seg_len;
+  } else {
+    const int tps = (out_stride_local + kAttnTile - 1) / kAttnTile;
+    const int s = blockIdx.x / tps;
+    ti.t0 = (blockIdx.x % tps) * kAttnTile;
+    ti.in_row0 = (int64_t)s * ly.L + ti.t0;
+    ti.out_base = (int64_t)s * ly.h_kv * kD * out_stride_local;
+    ti.n_valid = max(0, min(kAttnTile, ly.L - ti.t0));
+    row_stride = out_stride_local;
+  }
+  __shared__ T tile[kAttnTile][kD + 2];
+  for (int e = threadIdx.x; e < kAttnTile * kD; e += 256) {
+    const int t = e / kD, i = e % kD;
+    tile[t][i] = t < ti.n_valid ? in[(size_t)(ti.in_row0 + t) * ly.h_kv * kD + h * kD + i]
+                                : (T)0;
+  }
+  __syncthreads();
+  const int ncols = ly.mode == 0 ? kAttnTile : min(kAttnTile, row_stride - ti.t0);
+  T* dst = out + ti.out_base + (size_t)h * kD * row_stride + ti.t0;
+  for (int e = threadIdx.x; e < kAttnTile * kD; e += 256) {
+    const int i = e / kAttnTile, t = e % kAttnTile;
+    if (t < ncols) dst[(size_t)i * row_stride + t] = tile[t][i];
+  }
+}
+
+// ---------------------------------------------------------------- queries
+template <typename T>
+__global__ __launch_bounds__(256) void rope_queries_kernel(const T* __restrict__ q, int n_q,
+                                                           int h_q, int pos0, int pos_step,
+                                                           const double* __restrict__ inv_freq,
+                                                           double scale, T* __restrict__ out) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)n_q * 64) return;
+  const int i = (int)(idx >> 6), pair = (int)(idx & 63);
+  double sn, cs;
+  sincos((double)(pos0 + (int64_t)i * pos_step) * inv_freq[pair], &sn, &cs);
+  for (int h = 0; h < h_q; ++h) {
+    const size_t o = ((size_t)i * h_q + h) * kD;
+    const double x1 = St<T>::load(q[o + pair]), x2 = St<T>::load(q[o + 64 + pair]);
+    out[o + pair] = St<T>::store((x1 * cs - x2 * sn) * scale);
+    out[o + 64 + pair] = St<T>::store((x2 * cs + x1 * sn) * scale);
+  }
+}
+
+KLayout bank_layout(const Bank& bk, int doc0, int doc1) {
+  KLayout ly{};
+  ly.mode = 0;
+  ly.tok_off = bk.d_tok_off;
+  ly.kv_off = bk.d_kv_off;
+  ly.doc_len = bk.d_doc_len;
+  ly.doc0 = doc0;
+  ly.doc1 = doc1;
+  ly.slice_tok0 = bk.tok_off[doc0];
+  ly.h_kv = bk.desc.h_kv;
+  return ly;
+}
+
+}  // namespace
+
+hipError_t launch_pool_keys(const Bank& bk, int doc0, int doc1, const void* rv, hipStream_t s) {
+  const int64_t c0 = bk.chunk_off[doc0], nc = bk.chunk_off[doc1] - c0;
+  if (nc == 0) return hipSuccess;
+  if (bk.desc.dtype == MSA_BF16)
+    hipLaunchKernelGGL(pool_keys_kernel<uint16_t>, dim3((unsigned)nc), dim3(256), 0, s,
+                       (const uint16_t*)rv, c0, bk.desc.h_r, bk.n_chunks,
+                       (uint16_t*)bk.desc.kr, bk.desc.inv_norm);
+  else
+    hipLaunchKernelGGL(pool_keys_kernel<float>, dim3((unsigned)nc), dim3(256), 0, s,
+                       (const float*)rv, c0, bk.desc.h_r, bk.n_chunks, (float*)bk.desc.kr,
+                       bk.desc.inv_norm);
+  return hipGetLastError();
+}
+
+hipError_t launch_key_norms(const Bank& bk, int doc0, int doc1, hipStream_t s) {
+  const int64_t c0 = bk.chunk_off[doc0], nc = bk.chunk_off[doc1] - c0;
+  if (nc == 0) return hipSuccess;
+  const int64_t rows = nc * bk.desc.h_r;
+  const unsigned grid = (unsigned)((rows + 255) / 256);
+  if (bk.desc.dtype == MSA_BF16)
+    hipLaunchKernelGGL(key_norms_kernel<uint16_t>, dim3(grid), dim3(256), 0, s,
+                       (const uint16_t*)bk.desc.kr, c0, nc, bk.desc.h_r, bk.n_chunks,
+                       bk.desc.inv_norm);
+  else
+    hipLaunchKernelGGL(key_norms_kernel<float>, dim3(grid), dim3(256), 0, s,
+                       (const float*)bk.desc.kr, c0, nc, bk.desc.h_r, bk.n_chunks,
+                       bk.desc.inv_norm);
+  return hipGetLastError();
+}
+
+hipError_t launch_store_kv(const Bank& bk, int doc0, int doc1, const void* k_raw,
+                           const void* v_raw, hipStream_t s) {
+  const int64_t ntok = bk.tok_off[doc1] - bk.tok_off[doc0];
+  if (ntok == 0) return hipSuccess;
+  const unsigned tiles = (unsigned)(ntok / kAttnTile);
+  const KLayout ly = bank_layout(bk, doc0, doc1);
+  if (bk.desc.dtype == MSA_BF16) {
+    hipLaunchKernelGGL(rotate_k_kernel<uint16_t>, dim3(tiles), dim3(256), 0, s,
+                       (const uint16_t*)k_raw, (uint16_t*)bk.desc.k_store, ly, bk.d_inv_freq);
+    hipLaunchKernelGGL(transpose_v_kernel<uint16_t>, dim3(tiles, bk.desc.h_kv), dim3(256), 0, s,
+                       (const uint16_t*)v_raw, (uint16_t*)bk.desc.v_store, ly, 0);
+  } else {
+    hipLaunchKernelGGL(rotate_k_kernel<float>, dim3(tiles), dim3(256), 0, s,
+                       (const float*)k_raw, (float*)bk.desc.k_store, ly, bk.d_inv_freq);
+    hipLaunchKernelGGL(transpose_v_kernel<float>, dim3(tiles, bk.desc.h_kv), dim3(256), 0, s,
+                       (const float*)v_raw, (float*)bk.desc.v_store, ly, 0);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prepare_local(const Bank& bk, const void* k_raw, const void* v_raw, int n_seq,
+                                int L, int pos0, void* k_loc, void* v_loc, int loc_stride,
+                                hipStream_t s) {
+  KLayout ly{};
+  ly.mode = 1;
+  ly.L = L;
+  ly.pos0 = pos0;
+  ly.tiles_per_seq = (L + kAttnTile - 1) / kAttnTile;
+  ly.h_kv = bk.desc.h_kv;
+  const unsigned ktiles = (unsigned)(n_seq * ly.tiles_per_seq);
+  const unsigned vtiles = (unsigned)(n_seq * ((loc_stride + kAttnTile - 1) / kAttnTile));
+  if (bk.desc.dtype == MSA_BF16) {
+    if (ktiles)
+      hipLaunchKernelGGL(rotate_k_kernel<uint16_t>, dim3(ktiles), dim3(256), 0, s,
+                         (const uint16_t*)k_raw, (uint16_t*)k_loc, ly, bk.d_inv_freq);
+    if (vtiles)
+      hipLaunchKernelGGL(transpose_v_kernel<uint16_t>, dim3(vtiles, bk.desc.h_kv), dim3(256), 0,
+                         s, (const uint16_t*)v_raw, (uint16_t*)v_loc, ly, loc_stride);
+  } else {
+    if (ktiles)
+      hipLaunchKernelGGL(rotate_k_kernel<float>, dim3(ktiles), dim3(256), 0, s,
+                         (const float*)k_raw, (float*)k_loc, ly, bk.d_inv_freq);
+    if (vtiles)
+      hipLaunchKernelGGL(transpose_v_kernel<float>, dim3(vtiles, bk.desc.h_kv), dim3(256), 0, s,
+                         (const float*)v_raw, (float*)v_loc, ly, loc_stride);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_queries(const Bank& bk, const void* q, int n_q, int h_q, int pos0,
+                               int pos_step, void* q_rot, hipStream_t s) {
+  if (n_q == 0) return hipSuccess;
+  const double scale = 1.4426950408889634 / sqrt((double)kD);  // log2(e) / sqrt(d)
+  const unsigned grid = (unsigned)(((int64_t)n_q * 64 + 255) / 256);
+  if (bk.desc.dtype == MSA_BF16)
+    hipLaunchKernelGGL(rope_queries_kernel<uint16_t>, dim3(grid), dim3(256), 0, s,
+                       (const uint16_t*)q, n_q, h_q, pos0, pos_step, bk.d_inv_freq, scale,
+                       (uint16_t*)q_rot);
+  else
+    hipLaunchKernelGGL(rope_queries_kernel<float>, dim3(grid), dim3(256), 0, s,
+                       (const float*)q, n_q, h_q, pos0, pos_step, bk.d_inv_freq, scale,
+                       (float*)q_rot);
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -1,0 +1,443 @@
+// Split-K decode attention over the union of the selected documents and the
+// local context ("MSA" card, robocikowo.com, "Komponenty", the MSA layer:
+// the top-k documents' K/V are appended to the local context; "Paradygmat
+// wykonania": only the selected blocks take part), GQA with G query heads per
+// KV head, scale 1/sqrt(d) (mlqm.cn MLA/CSA article, section 6.2).
+//
+// HBM-bound: every K/V byte of the union is read once and feeds G query
+// heads (4 flop per byte at G = 4), so the kernel is built around streaming:
+//   - workgroup = 4 independent waves; grid = (splits/4, h_kv, B).  Each wave
+//     owns a contiguous range of 64-token tiles of its (query, KV head) union
+//     and keeps its own online-softmax state; partials are merged by
+//     combine_kernel.
+//   - K tile [64 tok][128] (row-major): 8 lanes per token row, 16 channels per
+//     lane, fully used 128-byte lines; bf16 pair dots (v_dot2_f32_bf16, fp32
+//     accumulate) against register-resident query fragments, then a three-step
+//     DPP transpose-reduce leaves lane l with the G scores of one token.
+//   - V tile [128 ch][64 tok] (channel-major store): 8 lanes per channel row,
+//     8 tokens per lane; each lane keeps its 16 rows x G accumulators for the
+//     whole range and contracts over its 8 tokens with bf16 pair dots against
+//     probabilities staged (as bf16) in a per-wave LDS slot.  The 8-lane
+//     reduction of the accumulators happens once, at the end.
+//   - the "gather" is an indirection: per (query, head) the workgroup reads
+//     the k selected ids and the document table and walks the tiles in place.
+#include <algorithm>
+
+#include "msa_internal.h"
+
+namespace msa {
+namespace {
+
+struct DecodeP {
+  const void* q;       // [B][h_q][128] rotated, pre-scaled by log2(e)/sqrt(d)
+  const int32_t* ids;  // [B][k]
+  const void* ks;
+  const void* vs;
+  const int64_t* soff;
+  const int32_t* slen;
+  int n_src;
+  const void* kl;
+  const void* vl;
+  int k, L_loc, loc_stride, h_kv, S, h_q;
+  int id_div;      // queries per id row (decode 1; prefill: the routing block)
+  int loc_shared;  // 1: every query reads local sequence 0 (prefill)
+  int causal_off;  // < 0: none; else query b sees local tokens j < causal_off + b + 1
+  float* part;     // [B][h_kv][S][G][130]: m (log2 units), l, o[128]
+};
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// one transpose-reduce step over lane pairs chosen by CTRL: the lane with
+// `upper` set keeps the upper half of its N values, its partner the lower.
+template <int CTRL, int N>
+__device__ __forceinline__ void treduce(float (&a)[N], int n, bool upper) {
+  const int half = n / 2;
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    if (i < half) {
+      const float send = upper ? a[i] : a[i + half];
+      const float keep = upper ? a[i + half] : a[i];
+      a[i] = keep + dpp_f<CTRL>(send);
+    }
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void treduce8(float (&a)[N], int j) {
+  treduce<kDppHalfMirror, N>(a, N, (j & 4) != 0);
+  treduce<kDppXor2, N>(a, N / 2, (j & 2) != 0);
+  treduce<kDppXor1, N>(a, N / 4, (j & 1) != 0);
+}
+
+template <typename T, int G>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeP p) {
+  constexpr bool kBF = sizeof(T) == 2;
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int split = blockIdx.x * 4 + wave;
+
+  __shared__ int64_t s_koff[kMaxK + 1], s_voff[kMaxK + 1];
+  __shared__ int s_len[kMaxK + 1], s_vstr[kMaxK + 1], s_tile0[kMaxK + 2];
+  __shared__ __attribute__((aligned(16))) T s_p[4][G][kAttnTile];
+
+  const int k = p.k;
+  if ((int)threadIdx.x < k) {
+    const int id = p.ids[(size_t)(b / p.id_div) * k + threadIdx.x];
+    int L = 0;
+    int64_t off = 0;
+    if (id >= 0 && id < p.n_src) {
+      L = p.slen[id];
+      off = p.soff[id];
+    }
+    const int64_t o = (off * p.h_kv + (int64_t)h * L) * kD;
+    s_len[threadIdx.x] = L;
+    s_koff[threadIdx.x] = o;
+    s_voff[threadIdx.x] = o;
+    s_vstr[threadIdx.x] = L;
+  } else if ((int)threadIdx.x == k) {
+    const int64_t seq = p.loc_shared ? 0 : b;
+    s_len[k] = p.causal_off < 0 ? p.L_loc : min(p.L_loc, p.causal_off + b + 1);
+    s_koff[k] = (seq * p.h_kv + h) * p.L_loc * kD;
+    s_voff[k] = (seq * p.h_kv + h) * kD * p.loc_stride;
+    s_vstr[k] = p.loc_stride;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int r = 0; r <= k; ++r) {
+      s_tile0[r] = acc;
+      acc += (s_len[r] + kAttnTile - 1) / kAttnTile;
+    }
+    s_tile0[k + 1] = acc;
+  }
+  __syncthreads();
+
+  const int NT = s_tile0[k + 1];
+  const int u0 = (int)((int64_t)NT * split / p.S);
+  const int u1 = (int)((int64_t)NT * (split + 1) / p.S);
+  const int j = lane & 7, g8 = lane >> 3;
+  const int tau = 8 * j + g8;  // token this lane scores after the reduction
+  const T* qrow = (const T*)p.q + ((size_t)b * p.h_q + (size_t)h * G) * kD;
+
+  // query fragments: 16 channels per lane (bf16: chunks j and j+8 of 8;
+  // fp32: chunks j, j+8, j+16, j+24 of 4)
+  constexpr int QV = kBF ? 2 : 4;  // 16-byte vectors per lane per head
+  uint4 qf[G][QV];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int c = 0; c < QV; ++c)
+      qf[g][c] = *reinterpret_cast<const uint4*>(qrow + (size_t)g * kD +
+                                                 (kBF ? (c * 64 + 8 * j) : (c * 32 + 4 * j)));
+
+  float m_run[G], l_run[G], o[16 * G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m_run[g] = -INFINITY;
+    l_run[g] = 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < 16 * G; ++i) o[i] = 0.f;
+
+  int r = 0;
+  for (int u = u0; u < u1; ++u) {
+    while (u >= s_tile0[r + 1]) ++r;
+    const int t0 = (u - s_tile0[r]) * kAttnTile;
+    const int nvalid = min(kAttnTile, s_len[r] - t0);
+    const bool loc = r == k;
+    const T* kb = (const T*)(loc ? p.kl : p.ks) + s_koff[r] + (size_t)t0 * kD;
+    const T* vb = (const T*)(loc ? p.vl : p.vs) + s_voff[r] + t0;
+    const int vstr = s_vstr[r];
+
+    // ---- loads: K 8 token rows x QV vectors, V 16 channel rows x (1|2) vectors
+    uint4 kv[8][QV];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int tt = 8 * s + g8;
+#pragma unroll
+      for (int c = 0; c < QV; ++c) {
+        kv[s][c] = make_uint4(0, 0, 0, 0);
+        if (tt < nvalid)
+          kv[s][c] = *reinterpret_cast<const uint4*>(kb + (size_t)tt * kD +
+                                                     (kBF ? (c * 64 + 8 * j) : (c * 32 + 4 * j)));
+      }
+    }
+    constexpr int VV = kBF ? 1 : 2;
+    uint4 vv[16][VV];
+    const bool vok = 8 * j < nvalid;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int d = 8 * i + g8;
+#pragma unroll
+      for (int c = 0; c < VV; ++c) {
+        vv[i][c] = make_uint4(0, 0, 0, 0);
+        if (vok)
+          vv[i][c] = *reinterpret_cast<const uint4*>(vb + (size_t)d * vstr + 8 * j + c * 4);
+      }
+    }
+
+    // ---- scores: partial dots over this lane's 16 channels
+    float acc[8 * G];
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float a = 0.f;
+#pragma unroll
+        for (int c = 0; c < QV; ++c) {
+          if constexpr (kBF) {
+            a = dot2_bf16(kv[s][c].x, qf[g][c].x, a);
+            a = dot2_bf16(kv[s][c].y, qf[g][c].y, a);
+            a = dot2_bf16(kv[s][c].z, qf[g][c].z, a);
+            a = dot2_bf16(kv[s][c].w, qf[g][c].w, a);
+          } else {
+            a = fmaf(__uint_as_float(kv[s][c].x), __uint_as_float(qf[g][c].x), a);
+            a = fmaf(__uint_as_float(kv[s][c].y), __uint_as_float(qf[g][c].y), a);
+            a = fmaf(__uint_as_float(kv[s][c].z), __uint_as_float(qf[g][c].z), a);
+            a = fmaf(__uint_as_float(kv[s][c].w), __uint_as_float(qf[g][c].w), a);
+          }
+        }
+        acc[s * G + g] = a;
+      }
+    treduce8<8 * G>(acc, j);  // lane now holds token tau's G scores in acc[0..G)
+
+    // ---- online softmax (base 2; scores are pre-scaled by log2 e)
+    const bool tv = tau < nvalid;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float sc = tv ? acc[g] : -INFINITY;
+      const float m_new = fmaxf(m_run[g], wave_max(sc));
+      const float alpha = exp2f(m_run[g] - m_new);
+      const float pe = exp2f(sc - m_new);
+      float pq;
+      if constexpr (kBF) {
+        const uint16_t pb = (uint16_t)f32_to_bf16(pe);
+        s_p[wave][g][tau] = pb;
+        pq = bf16_to_f32(pb);
+      } else {
+        s_p[wave][g][tau] = pe;
+        pq = pe;
+      }
+      l_run[g] = l_run[g] * alpha + pq;
+      m_run[g] = m_new;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[i * G + g] *= alpha;
+    }
+    wave_lds_sync();
+
+    // ---- values: zero channels past the end of a ragged tail
+    if (nvalid < kAttnTile && vok && nvalid - 8 * j < 8) {
+      const int nv = nvalid - 8 * j;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+#pragma unroll
+        for (int c = 0; c < VV; ++c) {
+          uint32_t* w = reinterpret_cast<uint32_t*>(&vv[i][c]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if constexpr (kBF) {
+              const int t = 2 * e;
+              if (t >= nv) w[e] = 0;
+              else if (t + 1 >= nv) w[e] &= 0xffffu;
+            } else {
+              if (c * 4 + e >= nv) w[e] = 0;
+            }
+          }
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if constexpr (kBF) {
+        const uint4 pp = *reinterpret_cast<const uint4*>(&s_p[wave][g][8 * j]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float a = o[i * G + g];
+          a = dot2_bf16(vv[i][0].x, pp.x, a);
+          a = dot2_bf16(vv[i][0].y, pp.y, a);
+          a = dot2_bf16(vv[i][0].z, pp.z, a);
+          a = dot2_bf16(vv[i][0].w, pp.w, a);
+          o[i * G + g] = a;
+        }
+      } else {
+        const float4 p0 = *reinterpret_cast<const float4*>(&s_p[wave][g][8 * j]);
+        const float4 p1 = *reinterpret_cast<const float4*>(&s_p[wave][g][8 * j + 4]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float a = o[i * G + g];
+          a = fmaf(__uint_as_float(vv[i][0].x), p0.x, a);
+          a = fmaf(__uint_as_float(vv[i][0].y), p0.y, a);
+          a = fmaf(__uint_as_float(vv[i][0].z), p0.z, a);
+          a = fmaf(__uint_as_float(vv[i][0].w), p0.w, a);
+          a = fmaf(__uint_as_float(vv[i][1].x), p1.x, a);
+          a = fmaf(__uint_as_float(vv[i][1].y), p1.y, a);
+          a = fmaf(__uint_as_float(vv[i][1].z), p1.z, a);
+          a = fmaf(__uint_as_float(vv[i][1].w), p1.w, a);
+          o[i * G + g] = a;
+        }
+      }
+    }
+    wave_lds_sync();  // probabilities consumed before the next tile overwrites them
+  }
+
+  // ---- wave epilogue: total l, 8-lane reduction of the accumulators
+  float l_tot[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) l_tot[g] = wave_sum(l_run[g]);
+  treduce8<16 * G>(o, j);  // lane keeps o indices [2G*j, 2G*j + 2G)
+  const size_t pbase = (((size_t)b * p.h_kv + h) * p.S + split) * G;
+#pragma unroll
+  for (int e = 0; e < 2 * G; ++e) {
+    const int idx = 2 * G * j + e;
+    const int i = idx / G, g = idx % G;
+    p.part[(pbase + g) * (kD + 2) + 2 + 8 * i + g8] = o[e];
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+    if (lane == g) {
+      p.part[(pbase + g) * (kD + 2) + 0] = m_run[g];
+      p.part[(pbase + g) * (kD + 2) + 1] = l_tot[g];
+    }
+}
+
+// merge the S partials of each (query, KV head): log-sum-exp in base 2
+template <int G>
+__global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ part, int S,
+                                                      int h_kv, int h_q, float* __restrict__ out) {
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const float* pb = part + ((size_t)b * h_kv + h) * S * G * (kD + 2);
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float M = -INFINITY;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, pb[((size_t)s * G + g) * (kD + 2)]);
+    float L = 0.f, acc = 0.f;
+    if (M != -INFINITY) {
+      for (int s = 0; s < S; ++s) {
+        const float* ps = pb + ((size_t)s * G + g) * (kD + 2);
+        const float w = exp2f(ps[0] - M);
+        L = fmaf(w, ps[1], L);
+        acc = fmaf(w, ps[2 + d], acc);
+      }
+    }
+    out[((size_t)b * h_q + (size_t)h * G + g) * kD + d] = L > 0.f ? acc / L : 0.f;
+  }
+}
+
+template <typename T, int G>
+hipError_t run_decode(const DecodeP& p, int B, float* out, hipStream_t s) {
+  const dim3 grid((unsigned)(p.S / 4), (unsigned)p.h_kv, (unsigned)B);
+  hipLaunchKernelGGL((decode_kernel<T, G>), grid, dim3(256), 0, s, p);
+  hipLaunchKernelGGL((combine_kernel<G>), dim3((unsigned)p.h_kv, (unsigned)B), dim3(128), 0, s,
+                     p.part, p.S, p.h_kv, p.h_q, out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t decode_partial_floats(int B, int h_kv, int G, int splits) {
+  return (size_t)B * h_kv * splits * G * (kD + 2);
+}
+
+int decode_auto_splits(const Bank& bk, int B, int k, int L_loc) {
+  // average union length -> tiles per (query, head); aim for >= ~4096 waves
+  // in flight and >= 2 tiles per wave
+  const double avg_doc = (double)bk.n_tokens / bk.desc.n_docs;
+  const double tiles = k * avg_doc / kAttnTile + (L_loc + kAttnTile - 1) / kAttnTile;
+  const int want = (int)((4096 + (int64_t)B * bk.desc.h_kv - 1) / ((int64_t)B * bk.desc.h_kv));
+  int s = (int)std::min<double>(want, std::max(1.0, tiles / 2));
+  s = std::max(4, ((s + 3) / 4) * 4);
+  return std::min(s, 256);
+}
+
+hipError_t launch_decode(const Bank& bk, const void* q_rot, int B, int h_q, const int32_t* ids,
+                         int k, const AttnSources& src, const void* k_loc, const void* v_loc,
+                         int L_loc, int loc_stride, int splits, float* part, float* out,
+                         hipStream_t s) {
+  DecodeP p;
+  p.q = q_rot;
+  p.ids = ids;
+  p.ks = src.k;
+  p.vs = src.v;
+  p.soff = src.off;
+  p.slen = src.len;
+  p.n_src = src.n;
+  p.kl = k_loc;
+  p.vl = v_loc;
+  p.k = k;
+  p.L_loc = L_loc;
+  p.loc_stride = loc_stride;
+  p.h_kv = bk.desc.h_kv;
+  p.S = splits;
+  p.h_q = h_q;
+  p.part = part;
+  p.id_div = 1;
+  p.loc_shared = 0;
+  p.causal_off = -1;
+  const int G = h_q / bk.desc.h_kv;
+  const bool bf = bk.desc.dtype == MSA_BF16;
+#define MSA_DEC(GG)                                                              \
+  case GG:                                                                       \
+    return bf ? run_decode<uint16_t, GG>(p, B, out, s) : run_decode<float, GG>(p, B, out, s);
+  switch (G) {
+    MSA_DEC(1)
+    MSA_DEC(2)
+    MSA_DEC(4)
+    MSA_DEC(8)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef MSA_DEC
+}
+
+}  // namespace msa
+
+namespace msa {
+
+// Blocked prefill on the decode kernel: every query token is its own split-K
+// job that reads its block's document set and a causal prefix of the shared
+// local context.  Exact, but each block's documents are re-read per query;
+// the MFMA kernel in prefill.hip shares them across the block.
+hipError_t launch_prefill_vector(const Bank& bk, const void* q_rot, int n_q, int h_q,
+                                 const int32_t* ids, int k, int block, const AttnSources& src,
+                                 const void* k_loc, const void* v_loc, int L_loc, int loc_stride,
+                                 int splits, float* part, float* out, hipStream_t s) {
+  DecodeP p;
+  p.q = q_rot;
+  p.ids = ids;
+  p.ks = src.k;
+  p.vs = src.v;
+  p.soff = src.off;
+  p.slen = src.len;
+  p.n_src = src.n;
+  p.kl = k_loc;
+  p.vl = v_loc;
+  p.k = k;
+  p.L_loc = L_loc;
+  p.loc_stride = loc_stride;
+  p.h_kv = bk.desc.h_kv;
+  p.S = splits;
+  p.h_q = h_q;
+  p.part = part;
+  p.id_div = block;
+  p.loc_shared = 1;
+  p.causal_off = L_loc - n_q;
+  const int G = h_q / bk.desc.h_kv;
+  const bool bf = bk.desc.dtype == MSA_BF16;
+#define MSA_DEC(GG)                                                                   \
+  case GG:                                                                            \
+    return bf ? run_decode<uint16_t, GG>(p, n_q, out, s) : run_decode<float, GG>(p, n_q, out, s);
+  switch (G) {
+    MSA_DEC(1)
+    MSA_DEC(2)
+    MSA_DEC(4)
+    MSA_DEC(8)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef MSA_DEC
+}
+
+}  // namespace msa

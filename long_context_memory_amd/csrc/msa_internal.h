@@ -1,0 +1,166 @@
+// Internal declarations of libmsa: the bank object, device helpers shared by
+// the kernels, and the launchers each translation unit exports to the API.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/msa.h"
+
+namespace msa {
+
+constexpr int kChunk = 256;     // routing-key chunk (tokens)
+constexpr int kD = 128;         // head size and routing-key size
+constexpr int kRouteTile = 64;  // chunks per routing wave
+constexpr int kAttnTile = 64;   // tokens per attention wave step
+constexpr int kMaxK = 64;       // documents per query the attention kernels accept
+
+struct Bank {
+  msa_bank_desc desc;  // host pointers inside are not retained
+  int device = 0;
+  int64_t n_tokens = 0, n_chunks = 0, max_doc_len = 0;
+  int32_t n_tiles = 0, n_pieces = 0;
+  std::vector<int64_t> doc_len, kv_off, tok_off;  // host copies; tok_off has N+1 entries
+  std::vector<int32_t> chunk_off;                 // N+1
+  // device tables, one allocation
+  void* dev_mem = nullptr;
+  int32_t* d_doc_len = nullptr;      // [N]
+  int64_t* d_kv_off = nullptr;       // [N]
+  int64_t* d_tok_off = nullptr;      // [N+1]
+  int32_t* d_chunk_doc = nullptr;    // [C]
+  int32_t* d_tile_piece0 = nullptr;  // [n_tiles + 1]
+  int32_t* d_doc_piece0 = nullptr;   // [N + 1]
+  double* d_inv_freq = nullptr;      // [64]
+  // pinned host buffer for reading back selected ids (host-resident banks)
+  int32_t* h_ids = nullptr;
+  size_t h_ids_cap = 0;
+  int32_t* h_src = nullptr;  // pinned [2 * cap] remap table staging
+  int64_t* h_src_off = nullptr;
+};
+
+// thread-local last error message
+void set_error(const std::string& msg);
+
+inline size_t dtype_size(msa_dtype t) { return t == MSA_BF16 ? 2 : 4; }
+
+// --------------------------------------------------------------------------
+// device helpers
+// --------------------------------------------------------------------------
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// float -> bfloat16, round to nearest even (finite inputs)
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// double -> bfloat16, round to nearest even, directly from the 64-bit pattern
+// (no intermediate float rounding).  Normal-range finite inputs; zero maps to
+// signed zero.
+__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
+  uint64_t u = (uint64_t)__double_as_longlong(x);
+  const uint64_t sign = u >> 63;
+  if ((u & 0x7fffffffffffffffull) == 0) return (uint16_t)(sign << 15);
+  u += 0xfffffffffffull + ((u >> 45) & 1ull);  // add half-ulp - 1 (+1 if odd): RNE at bit 45
+  const int64_t e = (int64_t)((u >> 52) & 0x7ff) - 1023 + 127;
+  const uint32_t mant = (uint32_t)((u >> 45) & 0x7f);
+  return (uint16_t)((sign << 15) | ((uint64_t)e << 7) | mant);
+}
+
+// fp32 accumulate of a bf16 pair dot product: c + a.lo*b.lo + a.hi*b.hi
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// DPP lane exchanges inside groups of 8 lanes (all sources valid)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xb1;        // quad_perm(1,0,3,2)
+constexpr int kDppXor2 = 0x4e;        // quad_perm(2,3,0,1)
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within each 8 lanes
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Order-preserving map of a float onto uint32 (larger float -> larger code).
+__device__ __forceinline__ uint32_t float_order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float float_from_order_key(uint32_t k) {
+  const uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+
+// --------------------------------------------------------------------------
+// launchers (each returns hipError_t of the launch)
+// --------------------------------------------------------------------------
+// bank build
+hipError_t launch_pool_keys(const Bank& bk, int doc0, int doc1, const void* route_vec,
+                            hipStream_t s);
+hipError_t launch_key_norms(const Bank& bk, int doc0, int doc1, hipStream_t s);
+hipError_t launch_store_kv(const Bank& bk, int doc0, int doc1, const void* k_raw,
+                           const void* v_raw, hipStream_t s);
+hipError_t launch_prepare_local(const Bank& bk, const void* k_raw, const void* v_raw, int n_seq,
+                                int L, int pos0, void* k_loc, void* v_loc, int loc_stride,
+                                hipStream_t s);
+// queries: rotate at positions (pos0 + i*pos_step) and pre-scale by log2(e)/sqrt(d)
+hipError_t launch_rope_queries(const Bank& bk, const void* q, int n_q, int h_q, int pos0,
+                               int pos_step, void* q_rot, hipStream_t s);
+
+// routing
+hipError_t launch_route_scan(const Bank& bk, const float* q_route, int B, float* piecemax,
+                             hipStream_t s);
+hipError_t launch_topk(const Bank& bk, const float* piecemax, int B, int k,
+                       const uint32_t* exclude, uint32_t* exclude_out, int32_t* ids,
+                       float* scores, uint64_t* keys, hipStream_t s);
+hipError_t launch_block_mean(const Bank& bk, const void* route_tokens, int n_tok, int block,
+                             float* q_out, hipStream_t s);
+hipError_t launch_project(const float* out, const float* w, int B, int n_in, int d_r,
+                          float* q_next, hipStream_t s);
+
+// attention
+struct AttnSources {
+  const void* k;
+  const void* v;
+  const int64_t* off;
+  const int32_t* len;
+  int n;  // entries in off / len
+};
+hipError_t launch_decode(const Bank& bk, const void* q_rot, int B, int h_q, const int32_t* ids,
+                         int k, const AttnSources& src, const void* k_loc, const void* v_loc,
+                         int L_loc, int loc_stride, int splits, float* part, float* out,
+                         hipStream_t s);
+hipError_t launch_prefill(const Bank& bk, const void* q_rot, int n_q, int h_q, const int32_t* ids,
+                          int k, int block, const AttnSources& src, const void* k_loc,
+                          const void* v_loc, int L_loc, int loc_stride, int splits, float* part,
+                          float* out, hipStream_t s);
+
+// sizes of the attention partial buffers
+size_t decode_partial_floats(int B, int h_kv, int G, int splits);
+int decode_auto_splits(const Bank& bk, int B, int k, int L_loc);
+size_t prefill_partial_floats(int n_q, int h_q, int block, int splits);
+int prefill_auto_splits(const Bank& bk, int n_q, int h_q, int block, int k, int L_loc);
+
+}  // namespace msa

@@ -1,0 +1,262 @@
+"""Thin ctypes binding of libmsa.so (include/msa.h).
+
+Argument marshalling only: every step of the path runs in the HIP library.
+PyTorch provides device memory, pinned host memory and the current stream.
+Importing this module loads the library and raises if it is missing; there
+is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import torch  # noqa: F401  (loads the HIP runtime the library binds to)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmsa.so")
+
+MSA_OK, MSA_EINVAL, MSA_ENOMEM, MSA_EHIP, MSA_EUNSUPPORTED = 0, 1, 2, 3, 4
+MSA_F32, MSA_BF16 = 0, 1
+MSA_KV_DEVICE, MSA_KV_HOST = 0, 1
+MSA_DECODE, MSA_PREFILL = 0, 1
+
+EXPORTS = [
+    "msa_status_string", "msa_last_error", "msa_version", "msa_bank_create",
+    "msa_bank_destroy", "msa_bank_get_info", "msa_build_bank", "msa_prepare_local",
+    "msa_workspace_bytes", "msa_staging_bytes", "msa_route", "msa_attend", "msa_step",
+]
+
+vp = C.c_void_p
+i32 = C.c_int32
+i64 = C.c_int64
+
+
+class BankDesc(C.Structure):
+    _fields_ = [("dtype", C.c_int), ("n_docs", i32), ("doc_len", C.POINTER(i64)),
+                ("kv_off", C.POINTER(i64)), ("kv_tokens", i64), ("h_r", i32), ("d_r", i32),
+                ("h_kv", i32), ("d", i32), ("rope_base", C.c_double), ("kv_loc", C.c_int),
+                ("kr", vp), ("inv_norm", vp), ("k_store", vp), ("v_store", vp)]
+
+
+class BankInfo(C.Structure):
+    _fields_ = [("n_chunks", i64), ("n_tokens", i64), ("max_doc_len", i64), ("n_docs", i32),
+                ("n_pieces", i32)]
+
+
+class AttendArgs(C.Structure):
+    _fields_ = [("mode", i32), ("n_q", i32), ("h_q", i32), ("q", vp), ("q_pos", i32),
+                ("ids", vp), ("k", i32), ("block", i32), ("k_loc", vp), ("v_loc", vp),
+                ("L_loc", i32), ("loc_stride", i32), ("out", vp), ("ws", vp),
+                ("ws_bytes", C.c_size_t), ("splits", i32), ("src_k", vp), ("src_v", vp),
+                ("src_off", vp), ("src_len", vp), ("n_src", i32)]
+
+
+class StepArgs(C.Structure):
+    _fields_ = [("mode", i32), ("n_q", i32), ("h_q", i32), ("k", i32), ("q", vp),
+                ("q_pos", i32), ("q_route", vp), ("route_tokens", vp), ("block", i32),
+                ("k_loc", vp), ("v_loc", vp), ("L_loc", i32), ("loc_stride", i32),
+                ("hops", i32), ("w_proj", vp), ("exclude_selected", i32), ("exclude", vp),
+                ("ids", vp), ("scores", vp), ("out", vp), ("ws", vp), ("ws_bytes", C.c_size_t),
+                ("staging", vp), ("staging_bytes", C.c_size_t), ("splits", i32)]
+
+
+class StepStats(C.Structure):
+    _fields_ = [("docs_copied", i64), ("bytes_copied", i64)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m long_context_memory_amd.build` (no fallback path)")
+    lib = C.CDLL(LIB_PATH)
+    lib.msa_status_string.restype = C.c_char_p
+    lib.msa_status_string.argtypes = [C.c_int]
+    lib.msa_last_error.restype = C.c_char_p
+    lib.msa_last_error.argtypes = []
+    lib.msa_version.restype = C.c_int
+    lib.msa_bank_create.argtypes = [C.POINTER(BankDesc), C.POINTER(vp)]
+    lib.msa_bank_destroy.argtypes = [vp]
+    lib.msa_bank_get_info.argtypes = [vp, C.POINTER(BankInfo)]
+    lib.msa_build_bank.argtypes = [vp, i32, i32, vp, vp, vp, vp]
+    lib.msa_prepare_local.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, i32, vp]
+    lib.msa_workspace_bytes.restype = C.c_size_t
+    lib.msa_workspace_bytes.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32]
+    lib.msa_staging_bytes.restype = C.c_size_t
+    lib.msa_staging_bytes.argtypes = [vp, i32, i32]
+    lib.msa_route.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp, C.c_size_t, vp]
+    lib.msa_attend.argtypes = [vp, C.POINTER(AttendArgs), vp]
+    lib.msa_step.argtypes = [vp, C.POINTER(StepArgs), vp, vp, C.POINTER(StepStats)]
+    for f in (lib.msa_bank_create, lib.msa_bank_destroy, lib.msa_bank_get_info,
+              lib.msa_build_bank, lib.msa_prepare_local, lib.msa_route, lib.msa_attend,
+              lib.msa_step):
+        f.restype = C.c_int
+    return lib
+
+
+lib = _load()
+
+
+class MSAError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {lib.msa_status_string(status).decode()} "
+                         f"({lib.msa_last_error().decode()})")
+
+
+def _check(status, where):
+    if status != MSA_OK:
+        raise MSAError(status, where)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _dt(dtype) -> int:
+    return MSA_BF16 if dtype in ("bf16", torch.bfloat16) else MSA_F32
+
+
+def _tdt(dtype):
+    return torch.bfloat16 if _dt(dtype) == MSA_BF16 else torch.float32
+
+
+class Bank:
+    """A memory bank: routing keys and K/V stores (allocated by PyTorch) and
+    the library's bank handle.  Store layouts are those of include/msa.h."""
+
+    def __init__(self, doc_len, h_r: int, h_kv: int, dtype="bf16", device="cuda",
+                 kv_loc: str = "device", kv_off=None, kv_tokens: Optional[int] = None,
+                 rope_base: float = 10000.0, kr=None, k_store=None, v_store=None):
+        self.doc_len = [int(x) for x in doc_len]
+        self.n_docs = len(self.doc_len)
+        self.h_r, self.h_kv, self.d = int(h_r), int(h_kv), 128
+        self.dtype = _tdt(dtype)
+        self.device = torch.device(device)
+        self.kv_host = kv_loc == "host"
+        T = sum(self.doc_len)
+        self.C = T // 256
+        self.kv_tokens = int(kv_tokens) if kv_tokens is not None else T
+        self.kr = kr if kr is not None else torch.empty(
+            (self.h_r, self.C, 128), dtype=self.dtype, device=self.device)
+        self.inv_norm = torch.empty((self.h_r, self.C), dtype=torch.float32, device=self.device)
+        n = self.kv_tokens * self.h_kv * 128
+        if k_store is None:
+            if self.kv_host:
+                k_store = torch.empty(n, dtype=self.dtype, pin_memory=True)
+                v_store = torch.empty(n, dtype=self.dtype, pin_memory=True)
+            else:
+                k_store = torch.empty(n, dtype=self.dtype, device=self.device)
+                v_store = torch.empty(n, dtype=self.dtype, device=self.device)
+        self.k_store, self.v_store = k_store, v_store
+        self._dl = (i64 * self.n_docs)(*self.doc_len)
+        self._ko = None if kv_off is None else (i64 * self.n_docs)(*[int(x) for x in kv_off])
+        desc = BankDesc(_dt(self.dtype), self.n_docs, self._dl, self._ko, self.kv_tokens,
+                        self.h_r, 128, self.h_kv, 128, float(rope_base),
+                        MSA_KV_HOST if self.kv_host else MSA_KV_DEVICE, _ptr(self.kr),
+                        _ptr(self.inv_norm), _ptr(self.k_store), _ptr(self.v_store))
+        h = vp()
+        _check(lib.msa_bank_create(C.byref(desc), C.byref(h)), "msa_bank_create")
+        self.handle = h
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value:
+            lib.msa_bank_destroy(h)
+            self.handle = None
+
+    def info(self) -> BankInfo:
+        inf = BankInfo()
+        _check(lib.msa_bank_get_info(self.handle, C.byref(inf)), "msa_bank_get_info")
+        return inf
+
+    # -- build --------------------------------------------------------------
+    def build(self, doc0: int, doc1: int, route_vec=None, k_raw=None, v_raw=None, stream=None):
+        _check(lib.msa_build_bank(self.handle, doc0, doc1, _ptr(route_vec), _ptr(k_raw),
+                                  _ptr(v_raw), _stream(stream)), "msa_build_bank")
+
+    def prepare_local(self, k_raw, v_raw, pos0: int, loc_stride: Optional[int] = None,
+                      stream=None):
+        """k_raw, v_raw: [n_seq, L, h_kv, 128] -> (k_loc, v_loc, L, loc_stride)."""
+        n_seq, L = int(k_raw.shape[0]), int(k_raw.shape[1])
+        ls = int(loc_stride) if loc_stride is not None else max(8, (L + 7) // 8 * 8)
+        k_loc = torch.empty((n_seq, self.h_kv, L, 128), dtype=self.dtype, device=self.device)
+        v_loc = torch.empty((n_seq, self.h_kv, 128, ls), dtype=self.dtype, device=self.device)
+        _check(lib.msa_prepare_local(self.handle, _ptr(k_raw), _ptr(v_raw), n_seq, L, int(pos0),
+                                     _ptr(k_loc), _ptr(v_loc), ls, _stream(stream)),
+               "msa_prepare_local")
+        return k_loc, v_loc, L, ls
+
+    # -- workspace ----------------------------------------------------------
+    def workspace_bytes(self, mode, n_q, h_q, k, block=64, hops=1, splits=0) -> int:
+        return int(lib.msa_workspace_bytes(self.handle, mode, n_q, h_q, k, block, hops, splits))
+
+    def workspace(self, mode, n_q, h_q, k, block=64, hops=1, splits=0):
+        n = self.workspace_bytes(mode, n_q, h_q, k, block, hops, splits)
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
+
+    def staging(self, n_groups, k):
+        n = int(lib.msa_staging_bytes(self.handle, n_groups, k))
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
+
+    # -- hot path -----------------------------------------------------------
+    def route(self, q_route, k: int, exclude=None, ws=None, stream=None):
+        B = int(q_route.shape[0])
+        if ws is None:
+            ws = self.workspace(MSA_DECODE, B, self.h_kv, k)
+        ids = torch.empty((B, k), dtype=torch.int32, device=self.device)
+        scores = torch.empty((B, k), dtype=torch.float32, device=self.device)
+        _check(lib.msa_route(self.handle, _ptr(q_route), B, k, _ptr(exclude), _ptr(ids),
+                             _ptr(scores), _ptr(ws), ws.numel(), _stream(stream)), "msa_route")
+        return ids, scores
+
+    def attend(self, q, q_pos: int, ids, k_loc, v_loc, L_loc: int, loc_stride: int,
+               mode=MSA_DECODE, block: int = 64, splits: int = 0, ws=None, src=None,
+               out=None, stream=None):
+        n_q, h_q = int(q.shape[0]), int(q.shape[1])
+        k = 0 if ids is None else int(ids.shape[1])
+        if ws is None:
+            ws = self.workspace(mode, n_q, h_q, k, block, 1, splits)
+        if out is None:
+            out = torch.empty((n_q, h_q, 128), dtype=torch.float32, device=self.device)
+        sk, sv, so, sl = (None, None, None, None) if src is None else src
+        a = AttendArgs(mode, n_q, h_q, _ptr(q), int(q_pos), _ptr(ids), k, block, _ptr(k_loc),
+                       _ptr(v_loc), int(L_loc), int(loc_stride), _ptr(out), _ptr(ws),
+                       ws.numel(), splits, _ptr(sk), _ptr(sv), _ptr(so), _ptr(sl),
+                       0 if sl is None else int(sl.numel()))
+        _check(lib.msa_attend(self.handle, C.byref(a), _stream(stream)), "msa_attend")
+        return out
+
+    def step(self, q, q_pos: int, k: int, k_loc, v_loc, L_loc: int, loc_stride: int,
+             q_route=None, route_tokens=None, mode=MSA_DECODE, block: int = 64, hops: int = 1,
+             w_proj=None, exclude_selected: bool = False, exclude=None, splits: int = 0,
+             ws=None, staging=None, outputs=None, stream=None, copy_stream=None):
+        """Returns (ids [hops, n_groups, k], scores, out [hops, n_q, h_q, 128], stats)."""
+        n_q, h_q = int(q.shape[0]), int(q.shape[1])
+        n_groups = n_q // block if mode == MSA_PREFILL else n_q
+        if ws is None:
+            ws = self.workspace(mode, n_q, h_q, k, block, hops, splits)
+        if self.kv_host and staging is None:
+            staging = self.staging(n_groups, k)
+        if outputs is None:
+            ids = torch.empty((hops, n_groups, k), dtype=torch.int32, device=self.device)
+            scores = torch.empty((hops, n_groups, k), dtype=torch.float32, device=self.device)
+            out = torch.empty((hops, n_q, h_q, 128), dtype=torch.float32, device=self.device)
+        else:
+            ids, scores, out = outputs
+        a = StepArgs(mode, n_q, h_q, k, _ptr(q), int(q_pos), _ptr(q_route), _ptr(route_tokens),
+                     block, _ptr(k_loc), _ptr(v_loc), int(L_loc), int(loc_stride), hops,
+                     _ptr(w_proj), int(bool(exclude_selected)), _ptr(exclude), _ptr(ids),
+                     _ptr(scores), _ptr(out), _ptr(ws), ws.numel(), _ptr(staging),
+                     0 if staging is None else staging.numel(), splits)
+        st = StepStats()
+        cs = None if copy_stream is None else _stream(copy_stream)
+        _check(lib.msa_step(self.handle, C.byref(a), _stream(stream), cs, C.byref(st)),
+               "msa_step")
+        return ids, scores, out, st

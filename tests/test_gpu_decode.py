@@ -1,0 +1,250 @@
+"""GPU parity of the decode path (bank build, routing, top-k, gather, split-K
+decode attention) against the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+from long_context_memory_amd import synth as S
+from oracle import msa_oracle as O
+import msa_cases as M
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def msa():
+    from long_context_memory_amd import msa as m
+    return m
+
+
+_CACHE = {}
+
+
+def decode_case(msa, name):
+    if name in _CACHE:
+        return _CACHE[name]
+    w = S.workload(name)
+    r = S.route_vectors(w, DEV)
+    k_raw, v_raw = S.kv_raw(w, DEV)
+    bank = msa.Bank(w.doc_len, w.h_r, w.h_kv, w.dtype, DEV, rope_base=w.rope_base)
+    bank.build(0, w.n_docs, r, k_raw, v_raw)
+    kr_o, inv_o = M.pool_oracle(w, r)
+    if w.plant == "pooled_key":
+        doc, ch = S.pooled_key_target(w)
+        q_route = S.pooled_key_query(w, kr_o[ch], DEV)
+    else:
+        doc = None
+        q_route = S.route_queries(w, DEV)
+    q = S.queries(w, DEV)
+    lk, lv = S.local_raw(w, DEV)
+    k_loc, v_loc, L, ls = bank.prepare_local(lk, lv, w.P0)
+    torch.cuda.synchronize()
+    c = dict(w=w, r=r, k_raw=k_raw, v_raw=v_raw, bank=bank, kr_o=kr_o, inv_o=inv_o,
+             q_route=q_route, q=q, lk=lk, lv=lv, k_loc=k_loc, v_loc=v_loc, L=L, ls=ls,
+             target_doc=doc)
+    _CACHE[name] = c
+    return c
+
+
+SMALL = ["c1_small", "c2_small", "c1"]
+
+
+@pytest.mark.parametrize("name", SMALL + ["c2"])
+def test_bank_build_matches_oracle(msa, name):
+    c = decode_case(msa, name)
+    w, bank = c["w"], c["bank"]
+    kr = M.np64(bank.kr.permute(1, 0, 2))
+    np.testing.assert_array_equal(kr, c["kr_o"])  # float64 mean, one rounding: bit-exact
+    inv = M.np64(bank.inv_norm.t())
+    np.testing.assert_allclose(inv, c["inv_o"], rtol=2e-7, atol=0)
+    for n in M.seeded_subset(w.n_docs, 6, 7):
+        k_o, v_o = M.oracle_doc_kv(w, c["k_raw"], c["v_raw"], n)
+        kg = M.natural_from_store_k(bank, n)
+        vg = M.natural_from_store_v(bank, n)
+        np.testing.assert_array_equal(M.np64(vg), v_o)
+        kt = torch.from_numpy(k_o).to(kg.dtype)
+        if w.dtype == "bf16":
+            ud = M.ulp_diff_bf16(kg.cpu(), kt)
+            assert int(ud.max()) <= 1 and float((ud > 0).float().mean()) < 1e-3
+        else:
+            np.testing.assert_allclose(M.np64(kg), k_o, rtol=2.5e-7, atol=1e-30)
+
+
+@pytest.mark.parametrize("name", ["c1_small", "c2_small"])
+def test_prepare_local_matches_oracle(msa, name):
+    c = decode_case(msa, name)
+    w = c["w"]
+    L = c["L"]
+    for b in range(w.B):
+        lk_o = O.round_to_storage(O.rope_rotate(M.np64(c["lk"][b]), (w.P0 + np.arange(L))[:, None],
+                                                w.rope_base), w.dtype)
+        kg = M.np64(c["k_loc"][b].permute(1, 0, 2))
+        np.testing.assert_allclose(kg, lk_o, rtol=0, atol=(8e-3 if w.dtype == "bf16" else 1e-6))
+        vg = c["v_loc"][b]
+        np.testing.assert_array_equal(M.np64(vg[:, :, :L].permute(2, 0, 1)), M.np64(c["lv"][b]))
+        assert float(vg[:, :, L:].abs().max() if c["ls"] > L else 0.0) == 0.0
+
+
+def oracle_scores(c, exclude=None):
+    w = c["w"]
+    return O.cosine_doc_scores(M.np64(c["q_route"]), c["kr_o"], c["inv_o"], w.doc_len, exclude)
+
+
+@pytest.mark.parametrize("name", SMALL + ["c2"])
+def test_route_matches_oracle(msa, name):
+    c = decode_case(msa, name)
+    w = c["w"]
+    ids, scores = c["bank"].route(c["q_route"], w.k)
+    torch.cuda.synchronize()
+    so = oracle_scores(c)
+    M.check_topk(ids.cpu().numpy(), scores.cpu().numpy(), so, w.k)
+    if w.plant == "direction":
+        tgt, _ = S.planted_targets(w)
+        for b in range(w.B):
+            assert set(ids[b].tolist()) == set(tgt[b].tolist())
+    if w.plant == "pooled_key":
+        assert all(int(ids[b, 0]) == c["target_doc"] for b in range(w.B))
+
+
+@pytest.mark.parametrize("name", ["c2_small"])
+def test_route_exclusion_and_k_equals_n(msa, name):
+    c = decode_case(msa, name)
+    w = c["w"]
+    N = w.n_docs
+    rng = np.random.default_rng(5)
+    excl = rng.random((w.B, N)) < 0.3
+    words = np.zeros((w.B, (N + 31) // 32), dtype=np.uint32)
+    for b in range(w.B):
+        for n in np.nonzero(excl[b])[0]:
+            words[b, n // 32] |= np.uint32(1 << (n % 32))
+    ex = torch.from_numpy(words.view(np.int32)).to(DEV)
+    kk = min(w.k, int((~excl).sum(axis=1).min()))
+    ids, scores = c["bank"].route(c["q_route"], kk, exclude=ex)
+    so = oracle_scores(c, excl)
+    M.check_topk(ids.cpu().numpy(), scores.cpu().numpy(), so, kk)
+    # more requested than remain: the tail is -1 / -inf
+    ids, scores = c["bank"].route(c["q_route"], N, exclude=ex)
+    for b in range(w.B):
+        nv = int((~excl[b]).sum())
+        assert (ids[b, nv:] == -1).all() and torch.isinf(scores[b, nv:]).all()
+        assert set(ids[b, :nv].tolist()) == set(np.nonzero(~excl[b])[0].tolist())
+    # k = N without exclusion: every document, in score order
+    ids, scores = c["bank"].route(c["q_route"], N)
+    so = oracle_scores(c)
+    M.check_topk(ids.cpu().numpy(), scores.cpu().numpy(), so, N)
+
+
+def oracle_decode(c, ids_gpu, so):
+    """Oracle outputs for every query; the oracle's own top-k unless the GPU
+    chose a valid alternative inside a near-tie."""
+    w = c["w"]
+    o_ids, _ = O.select_topk(so, w.k)
+    q = M.np64(c["q"])
+    lk, lv = M.np64(c["lk"]), M.np64(c["lv"])
+    outs = []
+    cache = {}
+    for b in range(w.B):
+        sel = o_ids[b] if set(o_ids[b].tolist()) == set(ids_gpu[b].tolist()) else ids_gpu[b]
+        for n in sel:
+            if n not in cache:
+                cache[n] = M.oracle_doc_kv(w, c["k_raw"], c["v_raw"], n)
+        outs.append(M.oracle_attend_decode(w, q[b], w.q_pos, sel, cache, lk[b], lv[b], w.P0))
+    return np.stack(outs)
+
+
+@pytest.mark.parametrize("name", SMALL + ["c2"])
+def test_decode_step_matches_oracle(msa, name):
+    c = decode_case(msa, name)
+    w = c["w"]
+    ids, scores, out, _ = c["bank"].step(c["q"], w.q_pos, w.k, c["k_loc"], c["v_loc"], c["L"],
+                                         c["ls"], q_route=c["q_route"])
+    torch.cuda.synchronize()
+    so = oracle_scores(c)
+    ids_np = ids[0].cpu().numpy()
+    M.check_topk(ids_np, scores[0].cpu().numpy(), so, w.k)
+    ref = oracle_decode(c, ids_np, so)
+    mx, rel = M.check_out(out[0].cpu().numpy(), ref, w.dtype, name)
+    print(f"{name}: max abs {mx:.3e} rel rms {rel:.3e}")
+
+
+def test_decode_power_wrong_document_is_caught(msa):
+    # the tolerance is tight enough to see one swapped document
+    c = decode_case(msa, "c2_small")
+    w = c["w"]
+    ids, scores, out, _ = c["bank"].step(c["q"], w.q_pos, w.k, c["k_loc"], c["v_loc"], c["L"],
+                                         c["ls"], q_route=c["q_route"])
+    ids_np = ids[0].cpu().numpy().copy()
+    so = oracle_scores(c)
+    bad = ids_np.copy()
+    bad[0, -1] = [n for n in range(w.n_docs) if n not in bad[0]][0]
+    ref_bad = oracle_decode(c, bad, so)  # union with one document replaced
+    with pytest.raises(AssertionError):
+        M.check_out(out[0].cpu().numpy(), ref_bad, w.dtype, "power")
+
+
+@pytest.mark.parametrize("name", ["c1_small", "c2_small"])
+def test_decode_splits_and_determinism(msa, name):
+    c = decode_case(msa, name)
+    w = c["w"]
+    ids, _ = c["bank"].route(c["q_route"], w.k)
+    outs = [c["bank"].attend(c["q"], w.q_pos, ids, c["k_loc"], c["v_loc"], c["L"], c["ls"],
+                             splits=s) for s in (4, 8, 64)]
+    again = c["bank"].attend(c["q"], w.q_pos, ids, c["k_loc"], c["v_loc"], c["L"], c["ls"],
+                             splits=8)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[1], again)  # deterministic
+    # different splits see different running maxima; fp32 agrees to rounding,
+    # bf16 to the bf16 rounding of the probabilities (2^-8 relative)
+    scale = float(outs[0].abs().max())
+    tol = 2e-6 if w.dtype == "f32" else 2.0 ** -8
+    for o in outs[1:]:
+        assert float((o - outs[0]).abs().max()) <= tol * scale
+
+
+@pytest.mark.parametrize("L_loc", [0, 1, 63, 64, 65, 130])
+def test_decode_ragged_and_empty_local(msa, L_loc):
+    c = decode_case(msa, "c2_small")
+    w, bank = c["w"], c["bank"]
+    lk, lv = c["lk"][:, :L_loc].contiguous(), c["lv"][:, :L_loc].contiguous()
+    k_loc, v_loc, L, ls = bank.prepare_local(lk, lv, w.P0)
+    ids, _ = bank.route(c["q_route"], w.k)
+    out = bank.attend(c["q"], w.P0 + max(L_loc, 1) - 1, ids, k_loc, v_loc, L, ls)
+    torch.cuda.synchronize()
+    so = oracle_scores(c)
+    ids_np = ids.cpu().numpy()
+    q = M.np64(c["q"])
+    cache = {}
+    for b in range(w.B):
+        for n in ids_np[b]:
+            cache.setdefault(n, M.oracle_doc_kv(w, c["k_raw"], c["v_raw"], n))
+        ref = M.oracle_attend_decode(w, q[b], w.P0 + max(L_loc, 1) - 1, ids_np[b], cache,
+                                     M.np64(lk[b]), M.np64(lv[b]), w.P0)
+        M.check_out(out[b].cpu().numpy(), ref, w.dtype, f"L_loc={L_loc}")
+    del so
+
+
+def test_decode_local_only_and_docs_only(msa):
+    c = decode_case(msa, "c2_small")
+    w, bank = c["w"], c["bank"]
+    q = M.np64(c["q"])
+    # k = 0: attention over the local context alone
+    out = bank.attend(c["q"], w.q_pos, None, c["k_loc"], c["v_loc"], c["L"], c["ls"])
+    torch.cuda.synchronize()
+    for b in range(w.B):
+        ref = M.oracle_attend_decode(w, q[b], w.q_pos, [], {}, M.np64(c["lk"][b]),
+                                     M.np64(c["lv"][b]), w.P0)
+        M.check_out(out[b].cpu().numpy(), ref, w.dtype, "local only")
+    # one document, some ids -1 (skipped)
+    ids = torch.full((w.B, 3), -1, dtype=torch.int32, device=DEV)
+    ids[:, 1] = torch.arange(w.B, dtype=torch.int32, device=DEV) + 5
+    e = torch.empty((w.B, 0, w.h_kv, 128), dtype=c["lk"].dtype, device=DEV)
+    k0, v0, L0, ls0 = bank.prepare_local(e, e, w.P0)
+    out = bank.attend(c["q"], w.q_pos, ids, k0, v0, L0, ls0)
+    torch.cuda.synchronize()
+    for b in range(w.B):
+        n = b + 5
+        kv = {n: M.oracle_doc_kv(w, c["k_raw"], c["v_raw"], n)}
+        ref = M.oracle_attend_decode(w, q[b], w.q_pos, [n], kv, np.zeros((0, w.h_kv, 128)),
+                                     np.zeros((0, w.h_kv, 128)), w.P0)
+        M.check_out(out[b].cpu().numpy(), ref, w.dtype, "docs only")
