@@ -48,9 +48,9 @@ def main():
         q = S.queries(w, dev, batch=i)
         q_route = S.route_queries(w, dev, batch=i)
         lk, lv = S.local_raw(w, dev, batch=i)
-        k_loc, v_loc, L, ls = bank.prepare_local(lk, lv, w.P0)
+        k_loc, v_loc, L = bank.prepare_local(lk, lv, w.P0)
         del lk, lv
-        batches.append((q, q_route, k_loc, v_loc, L, ls))
+        batches.append((q, q_route, k_loc, v_loc, L))
     ws = bank.workspace(msa.MSA_DECODE, w.B, w.h_q, w.k)
     outs = [(torch.empty((1, w.B, w.k), dtype=torch.int32, device=dev),
              torch.empty((1, w.B, w.k), dtype=torch.float32, device=dev),
@@ -59,8 +59,8 @@ def main():
     torch.cuda.synchronize()
 
     def step(i):
-        q, q_route, k_loc, v_loc, L, ls = batches[i % args.batches]
-        bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, ls, q_route=q_route, ws=ws,
+        q, q_route, k_loc, v_loc, L = batches[i % args.batches]
+        bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=q_route, ws=ws,
                   outputs=outs[i % args.batches])
 
     print("[bench] warmup", file=sys.stderr, flush=True)

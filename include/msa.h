@@ -45,10 +45,12 @@
  *   Document K store  per document n at token offset kv_off[n]:
  *                     k_store + kv_off[n]*h_kv*d  ->  [h_kv][L_n][d]
  *                     (rotated at document-local positions 0..L_n-1)
- *   Document V store  v_store + kv_off[n]*h_kv*d  ->  [h_kv][d][L_n]
- *                     (d-major: one row of L_n tokens per channel)
- *   Local K           [n_seq][h_kv][L][d]           (rotated at pos0 + j)
- *   Local V           [n_seq][h_kv][d][loc_stride]  (loc_stride >= L, % 8 == 0)
+ *   Document V store  v_store + kv_off[n]*h_kv*d  ->  [h_kv][L_n/64][d][64]
+ *                     (tile-blocked: each 64-token tile is stored channel-major,
+ *                     one contiguous 16 KiB block per head in bf16)
+ *   Local K           [n_seq][h_kv][L][d]            (rotated at pos0 + j)
+ *   Local V           [n_seq][h_kv][ceil(L/64)][d][64]  (tile-blocked, tokens past
+ *                     L in the last tile are zero)
  *   Raw per-token inputs (what a model emits): [tokens][heads][128].
  */
 #ifndef MSA_H
@@ -121,9 +123,8 @@ typedef struct {
   int32_t k;                 /* documents per group, >= 0 */
   int32_t block;             /* prefill: queries per routing group (n_q % block == 0) */
   const void* k_loc;         /* device local K [n_seq][h_kv][L_loc][d] (prepared) */
-  const void* v_loc;         /* device local V [n_seq][h_kv][d][loc_stride] (prepared) */
+  const void* v_loc;         /* device local V [n_seq][h_kv][ceil(L_loc/64)][d][64] (prepared) */
   int32_t L_loc;             /* local tokens, >= 0 (decode: n_seq = n_q; prefill: n_seq = 1) */
-  int32_t loc_stride;        /* >= L_loc, % 8 == 0 */
   float* out;                /* device [n_q][h_q][d] float32 */
   void* ws;                  /* device workspace */
   size_t ws_bytes;
@@ -152,7 +153,6 @@ typedef struct {
   const void* k_loc;         /* prepared local context, as in msa_attend_args */
   const void* v_loc;
   int32_t L_loc;
-  int32_t loc_stride;
   int32_t hops;              /* >= 1; > 1 needs h_r == 1 and w_proj (decode only) */
   const float* w_proj;       /* device [d_r][h_q*d] float32: next hop's router query is
                                 w_proj times the concatenated per-head outputs */
@@ -206,11 +206,11 @@ int msa_build_bank(const msa_bank* bank, int32_t doc_begin, int32_t doc_end,
  * card, "Pułapki implementacyjne": global RoPE with an offset for the
  * active context) and lay K and V out for the attention kernels.
  *   k_raw, v_raw: device [n_seq][L][h_kv][d] dtype.
- *   k_loc: device [n_seq][h_kv][L][d]; v_loc: device [n_seq][h_kv][d][loc_stride],
- *   columns L..loc_stride-1 are zero-filled. */
+ *   k_loc: device [n_seq][h_kv][L][d];
+ *   v_loc: device [n_seq][h_kv][ceil(L/64)][d][64], tokens past L zero-filled. */
 int msa_prepare_local(const msa_bank* bank, const void* k_raw, const void* v_raw,
                       int32_t n_seq, int32_t L, int32_t pos0,
-                      void* k_loc, void* v_loc, int32_t loc_stride, void* stream);
+                      void* k_loc, void* v_loc, void* stream);
 
 /* Workspace bytes msa_route / msa_attend / msa_step need for these sizes.
  * mode: MSA_DECODE or MSA_PREFILL; n_q, h_q, k as in the args; hops >= 1. */

@@ -51,7 +51,8 @@ WsLayout ws_layout(const Bank& bk, int mode, int n_q, int h_q, int k, int block,
     return o;
   };
   L.piecemax = take((size_t)bk.desc.h_r * bk.n_pieces * n_groups * sizeof(float));
-  L.keys = take((size_t)n_groups * bk.desc.n_docs * sizeof(uint64_t));
+  L.keys = take((size_t)n_groups * topk_scratch_keys(bk.desc.n_docs, std::max(k, 1)) *
+                sizeof(uint64_t));
   L.qroute = take((size_t)n_groups * bk.desc.h_r * kD * sizeof(float));
   L.qrot = take((size_t)n_q * h_q * kD * esz);
   const int G = std::max(1, h_q / bk.desc.h_kv);
@@ -65,6 +66,8 @@ WsLayout ws_layout(const Bank& bk, int mode, int n_q, int h_q, int k, int block,
   return L;
 }
 
+constexpr int kMaxSplits = 256;
+
 int resolve_splits(const Bank& bk, int splits, int n_q, int k, int L_loc) {
   if (splits > 0) return ((splits + 3) / 4) * 4;
   return decode_auto_splits(bk, n_q, k, L_loc);
@@ -73,7 +76,7 @@ int resolve_splits(const Bank& bk, int splits, int n_q, int k, int L_loc) {
 const Bank* as_bank(const msa_bank* b) { return reinterpret_cast<const Bank*>(b); }
 
 int check_attend_common(const Bank& bk, int mode, int n_q, int h_q, int k, int block, int L_loc,
-                        int loc_stride, const void* k_loc, const void* v_loc) {
+                        const void* k_loc, const void* v_loc) {
   if (mode != MSA_DECODE && mode != MSA_PREFILL) return fail(MSA_EINVAL, "mode");
   if (n_q < 0) return fail(MSA_EINVAL, "n_q < 0");
   if (h_q <= 0 || h_q % bk.desc.h_kv) return fail(MSA_EINVAL, "h_q must be a multiple of h_kv");
@@ -84,10 +87,7 @@ int check_attend_common(const Bank& bk, int mode, int n_q, int h_q, int k, int b
   if (mode == MSA_PREFILL && (block <= 0 || n_q % block))
     return fail(MSA_EINVAL, "prefill: n_q must be a positive multiple of block");
   if (L_loc < 0) return fail(MSA_EINVAL, "L_loc < 0");
-  if (L_loc > 0) {
-    if (!k_loc || !v_loc) return fail(MSA_EINVAL, "local K/V pointers are NULL");
-    if (loc_stride < L_loc || loc_stride % 8) return fail(MSA_EINVAL, "loc_stride");
-  }
+  if (L_loc > 0 && (!k_loc || !v_loc)) return fail(MSA_EINVAL, "local K/V pointers are NULL");
   if (mode == MSA_PREFILL && L_loc < n_q)
     return fail(MSA_EINVAL, "prefill: the queries are the last n_q local tokens (L_loc >= n_q)");
   return MSA_OK;
@@ -279,16 +279,14 @@ int msa_build_bank(const msa_bank* b, int32_t doc0, int32_t doc1, const void* ro
 }
 
 int msa_prepare_local(const msa_bank* b, const void* k_raw, const void* v_raw, int32_t n_seq,
-                      int32_t L, int32_t pos0, void* k_loc, void* v_loc, int32_t loc_stride,
-                      void* stream) {
+                      int32_t L, int32_t pos0, void* k_loc, void* v_loc, void* stream) {
   if (!b) return fail(MSA_EINVAL, "NULL bank");
   if (n_seq < 0 || L < 0) return fail(MSA_EINVAL, "n_seq / L");
   if (pos0 < 0) return fail(MSA_EINVAL, "pos0 < 0");
-  if (loc_stride < L || loc_stride % 8) return fail(MSA_EINVAL, "loc_stride must be >= L and % 8 == 0");
-  if (n_seq == 0 || loc_stride == 0) return MSA_OK;
-  if (!v_loc || (L > 0 && (!k_loc || !k_raw || !v_raw))) return fail(MSA_EINVAL, "NULL pointer");
+  if (n_seq == 0 || L == 0) return MSA_OK;
+  if (!k_loc || !v_loc || !k_raw || !v_raw) return fail(MSA_EINVAL, "NULL pointer");
   MSA_CHECK_HIP(launch_prepare_local(*as_bank(b), k_raw, v_raw, n_seq, L, pos0, k_loc, v_loc,
-                                     loc_stride, (hipStream_t)stream));
+                                     (hipStream_t)stream));
   return MSA_OK;
 }
 
@@ -315,10 +313,11 @@ int msa_route(const msa_bank* b, const float* q_route, int32_t B, int32_t k,
   const Bank& bk = *as_bank(b);
   if (B < 0) return fail(MSA_EINVAL, "B < 0");
   if (k < 1 || k > bk.desc.n_docs) return fail(MSA_EINVAL, "k must be in [1, n_docs]");
+  if (k > kMaxK) return fail(MSA_EUNSUPPORTED, "k must be <= 64");
   if (B == 0) return MSA_OK;
   if (!q_route || !ids || !scores || !ws) return fail(MSA_EINVAL, "NULL pointer");
   const WsLayout L = ws_layout(bk, MSA_DECODE, B, bk.desc.h_kv, k, 1, 1, 4);
-  const size_t need = L.keys + align256((size_t)B * bk.desc.n_docs * 8);
+  const size_t need = L.keys + align256((size_t)B * topk_scratch_keys(bk.desc.n_docs, k) * 8);
   if (ws_bytes < need) return fail(MSA_ENOMEM, "workspace too small for msa_route");
   char* w = (char*)ws;
   hipStream_t s = (hipStream_t)stream;
@@ -331,8 +330,8 @@ int msa_route(const msa_bank* b, const float* q_route, int32_t B, int32_t k,
 int msa_attend(const msa_bank* b, const msa_attend_args* a, void* stream) {
   if (!b || !a) return fail(MSA_EINVAL, "NULL bank or args");
   const Bank& bk = *as_bank(b);
-  int st = check_attend_common(bk, a->mode, a->n_q, a->h_q, a->k, a->block, a->L_loc,
-                               a->loc_stride, a->k_loc, a->v_loc);
+  int st = check_attend_common(bk, a->mode, a->n_q, a->h_q, a->k, a->block, a->L_loc, a->k_loc,
+                               a->v_loc);
   if (st) return st;
   if (a->n_q == 0) return MSA_OK;
   if (!a->q || !a->out || !a->ws || (a->k > 0 && !a->ids)) return fail(MSA_EINVAL, "NULL pointer");
@@ -345,6 +344,7 @@ int msa_attend(const msa_bank* b, const msa_attend_args* a, void* stream) {
   } else if (bk.desc.kv_loc != MSA_KV_DEVICE && a->k > 0) {
     return fail(MSA_EUNSUPPORTED, "host-resident bank: use msa_step or a source override");
   }
+  if (a->splits < 0 || a->splits > kMaxSplits) return fail(MSA_EINVAL, "splits must be in [0, 256]");
   const int splits = resolve_splits(bk, a->splits, a->n_q, a->k, a->L_loc);
   const WsLayout L = ws_layout(bk, a->mode, a->n_q, a->h_q, a->k, a->block, 1, splits);
   if (a->ws_bytes < L.total) return fail(MSA_ENOMEM, "workspace too small for msa_attend");
@@ -355,12 +355,11 @@ int msa_attend(const msa_bank* b, const msa_attend_args* a, void* stream) {
                                     w + L.qrot, s));
   if (prefill)
     MSA_CHECK_HIP(launch_prefill(bk, w + L.qrot, a->n_q, a->h_q, a->ids, a->k, a->block, src,
-                                 a->k_loc, a->v_loc, a->L_loc, a->loc_stride, splits,
-                                 (float*)(w + L.part), a->out, s));
+                                 a->k_loc, a->v_loc, a->L_loc, splits, (float*)(w + L.part),
+                                 a->out, s));
   else
     MSA_CHECK_HIP(launch_decode(bk, w + L.qrot, a->n_q, a->h_q, a->ids, a->k, src, a->k_loc,
-                                a->v_loc, a->L_loc, a->loc_stride, splits, (float*)(w + L.part),
-                                a->out, s));
+                                a->v_loc, a->L_loc, splits, (float*)(w + L.part), a->out, s));
   return MSA_OK;
 }
 
@@ -369,8 +368,8 @@ int msa_step(const msa_bank* b, const msa_step_args* a, void* stream, void* copy
   if (!b || !a) return fail(MSA_EINVAL, "NULL bank or args");
   Bank& bk = *const_cast<Bank*>(as_bank(b));
   const int N = bk.desc.n_docs;
-  int st = check_attend_common(bk, a->mode, a->n_q, a->h_q, a->k, a->block, a->L_loc,
-                               a->loc_stride, a->k_loc, a->v_loc);
+  int st = check_attend_common(bk, a->mode, a->n_q, a->h_q, a->k, a->block, a->L_loc, a->k_loc,
+                               a->v_loc);
   if (st) return st;
   if (a->k < 1 || a->k > N) return fail(MSA_EINVAL, "k must be in [1, n_docs]");
   if (a->hops < 1) return fail(MSA_EINVAL, "hops must be >= 1");
@@ -388,6 +387,7 @@ int msa_step(const msa_bank* b, const msa_step_args* a, void* stream, void* copy
   const bool host = bk.desc.kv_loc == MSA_KV_HOST;
   const int n_groups = prefill ? a->n_q / a->block : a->n_q;
   const int k = a->k;
+  if (a->splits < 0 || a->splits > kMaxSplits) return fail(MSA_EINVAL, "splits must be in [0, 256]");
   const int splits = resolve_splits(bk, a->splits, a->n_q, k, a->L_loc);
   const WsLayout L = ws_layout(bk, a->mode, a->n_q, a->h_q, k, a->block, a->hops, splits);
   if (a->ws_bytes < L.total) return fail(MSA_ENOMEM, "workspace too small for msa_step");
@@ -505,12 +505,11 @@ int msa_step(const msa_bank* b, const msa_step_args* a, void* stream, void* copy
     }
     if (prefill)
       MSA_CHECK_HIP(launch_prefill(bk, w + L.qrot, a->n_q, a->h_q, att_ids, k, a->block, src,
-                                   a->k_loc, a->v_loc, a->L_loc, a->loc_stride, splits,
-                                   (float*)(w + L.part), out, s));
+                                   a->k_loc, a->v_loc, a->L_loc, splits, (float*)(w + L.part), out,
+                                   s));
     else
       MSA_CHECK_HIP(launch_decode(bk, w + L.qrot, a->n_q, a->h_q, att_ids, k, src, a->k_loc,
-                                  a->v_loc, a->L_loc, a->loc_stride, splits, (float*)(w + L.part),
-                                  out, s));
+                                  a->v_loc, a->L_loc, splits, (float*)(w + L.part), out, s));
     if (hop + 1 < a->hops) {
       MSA_CHECK_HIP(launch_project(out, a->w_proj, a->n_q, a->h_q * kD, kD, q_route, s));
       qr = q_route;

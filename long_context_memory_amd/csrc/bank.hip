@@ -4,8 +4,8 @@
 //     accumulated in float64, rounded once to the storage type, plus the
 //     inverse norm of the rounded key;
 //   - document K/V store: K rotated at document-local positions (document-wise
-//     RoPE, "MSA" card, robocikowo.com, "Komponenty"), V transposed to the
-//     channel-major layout the attention kernels stream;
+//     RoPE, "MSA" card, robocikowo.com, "Komponenty"), V laid out as
+//     channel-major 64-token tiles, the blocks the attention kernels stream;
 //   - local context: K rotated at global positions pos0 + j (global RoPE with
 //     an offset, same card, "Pułapki implementacyjne");
 //   - queries: rotated at their positions and pre-scaled by log2(e)/sqrt(d) so
@@ -174,27 +174,20 @@ __global__ __launch_bounds__(256) void rotate_k_kernel(const T* __restrict__ in,
 }
 
 // ---------------------------------------------------------------- V transpose
-// One workgroup per (tile of 64 tokens, head): [64 tokens][128] -> rows of the
-// channel-major output.  Local mode tiles cover loc_stride columns and write
-// zeros past L.
+// One workgroup per (tile of 64 tokens, head): [64 tokens][128] -> the tile's
+// channel-major block [128][64] (tokens past the end of a local sequence are
+// written as zeros).
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_v_kernel(const T* __restrict__ in,
-                                                          T* __restrict__ out, KLayout ly,
-                                                          int out_stride_local) {
+                                                          T* __restrict__ out, KLayout ly) {
   const int h = blockIdx.y;
-  TileInfo ti;
-  int row_stride;
+  const TileInfo ti = tile_info(ly, blockIdx.x);
+  size_t blk;  // element offset of the tile block
   if (ly.mode == 0) {
-    ti = tile_info(ly, blockIdx.x);
-    row_stride = ti.seg_len;
+    blk = (size_t)ti.out_base + ((size_t)h * ti.seg_len + ti.t0) * kD;
   } else {
-    const int tps = (out_stride_local + kAttnTile - 1) / kAttnTile;
-    const int s = blockIdx.x / tps;
-    ti.t0 = (blockIdx.x % tps) * kAttnTile;
-    ti.in_row0 = (int64_t)s * ly.L + ti.t0;
-    ti.out_base = (int64_t)s * ly.h_kv * kD * out_stride_local;
-    ti.n_valid = max(0, min(kAttnTile, ly.L - ti.t0));
-    row_stride = out_stride_local;
+    const int s = blockIdx.x / ly.tiles_per_seq, m = blockIdx.x % ly.tiles_per_seq;
+    blk = (((size_t)s * ly.h_kv + h) * ly.tiles_per_seq + m) * kAttnTile * kD;
   }
   __shared__ T tile[kAttnTile][kD + 2];
   for (int e = threadIdx.x; e < kAttnTile * kD; e += 256) {
@@ -203,11 +196,10 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const T* __restrict__ 
                                 : (T)0;
   }
   __syncthreads();
-  const int ncols = ly.mode == 0 ? kAttnTile : min(kAttnTile, row_stride - ti.t0);
-  T* dst = out + ti.out_base + (size_t)h * kD * row_stride + ti.t0;
+  T* dst = out + blk;
   for (int e = threadIdx.x; e < kAttnTile * kD; e += 256) {
     const int i = e / kAttnTile, t = e % kAttnTile;
-    if (t < ncols) dst[(size_t)i * row_stride + t] = tile[t][i];
+    dst[(size_t)i * kAttnTile + t] = tile[t][i];
   }
 }
 
@@ -217,17 +209,18 @@ __global__ __launch_bounds__(256) void rope_queries_kernel(const T* __restrict__
                                                            int h_q, int pos0, int pos_step,
                                                            const double* __restrict__ inv_freq,
                                                            double scale, T* __restrict__ out) {
+  // one thread per (query row, head, channel pair)
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)n_q * 64) return;
-  const int i = (int)(idx >> 6), pair = (int)(idx & 63);
+  if (idx >= (int64_t)n_q * h_q * 64) return;
+  const int pair = (int)(idx & 63);
+  const int64_t row = idx >> 6;  // i * h_q + h
+  const int i = (int)(row / h_q);
   double sn, cs;
   sincos((double)(pos0 + (int64_t)i * pos_step) * inv_freq[pair], &sn, &cs);
-  for (int h = 0; h < h_q; ++h) {
-    const size_t o = ((size_t)i * h_q + h) * kD;
-    const double x1 = St<T>::load(q[o + pair]), x2 = St<T>::load(q[o + 64 + pair]);
-    out[o + pair] = St<T>::store((x1 * cs - x2 * sn) * scale);
-    out[o + 64 + pair] = St<T>::store((x2 * cs + x1 * sn) * scale);
-  }
+  const size_t o = (size_t)row * kD;
+  const double x1 = St<T>::load(q[o + pair]), x2 = St<T>::load(q[o + 64 + pair]);
+  out[o + pair] = St<T>::store((x1 * cs - x2 * sn) * scale);
+  out[o + 64 + pair] = St<T>::store((x2 * cs + x1 * sn) * scale);
 }
 
 KLayout bank_layout(const Bank& bk, int doc0, int doc1) {
@@ -285,41 +278,36 @@ hipError_t launch_store_kv(const Bank& bk, int doc0, int doc1, const void* k_raw
     hipLaunchKernelGGL(rotate_k_kernel<uint16_t>, dim3(tiles), dim3(256), 0, s,
                        (const uint16_t*)k_raw, (uint16_t*)bk.desc.k_store, ly, bk.d_inv_freq);
     hipLaunchKernelGGL(transpose_v_kernel<uint16_t>, dim3(tiles, bk.desc.h_kv), dim3(256), 0, s,
-                       (const uint16_t*)v_raw, (uint16_t*)bk.desc.v_store, ly, 0);
+                       (const uint16_t*)v_raw, (uint16_t*)bk.desc.v_store, ly);
   } else {
     hipLaunchKernelGGL(rotate_k_kernel<float>, dim3(tiles), dim3(256), 0, s,
                        (const float*)k_raw, (float*)bk.desc.k_store, ly, bk.d_inv_freq);
     hipLaunchKernelGGL(transpose_v_kernel<float>, dim3(tiles, bk.desc.h_kv), dim3(256), 0, s,
-                       (const float*)v_raw, (float*)bk.desc.v_store, ly, 0);
+                       (const float*)v_raw, (float*)bk.desc.v_store, ly);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_prepare_local(const Bank& bk, const void* k_raw, const void* v_raw, int n_seq,
-                                int L, int pos0, void* k_loc, void* v_loc, int loc_stride,
-                                hipStream_t s) {
+                                int L, int pos0, void* k_loc, void* v_loc, hipStream_t s) {
   KLayout ly{};
   ly.mode = 1;
   ly.L = L;
   ly.pos0 = pos0;
   ly.tiles_per_seq = (L + kAttnTile - 1) / kAttnTile;
   ly.h_kv = bk.desc.h_kv;
-  const unsigned ktiles = (unsigned)(n_seq * ly.tiles_per_seq);
-  const unsigned vtiles = (unsigned)(n_seq * ((loc_stride + kAttnTile - 1) / kAttnTile));
+  const unsigned tiles = (unsigned)(n_seq * ly.tiles_per_seq);
+  if (tiles == 0) return hipSuccess;
   if (bk.desc.dtype == MSA_BF16) {
-    if (ktiles)
-      hipLaunchKernelGGL(rotate_k_kernel<uint16_t>, dim3(ktiles), dim3(256), 0, s,
-                         (const uint16_t*)k_raw, (uint16_t*)k_loc, ly, bk.d_inv_freq);
-    if (vtiles)
-      hipLaunchKernelGGL(transpose_v_kernel<uint16_t>, dim3(vtiles, bk.desc.h_kv), dim3(256), 0,
-                         s, (const uint16_t*)v_raw, (uint16_t*)v_loc, ly, loc_stride);
+    hipLaunchKernelGGL(rotate_k_kernel<uint16_t>, dim3(tiles), dim3(256), 0, s,
+                       (const uint16_t*)k_raw, (uint16_t*)k_loc, ly, bk.d_inv_freq);
+    hipLaunchKernelGGL(transpose_v_kernel<uint16_t>, dim3(tiles, bk.desc.h_kv), dim3(256), 0, s,
+                       (const uint16_t*)v_raw, (uint16_t*)v_loc, ly);
   } else {
-    if (ktiles)
-      hipLaunchKernelGGL(rotate_k_kernel<float>, dim3(ktiles), dim3(256), 0, s,
-                         (const float*)k_raw, (float*)k_loc, ly, bk.d_inv_freq);
-    if (vtiles)
-      hipLaunchKernelGGL(transpose_v_kernel<float>, dim3(vtiles, bk.desc.h_kv), dim3(256), 0, s,
-                         (const float*)v_raw, (float*)v_loc, ly, loc_stride);
+    hipLaunchKernelGGL(rotate_k_kernel<float>, dim3(tiles), dim3(256), 0, s,
+                       (const float*)k_raw, (float*)k_loc, ly, bk.d_inv_freq);
+    hipLaunchKernelGGL(transpose_v_kernel<float>, dim3(tiles, bk.desc.h_kv), dim3(256), 0, s,
+                       (const float*)v_raw, (float*)v_loc, ly);
   }
   return hipGetLastError();
 }
@@ -328,7 +316,7 @@ hipError_t launch_rope_queries(const Bank& bk, const void* q, int n_q, int h_q, 
                                int pos_step, void* q_rot, hipStream_t s) {
   if (n_q == 0) return hipSuccess;
   const double scale = 1.4426950408889634 / sqrt((double)kD);  // log2(e) / sqrt(d)
-  const unsigned grid = (unsigned)(((int64_t)n_q * 64 + 255) / 256);
+  const unsigned grid = (unsigned)(((int64_t)n_q * h_q * 64 + 255) / 256);
   if (bk.desc.dtype == MSA_BF16)
     hipLaunchKernelGGL(rope_queries_kernel<uint16_t>, dim3(grid), dim3(256), 0, s,
                        (const uint16_t*)q, n_q, h_q, pos0, pos_step, bk.d_inv_freq, scale,

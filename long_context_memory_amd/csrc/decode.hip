@@ -14,10 +14,10 @@
 //     lane, fully used 128-byte lines; bf16 pair dots (v_dot2_f32_bf16, fp32
 //     accumulate) against register-resident query fragments, then a three-step
 //     DPP transpose-reduce leaves lane l with the G scores of one token.
-//   - V tile [128 ch][64 tok] (channel-major store): 8 lanes per channel row,
-//     8 tokens per lane; each lane keeps its 16 rows x G accumulators for the
-//     whole range and contracts over its 8 tokens with bf16 pair dots against
-//     probabilities staged (as bf16) in a per-wave LDS slot.  The 8-lane
+//   - V tile [128 ch][64 tok] (channel-major store): 4 lanes per channel row,
+//     16 tokens per lane; each lane keeps its 8 rows x G accumulators for the
+//     whole range and contracts over its 16 tokens with bf16 pair dots against
+//     probabilities staged (as bf16) in a per-wave LDS slot.  The 4-lane
 //     reduction of the accumulators happens once, at the end.
 //   - the "gather" is an indirection: per (query, head) the workgroup reads
 //     the k selected ids and the document table and walks the tiles in place.
@@ -38,7 +38,7 @@ struct DecodeP {
   int n_src;
   const void* kl;
   const void* vl;
-  int k, L_loc, loc_stride, h_kv, S, h_q;
+  int k, L_loc, h_kv, S, h_q;
   int id_div;      // queries per id row (decode 1; prefill: the routing block)
   int loc_shared;  // 1: every query reads local sequence 0 (prefill)
   int causal_off;  // < 0: none; else query b sees local tokens j < causal_off + b + 1
@@ -59,8 +59,12 @@ __device__ __forceinline__ void treduce(float (&a)[N], int n, bool upper) {
 #pragma unroll
   for (int i = 0; i < N / 2; ++i) {
     if (i < half) {
-      const float send = upper ? a[i] : a[i + half];
-      const float keep = upper ? a[i + half] : a[i];
+      float lo = a[i], hi = a[i + half];
+      // opaque copies: keeps the compiler from turning the selects below
+      // into a lane-varying index into a[] (a compare/select chain)
+      asm volatile("" : "+v"(lo), "+v"(hi));
+      const float send = upper ? lo : hi;
+      const float keep = upper ? hi : lo;
       a[i] = keep + dpp_f<CTRL>(send);
     }
   }
@@ -77,11 +81,12 @@ template <typename T, int G>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeP p) {
   constexpr bool kBF = sizeof(T) == 2;
   const int b = blockIdx.z, h = blockIdx.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int split = blockIdx.x * 4 + wave;
 
   __shared__ int64_t s_koff[kMaxK + 1], s_voff[kMaxK + 1];
-  __shared__ int s_len[kMaxK + 1], s_vstr[kMaxK + 1], s_tile0[kMaxK + 2];
+  __shared__ int s_len[kMaxK + 1], s_tile0[kMaxK + 2];
   __shared__ __attribute__((aligned(16))) T s_p[4][G][kAttnTile];
 
   const int k = p.k;
@@ -97,13 +102,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeP p) {
     s_len[threadIdx.x] = L;
     s_koff[threadIdx.x] = o;
     s_voff[threadIdx.x] = o;
-    s_vstr[threadIdx.x] = L;
   } else if ((int)threadIdx.x == k) {
     const int64_t seq = p.loc_shared ? 0 : b;
+    const int64_t tp = (p.L_loc + kAttnTile - 1) / kAttnTile;  // padded local tiles
     s_len[k] = p.causal_off < 0 ? p.L_loc : min(p.L_loc, p.causal_off + b + 1);
     s_koff[k] = (seq * p.h_kv + h) * p.L_loc * kD;
-    s_voff[k] = (seq * p.h_kv + h) * kD * p.loc_stride;
-    s_vstr[k] = p.loc_stride;
+    s_voff[k] = (seq * p.h_kv + h) * tp * kAttnTile * kD;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -116,7 +120,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeP p) {
   }
   __syncthreads();
 
-  const int NT = s_tile0[k + 1];
+  const int NT = __builtin_amdgcn_readfirstlane(s_tile0[k + 1]);
   const int u0 = (int)((int64_t)NT * split / p.S);
   const int u1 = (int)((int64_t)NT * (split + 1) / p.S);
   const int j = lane & 7, g8 = lane >> 3;
@@ -134,50 +138,70 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeP p) {
       qf[g][c] = *reinterpret_cast<const uint4*>(qrow + (size_t)g * kD +
                                                  (kBF ? (c * 64 + 8 * j) : (c * 32 + 4 * j)));
 
-  float m_run[G], l_run[G], o[16 * G];
+  float m_run[G], l_run[G], o[8 * G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     m_run[g] = -INFINITY;
     l_run[g] = 0.f;
   }
 #pragma unroll
-  for (int i = 0; i < 16 * G; ++i) o[i] = 0.f;
+  for (int i = 0; i < 8 * G; ++i) o[i] = 0.f;
+  const int c4 = lane & 3, r0 = lane >> 2;  // PV: token chunk c4 (16 tokens), row r0
 
   int r = 0;
   for (int u = u0; u < u1; ++u) {
-    while (u >= s_tile0[r + 1]) ++r;
-    const int t0 = (u - s_tile0[r]) * kAttnTile;
-    const int nvalid = min(kAttnTile, s_len[r] - t0);
+    while (u >= __builtin_amdgcn_readfirstlane(s_tile0[r + 1])) ++r;
+    const int t0 = (u - __builtin_amdgcn_readfirstlane(s_tile0[r])) * kAttnTile;
+    const int nvalid = min(kAttnTile, __builtin_amdgcn_readfirstlane(s_len[r]) - t0);
     const bool loc = r == k;
-    const T* kb = (const T*)(loc ? p.kl : p.ks) + s_koff[r] + (size_t)t0 * kD;
-    const T* vb = (const T*)(loc ? p.vl : p.vs) + s_voff[r] + t0;
-    const int vstr = s_vstr[r];
+    const int64_t koff = ((int64_t)__builtin_amdgcn_readfirstlane((int)(s_koff[r] >> 32)) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane((int)s_koff[r]);
+    const int64_t voff = ((int64_t)__builtin_amdgcn_readfirstlane((int)(s_voff[r] >> 32)) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane((int)s_voff[r]);
+    const T* kb = (const T*)(loc ? p.kl : p.ks) + koff + (size_t)t0 * kD;
+    const T* vb = (const T*)(loc ? p.vl : p.vs) + voff + (size_t)t0 * kD;  // [128][64] block
 
-    // ---- loads: K 8 token rows x QV vectors, V 16 channel rows x (1|2) vectors
+    // ---- loads: K 8 token rows x QV vectors; V 8 channel rows x VV vectors.
+    // Document tiles are always full (lengths are multiples of 256); only a
+    // ragged local tail takes the guarded path.
+    constexpr int VV = kBF ? 2 : 4;  // 16-byte vectors per lane per row (16 tokens)
     uint4 kv[8][QV];
+    uint4 vv[8][VV];
+    const bool vok = 16 * c4 < nvalid;
+    if (nvalid == kAttnTile) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int tt = 8 * s + g8;
+      for (int s = 0; s < 8; ++s)
 #pragma unroll
-      for (int c = 0; c < QV; ++c) {
-        kv[s][c] = make_uint4(0, 0, 0, 0);
-        if (tt < nvalid)
-          kv[s][c] = *reinterpret_cast<const uint4*>(kb + (size_t)tt * kD +
+        for (int c = 0; c < QV; ++c)
+          kv[s][c] = *reinterpret_cast<const uint4*>(kb + (size_t)(8 * s + g8) * kD +
                                                      (kBF ? (c * 64 + 8 * j) : (c * 32 + 4 * j)));
-      }
-    }
-    constexpr int VV = kBF ? 1 : 2;
-    uint4 vv[16][VV];
-    const bool vok = 8 * j < nvalid;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int d = 8 * i + g8;
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int c = 0; c < VV; ++c) {
-        vv[i][c] = make_uint4(0, 0, 0, 0);
-        if (vok)
-          vv[i][c] = *reinterpret_cast<const uint4*>(vb + (size_t)d * vstr + 8 * j + c * 4);
+        for (int c = 0; c < VV; ++c)
+          vv[i][c] = *reinterpret_cast<const uint4*>(vb + (16 * i + r0) * kAttnTile + 16 * c4 +
+                                                     c * (16 / (int)sizeof(T)));
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int tt = 8 * s + g8;
+#pragma unroll
+        for (int c = 0; c < QV; ++c) {
+          kv[s][c] = make_uint4(0, 0, 0, 0);
+          if (tt < nvalid)
+            kv[s][c] = *reinterpret_cast<const uint4*>(
+                kb + (size_t)tt * kD + (kBF ? (c * 64 + 8 * j) : (c * 32 + 4 * j)));
+        }
       }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int c = 0; c < VV; ++c) {
+          vv[i][c] = make_uint4(0, 0, 0, 0);
+          if (vok)
+            vv[i][c] = *reinterpret_cast<const uint4*>(vb + (16 * i + r0) * kAttnTile +
+                                                       16 * c4 + c * (16 / (int)sizeof(T)));
+        }
     }
 
     // ---- scores: partial dots over this lane's 16 channels
@@ -225,22 +249,22 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeP p) {
       l_run[g] = l_run[g] * alpha + pq;
       m_run[g] = m_new;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[i * G + g] *= alpha;
+      for (int i = 0; i < 8; ++i) o[i * G + g] *= alpha;
     }
     wave_lds_sync();
 
-    // ---- values: zero channels past the end of a ragged tail
-    if (nvalid < kAttnTile && vok && nvalid - 8 * j < 8) {
-      const int nv = nvalid - 8 * j;
+    // ---- values: zero tokens past the end of a ragged tail
+    if (nvalid < kAttnTile && vok && nvalid - 16 * c4 < 16) {
+      const int nv = nvalid - 16 * c4;
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int c = 0; c < VV; ++c) {
           uint32_t* w = reinterpret_cast<uint32_t*>(&vv[i][c]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             if constexpr (kBF) {
-              const int t = 2 * e;
+              const int t = c * 8 + 2 * e;
               if (t >= nv) w[e] = 0;
               else if (t + 1 >= nv) w[e] &= 0xffffu;
             } else {
@@ -251,49 +275,45 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeP p) {
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      if constexpr (kBF) {
-        const uint4 pp = *reinterpret_cast<const uint4*>(&s_p[wave][g][8 * j]);
+      uint4 pp[VV];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float a = o[i * G + g];
-          a = dot2_bf16(vv[i][0].x, pp.x, a);
-          a = dot2_bf16(vv[i][0].y, pp.y, a);
-          a = dot2_bf16(vv[i][0].z, pp.z, a);
-          a = dot2_bf16(vv[i][0].w, pp.w, a);
-          o[i * G + g] = a;
-        }
-      } else {
-        const float4 p0 = *reinterpret_cast<const float4*>(&s_p[wave][g][8 * j]);
-        const float4 p1 = *reinterpret_cast<const float4*>(&s_p[wave][g][8 * j + 4]);
+      for (int c = 0; c < VV; ++c)
+        pp[c] = *reinterpret_cast<const uint4*>(&s_p[wave][g][16 * c4 + c * (16 / (int)sizeof(T))]);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float a = o[i * G + g];
-          a = fmaf(__uint_as_float(vv[i][0].x), p0.x, a);
-          a = fmaf(__uint_as_float(vv[i][0].y), p0.y, a);
-          a = fmaf(__uint_as_float(vv[i][0].z), p0.z, a);
-          a = fmaf(__uint_as_float(vv[i][0].w), p0.w, a);
-          a = fmaf(__uint_as_float(vv[i][1].x), p1.x, a);
-          a = fmaf(__uint_as_float(vv[i][1].y), p1.y, a);
-          a = fmaf(__uint_as_float(vv[i][1].z), p1.z, a);
-          a = fmaf(__uint_as_float(vv[i][1].w), p1.w, a);
-          o[i * G + g] = a;
+      for (int i = 0; i < 8; ++i) {
+        float a = o[i * G + g];
+#pragma unroll
+        for (int c = 0; c < VV; ++c) {
+          if constexpr (kBF) {
+            a = dot2_bf16(vv[i][c].x, pp[c].x, a);
+            a = dot2_bf16(vv[i][c].y, pp[c].y, a);
+            a = dot2_bf16(vv[i][c].z, pp[c].z, a);
+            a = dot2_bf16(vv[i][c].w, pp[c].w, a);
+          } else {
+            a = fmaf(__uint_as_float(vv[i][c].x), __uint_as_float(pp[c].x), a);
+            a = fmaf(__uint_as_float(vv[i][c].y), __uint_as_float(pp[c].y), a);
+            a = fmaf(__uint_as_float(vv[i][c].z), __uint_as_float(pp[c].z), a);
+            a = fmaf(__uint_as_float(vv[i][c].w), __uint_as_float(pp[c].w), a);
+          }
         }
+        o[i * G + g] = a;
       }
     }
     wave_lds_sync();  // probabilities consumed before the next tile overwrites them
   }
 
-  // ---- wave epilogue: total l, 8-lane reduction of the accumulators
+  // ---- wave epilogue: total l, 4-lane reduction of the accumulators
   float l_tot[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) l_tot[g] = wave_sum(l_run[g]);
-  treduce8<16 * G>(o, j);  // lane keeps o indices [2G*j, 2G*j + 2G)
+  treduce<kDppXor2, 8 * G>(o, 8 * G, (c4 & 2) != 0);
+  treduce<kDppXor1, 8 * G>(o, 4 * G, (c4 & 1) != 0);  // lane keeps o indices [2G*c4, 2G*c4 + 2G)
   const size_t pbase = (((size_t)b * p.h_kv + h) * p.S + split) * G;
 #pragma unroll
   for (int e = 0; e < 2 * G; ++e) {
-    const int idx = 2 * G * j + e;
+    const int idx = 2 * G * c4 + e;
     const int i = idx / G, g = idx % G;
-    p.part[(pbase + g) * (kD + 2) + 2 + 8 * i + g8] = o[e];
+    p.part[(pbase + g) * (kD + 2) + 2 + 16 * i + r0] = o[e];
   }
 #pragma unroll
   for (int g = 0; g < G; ++g)
@@ -303,25 +323,55 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeP p) {
     }
 }
 
-// merge the S partials of each (query, KV head): log-sum-exp in base 2
+// merge the S partials of each (query, KV head): log-sum-exp in base 2.
+// One workgroup per (KV head, query); the (split, head) weights go through
+// LDS, then each thread owns (head, channel) outputs and streams the splits.
 template <int G>
-__global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ part, int S,
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part, int S,
                                                       int h_kv, int h_q, float* __restrict__ out) {
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  constexpr int kMaxSG = 2048;
+  __shared__ float s_w[kMaxSG];
+  __shared__ float s_l[kMaxSG];
+  __shared__ float s_M[G], s_L[G];
+  const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const float* pb = part + ((size_t)b * h_kv + h) * S * G * (kD + 2);
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
+  const int SG = S * G;
+  for (int i = t; i < SG; i += 256) {
+    s_w[i] = pb[(size_t)i * (kD + 2)];
+    s_l[i] = pb[(size_t)i * (kD + 2) + 1];
+  }
+  __syncthreads();
+  if (t < G) {
     float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, pb[((size_t)s * G + g) * (kD + 2)]);
-    float L = 0.f, acc = 0.f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < S; ++s) {
-        const float* ps = pb + ((size_t)s * G + g) * (kD + 2);
-        const float w = exp2f(ps[0] - M);
-        L = fmaf(w, ps[1], L);
-        acc = fmaf(w, ps[2 + d], acc);
-      }
+    for (int s = 0; s < S; ++s) M = fmaxf(M, s_w[s * G + t]);
+    s_M[t] = M;
+  }
+  __syncthreads();
+  for (int i = t; i < SG; i += 256) {
+    const float M = s_M[i % G];
+    s_w[i] = M == -INFINITY ? 0.f : exp2f(s_w[i] - M);
+  }
+  __syncthreads();
+  if (t < G) {
+    float L = 0.f;
+    for (int s = 0; s < S; ++s) L = fmaf(s_w[s * G + t], s_l[s * G + t], L);
+    s_L[t] = L;
+  }
+  __syncthreads();
+  for (int e = t; e < G * kD; e += 256) {
+    const int g = e / kD, d = e % kD;
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int s = 0;
+    for (; s + 8 <= S; s += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = pb[((size_t)(s + u) * G + g) * (kD + 2) + 2 + d];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a[u] = fmaf(s_w[(s + u) * G + g], v[u], a[u]);
     }
+    for (; s < S; ++s) a[0] = fmaf(s_w[s * G + g], pb[((size_t)s * G + g) * (kD + 2) + 2 + d], a[0]);
+    const float acc = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+    const float L = s_L[g];
     out[((size_t)b * h_q + (size_t)h * G + g) * kD + d] = L > 0.f ? acc / L : 0.f;
   }
 }
@@ -330,7 +380,7 @@ template <typename T, int G>
 hipError_t run_decode(const DecodeP& p, int B, float* out, hipStream_t s) {
   const dim3 grid((unsigned)(p.S / 4), (unsigned)p.h_kv, (unsigned)B);
   hipLaunchKernelGGL((decode_kernel<T, G>), grid, dim3(256), 0, s, p);
-  hipLaunchKernelGGL((combine_kernel<G>), dim3((unsigned)p.h_kv, (unsigned)B), dim3(128), 0, s,
+  hipLaunchKernelGGL((combine_kernel<G>), dim3((unsigned)p.h_kv, (unsigned)B), dim3(256), 0, s,
                      p.part, p.S, p.h_kv, p.h_q, out);
   return hipGetLastError();
 }
@@ -354,8 +404,7 @@ int decode_auto_splits(const Bank& bk, int B, int k, int L_loc) {
 
 hipError_t launch_decode(const Bank& bk, const void* q_rot, int B, int h_q, const int32_t* ids,
                          int k, const AttnSources& src, const void* k_loc, const void* v_loc,
-                         int L_loc, int loc_stride, int splits, float* part, float* out,
-                         hipStream_t s) {
+                         int L_loc, int splits, float* part, float* out, hipStream_t s) {
   DecodeP p;
   p.q = q_rot;
   p.ids = ids;
@@ -368,7 +417,6 @@ hipError_t launch_decode(const Bank& bk, const void* q_rot, int B, int h_q, cons
   p.vl = v_loc;
   p.k = k;
   p.L_loc = L_loc;
-  p.loc_stride = loc_stride;
   p.h_kv = bk.desc.h_kv;
   p.S = splits;
   p.h_q = h_q;
@@ -402,8 +450,8 @@ namespace msa {
 // the MFMA kernel in prefill.hip shares them across the block.
 hipError_t launch_prefill_vector(const Bank& bk, const void* q_rot, int n_q, int h_q,
                                  const int32_t* ids, int k, int block, const AttnSources& src,
-                                 const void* k_loc, const void* v_loc, int L_loc, int loc_stride,
-                                 int splits, float* part, float* out, hipStream_t s) {
+                                 const void* k_loc, const void* v_loc, int L_loc, int splits,
+                                 float* part, float* out, hipStream_t s) {
   DecodeP p;
   p.q = q_rot;
   p.ids = ids;
@@ -416,7 +464,6 @@ hipError_t launch_prefill_vector(const Bank& bk, const void* q_rot, int n_q, int
   p.vl = v_loc;
   p.k = k;
   p.L_loc = L_loc;
-  p.loc_stride = loc_stride;
   p.h_kv = bk.desc.h_kv;
   p.S = splits;
   p.h_q = h_q;

@@ -94,13 +94,59 @@ constexpr int kDppXor1 = 0xb1;        // quad_perm(1,0,3,2)
 constexpr int kDppXor2 = 0x4e;        // quad_perm(2,3,0,1)
 constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within each 8 lanes
 
+constexpr int kDppRowMirror = 0x140;  // lane i <-> 15 - i within each 16 lanes
+
+// Wave-wide reductions (result in every lane): four DPP steps leave each
+// 16-lane row's result in all of its lanes, then the four row values are
+// read into scalars.
 __device__ __forceinline__ float wave_max(float v) {
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppRowMirror>(v));
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  v += dpp_f<kDppRowMirror>(v);
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (a + b) + (c + d);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max64_step(uint64_t v) {
+  const uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
+  const uint64_t o = ((uint64_t)dpp_u<CTRL>(hi) << 32) | dpp_u<CTRL>(lo);
+  return o > v ? o : v;
+}
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), l);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = dpp_max64_step<kDppXor1>(v);
+  v = dpp_max64_step<kDppXor2>(v);
+  v = dpp_max64_step<kDppHalfMirror>(v);
+  v = dpp_max64_step<kDppRowMirror>(v);
+  uint64_t a = readlane64(v, 0), b = readlane64(v, 16), c = readlane64(v, 32),
+           d = readlane64(v, 48);
+  a = a > b ? a : b;
+  c = c > d ? c : d;
+  return a > c ? a : c;
 }
 
 // Order-preserving map of a float onto uint32 (larger float -> larger code).
@@ -123,8 +169,7 @@ hipError_t launch_key_norms(const Bank& bk, int doc0, int doc1, hipStream_t s);
 hipError_t launch_store_kv(const Bank& bk, int doc0, int doc1, const void* k_raw,
                            const void* v_raw, hipStream_t s);
 hipError_t launch_prepare_local(const Bank& bk, const void* k_raw, const void* v_raw, int n_seq,
-                                int L, int pos0, void* k_loc, void* v_loc, int loc_stride,
-                                hipStream_t s);
+                                int L, int pos0, void* k_loc, void* v_loc, hipStream_t s);
 // queries: rotate at positions (pos0 + i*pos_step) and pre-scale by log2(e)/sqrt(d)
 hipError_t launch_rope_queries(const Bank& bk, const void* q, int n_q, int h_q, int pos0,
                                int pos_step, void* q_rot, hipStream_t s);
@@ -135,6 +180,7 @@ hipError_t launch_route_scan(const Bank& bk, const float* q_route, int B, float*
 hipError_t launch_topk(const Bank& bk, const float* piecemax, int B, int k,
                        const uint32_t* exclude, uint32_t* exclude_out, int32_t* ids,
                        float* scores, uint64_t* keys, hipStream_t s);
+size_t topk_scratch_keys(int N, int k);  // u64 keys per query launch_topk needs
 hipError_t launch_block_mean(const Bank& bk, const void* route_tokens, int n_tok, int block,
                              float* q_out, hipStream_t s);
 hipError_t launch_project(const float* out, const float* w, int B, int n_in, int d_r,
@@ -150,12 +196,11 @@ struct AttnSources {
 };
 hipError_t launch_decode(const Bank& bk, const void* q_rot, int B, int h_q, const int32_t* ids,
                          int k, const AttnSources& src, const void* k_loc, const void* v_loc,
-                         int L_loc, int loc_stride, int splits, float* part, float* out,
-                         hipStream_t s);
+                         int L_loc, int splits, float* part, float* out, hipStream_t s);
 hipError_t launch_prefill(const Bank& bk, const void* q_rot, int n_q, int h_q, const int32_t* ids,
                           int k, int block, const AttnSources& src, const void* k_loc,
-                          const void* v_loc, int L_loc, int loc_stride, int splits, float* part,
-                          float* out, hipStream_t s);
+                          const void* v_loc, int L_loc, int splits, float* part, float* out,
+                          hipStream_t s);
 
 // sizes of the attention partial buffers
 size_t decode_partial_floats(int B, int h_kv, int G, int splits);

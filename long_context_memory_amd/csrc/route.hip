@@ -13,188 +13,273 @@
 // query's cosines into per-document maxima over the tile's chunks: one
 // "piece" per (document, tile) it overlaps.  top-k later takes the max over a
 // document's pieces, so no atomics and no initialisation are needed.
+#include <algorithm>
+
 #include "msa_internal.h"
 
 namespace msa {
 namespace {
 
-constexpr int kRowPad = 68;      // floats per staged row (256 B of bf16 + 16 B pad)
 constexpr int kCosStride = 65;   // floats per query row of staged cosines
+constexpr int kQPerWave = 16;    // queries a wave scores per pass (64 per workgroup pass)
 
-template <typename T>
-__device__ __forceinline__ void load_row_f32(const T* __restrict__ rows, int nc, int lane,
-                                             float* lds_w, float (&kf)[kD]);
-
-template <>
-__device__ __forceinline__ void load_row_f32<uint16_t>(const uint16_t* __restrict__ rows, int nc,
-                                                       int lane, float* lds_w,
-                                                       float (&kf)[kD]) {
-  // 64 rows x 16 vectors of 16 B; flat vector f = i*64 + lane -> row f/16
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int f = i * 64 + lane;
-    const int row = f >> 4, col = f & 15;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (row < nc) v = *reinterpret_cast<const uint4*>(rows + (size_t)f * 8);
-    *reinterpret_cast<uint4*>(lds_w + row * kRowPad + col * 4) = v;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const uint4 v = *reinterpret_cast<const uint4*>(lds_w + lane * kRowPad + j * 4);
-    kf[j * 8 + 0] = bf16_lo(v.x); kf[j * 8 + 1] = bf16_hi(v.x);
-    kf[j * 8 + 2] = bf16_lo(v.y); kf[j * 8 + 3] = bf16_hi(v.y);
-    kf[j * 8 + 4] = bf16_lo(v.z); kf[j * 8 + 5] = bf16_hi(v.z);
-    kf[j * 8 + 6] = bf16_lo(v.w); kf[j * 8 + 7] = bf16_hi(v.w);
-  }
-}
-
-template <>
-__device__ __forceinline__ void load_row_f32<float>(const float* __restrict__ rows, int nc,
-                                                    int lane, float* lds_w, float (&kf)[kD]) {
-  // float32 keys: each lane reads its own 512 B row directly
-#pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (lane < nc) v = *reinterpret_cast<const float4*>(rows + (size_t)lane * kD + j * 4);
-    kf[j * 4 + 0] = v.x; kf[j * 4 + 1] = v.y; kf[j * 4 + 2] = v.z; kf[j * 4 + 3] = v.w;
-  }
-}
-
+// Routing scan.  Workgroup = one (tile of 64 chunks, router head); the tile's
+// key rows are staged once through LDS (coalesced 16-byte loads, all issued
+// before the first store) and every wave takes all 64 rows, one per lane.
+// The batch's router queries for this head are staged in LDS and read back as
+// broadcasts.  Wave w scores queries w, w+4, ... of a pass of 64, stages the
+// cosines in its own LDS rows, then lane j folds query j's cosines into
+// per-document maxima, one per run of equal documents ("piece") in the tile.
+//
+// bf16 keys: the dot products use v_dot2_f32_bf16 with the float32 query
+// split into two bfloat16 terms (q = hi + lo + r, |r| <= 2^-17 |q|), fp32
+// accumulation: one instruction per key element and query, and the packed
+// key row stays in 64 registers.  float32 keys: plain fp32 FMAs.
 template <typename T>
 __global__ __launch_bounds__(256) void route_scan_kernel(
     const T* __restrict__ kr, const float* __restrict__ inv_norm, const float* __restrict__ q,
-    int B, int h_r, int64_t C, int n_tiles, const int32_t* __restrict__ chunk_doc,
+    int B, int bg, int h_r, int64_t C, const int32_t* __restrict__ chunk_doc,
     const int32_t* __restrict__ tile_piece0, int P, float* __restrict__ piecemax) {
-  __shared__ float lds[4][64 * kRowPad];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int tile = blockIdx.x * 4 + wave;
-  const int h = blockIdx.y;
-  // a wave past the last tile keeps taking part in the workgroup barriers
-  const bool active = tile < n_tiles;
-  float* lds_w = lds[wave];
-  const int64_t c0 = (int64_t)(active ? tile : 0) * kRouteTile;
-  const int nc = active ? (int)min((int64_t)kRouteTile, C - c0) : 0;
+  // queries bg .. bg + min(64, B - bg) - 1 (one launch per group of 64)
+  constexpr bool kBF = sizeof(T) == 2;
+  constexpr int RowF = kD * (int)sizeof(T) / 4 + 4;  // 32-bit words per staged row (+16 B pad)
+  constexpr int QW = kBF ? kD : kD;                  // words per staged query (bf16: hi|lo pairs)
+  __shared__ __attribute__((aligned(16))) uint32_t s_rows[64 * RowF];
+  __shared__ __attribute__((aligned(16))) uint32_t s_q[64 * QW];
+  __shared__ float s_cos[4][kQPerWave * kCosStride];
+  __shared__ float s_iq[64];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int tile = blockIdx.x, h = blockIdx.y;
+  const int64_t c0 = (int64_t)tile * kRouteTile;
+  const int nc = (int)min((int64_t)kRouteTile, C - c0);
   const T* rows = kr + ((size_t)h * C + c0) * kD;
 
-  float kf[kD];
-  load_row_f32<T>(rows, nc, lane, lds_w, kf);
-  const float inv_k = lane < nc ? inv_norm[(size_t)h * C + c0 + lane] : 0.0f;
-  __syncthreads();  // every lane holds its row before LDS is reused for cosines
-
-  const int piece0 = active ? tile_piece0[tile] : 0;
-  const int doc_first = active ? chunk_doc[c0] : 0;
-  for (int bg = 0; bg < B; bg += 64) {
-    const int nb = min(64, B - bg);
-    // lane b's own query norm (applied after the max: x -> x * s is monotone)
-    float iq = 0.0f;
-    if (lane < nb) {
-      const float* qb = q + ((size_t)(bg + lane) * h_r + h) * kD;
-      float s = 0.f;
-      for (int i = 0; i < kD; i += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(qb + i);
-        s = fmaf(v.x, v.x, s); s = fmaf(v.y, v.y, s); s = fmaf(v.z, v.z, s); s = fmaf(v.w, v.w, s);
-      }
-      iq = s > 0.f ? 1.0f / sqrtf(s) : 0.0f;
-    }
-    // dot products of this lane's key row with queries bg .. bg+nb-1, four at
-    // a time (query values are wave-uniform)
-    for (int bb = 0; bb < nb; bb += 4) {
-      const float* q0 = q + ((size_t)(bg + bb) * h_r + h) * kD;
-      const float* q1 = q + ((size_t)(bg + min(bb + 1, nb - 1)) * h_r + h) * kD;
-      const float* q2 = q + ((size_t)(bg + min(bb + 2, nb - 1)) * h_r + h) * kD;
-      const float* q3 = q + ((size_t)(bg + min(bb + 3, nb - 1)) * h_r + h) * kD;
-      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  // stage the tile: 64 rows x VPR 16-byte vectors; rows past the end of the
+  // bank read the last row and are stored as zero
+  constexpr int VPR = kD * (int)sizeof(T) / 16;
+  constexpr int NLD = 64 * VPR / 256;
+  {
+    uint4 v[NLD];
 #pragma unroll
-      for (int i = 0; i < kD; ++i) {
-        a0 = fmaf(kf[i], q0[i], a0);
-        a1 = fmaf(kf[i], q1[i], a1);
-        a2 = fmaf(kf[i], q2[i], a2);
-        a3 = fmaf(kf[i], q3[i], a3);
+    for (int u = 0; u < NLD; ++u) {
+      const int f = u * 256 + threadIdx.x;
+      const int row = f / VPR, col = f % VPR;
+      v[u] = *reinterpret_cast<const uint4*>(rows + ((size_t)min(row, nc - 1) * VPR + col) *
+                                                        (16 / sizeof(T)));
+    }
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int f = u * 256 + threadIdx.x;
+      const int row = f / VPR, col = f % VPR;
+      *reinterpret_cast<uint4*>(s_rows + row * RowF + col * 4) =
+          row < nc ? v[u] : make_uint4(0, 0, 0, 0);
+    }
+  }
+  // document runs inside the tile (same for every wave)
+  const int my_doc = lane < nc ? chunk_doc[c0 + lane] : -1;
+  const int prev_doc = __shfl_up(my_doc, 1, 64);
+  const uint64_t starts = __ballot(lane < nc && (lane == 0 || my_doc != prev_doc));
+  const float inv_k = lane < nc ? inv_norm[(size_t)h * C + c0 + lane] : 0.0f;
+  const int piece0 = tile_piece0[tile];
+  __syncthreads();
+
+  // this lane's key row: bf16 stays packed (16 x uint4), f32 as 32 x uint4
+  uint4 kw[VPR];
+#pragma unroll
+  for (int c = 0; c < VPR; ++c) kw[c] = *reinterpret_cast<const uint4*>(s_rows + lane * RowF + c * 4);
+
+  float* cw = s_cos[wave];
+  {
+    const int npass = min(64, B - bg);
+    // stage this pass's queries (head h): 64 x 32 float4, loads first
+    {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int f = u * 256 + threadIdx.x;
+        const int qi = f / (kD / 4), col = f % (kD / 4);
+        v[u] = *reinterpret_cast<const float4*>(
+            q + ((size_t)(bg + min(qi, npass - 1)) * h_r + h) * kD + col * 4);
       }
-      lds_w[(bb + 0) * kCosStride + lane] = a0 * inv_k;
-      if (bb + 1 < nb) lds_w[(bb + 1) * kCosStride + lane] = a1 * inv_k;
-      if (bb + 2 < nb) lds_w[(bb + 2) * kCosStride + lane] = a2 * inv_k;
-      if (bb + 3 < nb) lds_w[(bb + 3) * kCosStride + lane] = a3 * inv_k;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int f = u * 256 + threadIdx.x;
+        const int qi = f / (kD / 4), col = f % (kD / 4);
+        if constexpr (kBF) {
+          // words [qi][0..63]: hi pairs; [qi][64..127]: lo pairs
+          const float x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+          uint32_t hi[2], lo[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const uint32_t h0 = f32_to_bf16(x[2 * e]), h1 = f32_to_bf16(x[2 * e + 1]);
+            hi[e] = h0 | (h1 << 16);
+            lo[e] = f32_to_bf16(x[2 * e] - __uint_as_float(h0 << 16)) |
+                    (f32_to_bf16(x[2 * e + 1] - __uint_as_float(h1 << 16)) << 16);
+          }
+          *reinterpret_cast<uint2*>(s_q + qi * QW + col * 2) = make_uint2(hi[0], hi[1]);
+          *reinterpret_cast<uint2*>(s_q + qi * QW + 64 + col * 2) = make_uint2(lo[0], lo[1]);
+        } else {
+          *reinterpret_cast<float4*>(s_q + qi * QW + col * 4) = v[u];
+        }
+        // partial squared norm of the float32 query
+        float ss = v[u].x * v[u].x + v[u].y * v[u].y + v[u].z * v[u].z + v[u].w * v[u].w;
+        // 32 consecutive threads hold one query row: reduce within the 32
+        ss += __shfl_xor(ss, 1, 64);
+        ss += __shfl_xor(ss, 2, 64);
+        ss += __shfl_xor(ss, 4, 64);
+        ss += __shfl_xor(ss, 8, 64);
+        ss += __shfl_xor(ss, 16, 64);
+        if (col == 0) s_iq[qi] = ss > 0.f ? 1.0f / sqrtf(ss) : 0.0f;
+      }
     }
     __syncthreads();
-    // lane b: per-document max over the tile's chunks (document runs are
-    // wave-uniform), then the query norm
-    int c = 0;
-    while (c < nc) {
-      const int d = chunk_doc[c0 + c];
-      float m = -INFINITY;
-      while (c < nc && chunk_doc[c0 + c] == d) {
-        if (lane < nb) m = fmaxf(m, lds_w[lane * kCosStride + c]);
-        ++c;
+    // this wave's queries: bg + wave + 4*j, j < nq
+    const int nq = max(0, min(kQPerWave, (npass - wave + 3) / 4));
+#pragma unroll 1
+    for (int j = 0; j < nq; ++j) {
+      const uint32_t* qj = s_q + (wave + 4 * j) * QW;
+      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+      if constexpr (kBF) {
+#pragma unroll
+        for (int c = 0; c < 16; c += 2) {
+          const uint4 h0 = *reinterpret_cast<const uint4*>(qj + c * 4);
+          const uint4 l0 = *reinterpret_cast<const uint4*>(qj + 64 + c * 4);
+          const uint4 h1 = *reinterpret_cast<const uint4*>(qj + c * 4 + 4);
+          const uint4 l1 = *reinterpret_cast<const uint4*>(qj + 64 + c * 4 + 4);
+          a0 = dot2_bf16(kw[c].x, h0.x, a0); a0 = dot2_bf16(kw[c].y, h0.y, a0);
+          a0 = dot2_bf16(kw[c].z, h0.z, a0); a0 = dot2_bf16(kw[c].w, h0.w, a0);
+          a1 = dot2_bf16(kw[c].x, l0.x, a1); a1 = dot2_bf16(kw[c].y, l0.y, a1);
+          a1 = dot2_bf16(kw[c].z, l0.z, a1); a1 = dot2_bf16(kw[c].w, l0.w, a1);
+          a2 = dot2_bf16(kw[c + 1].x, h1.x, a2); a2 = dot2_bf16(kw[c + 1].y, h1.y, a2);
+          a2 = dot2_bf16(kw[c + 1].z, h1.z, a2); a2 = dot2_bf16(kw[c + 1].w, h1.w, a2);
+          a3 = dot2_bf16(kw[c + 1].x, l1.x, a3); a3 = dot2_bf16(kw[c + 1].y, l1.y, a3);
+          a3 = dot2_bf16(kw[c + 1].z, l1.z, a3); a3 = dot2_bf16(kw[c + 1].w, l1.w, a3);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 32; c += 2) {
+          const float4 x0 = *reinterpret_cast<const float4*>(qj + c * 4);
+          const float4 x1 = *reinterpret_cast<const float4*>(qj + c * 4 + 4);
+          a0 = fmaf(__uint_as_float(kw[c].x), x0.x, a0); a1 = fmaf(__uint_as_float(kw[c].y), x0.y, a1);
+          a0 = fmaf(__uint_as_float(kw[c].z), x0.z, a0); a1 = fmaf(__uint_as_float(kw[c].w), x0.w, a1);
+          a2 = fmaf(__uint_as_float(kw[c + 1].x), x1.x, a2); a3 = fmaf(__uint_as_float(kw[c + 1].y), x1.y, a3);
+          a2 = fmaf(__uint_as_float(kw[c + 1].z), x1.z, a2); a3 = fmaf(__uint_as_float(kw[c + 1].w), x1.w, a3);
+        }
       }
-      if (lane < nb)
-        piecemax[((size_t)h * P + piece0 + (d - doc_first)) * B + bg + lane] = m * iq;
+      cw[j * kCosStride + lane] = ((a0 + a1) + (a2 + a3)) * inv_k;
     }
     __syncthreads();
+    // lane j: maxima over each run of equal documents, then the query norm
+    // (x -> x * s with s > 0 is monotone, so it commutes with the max)
+    const float my_iq = lane < nq ? s_iq[wave + 4 * lane] : 0.f;
+    uint64_t rest = starts;
+    int seg = 0;
+    while (rest) {
+      const int a0 = __builtin_ctzll(rest);
+      rest &= rest - 1;
+      const int e = rest ? __builtin_ctzll(rest) : nc;
+      if (lane < nq) {
+        float m = -INFINITY;
+        for (int c = a0; c < e; ++c) m = fmaxf(m, cw[lane * kCosStride + c]);
+        const int b = bg + wave + 4 * lane;
+        piecemax[((size_t)b * h_r + h) * P + piece0 + seg] = m * my_iq;
+      }
+      ++seg;
+    }
   }
 }
 
 // ---------------------------------------------------------------- top-k
-// One workgroup per query.  Each document's score is turned into a 64-bit
-// key (order-preserving score bits << 32 | ~id): the larger key is the higher
-// score, and among equal scores the lower id.  Key 0 marks an excluded or
-// taken document.  k rounds of a block-wide max pick the winners in rank
-// order; only the winner's owner rescans its strided share.
-__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+// Document n's score is the mean over router heads of the max over its
+// pieces; its key is (order-preserving score bits << 32 | ~n): a larger key
+// is a higher score, and among equal scores the lower id.  Key 0 marks an
+// excluded document (or no document).  Keys are unique, so a key's rank is
+// the number of larger keys.
+//
+// Selection runs in levels of the same kernel: every workgroup takes 256
+// keys (level 0: computed from the routing partials; later levels: the
+// previous level's lists), ranks each key by counting the larger keys of its
+// group in LDS, and writes the k best in rank order.  Each level shrinks the
+// candidates by 256/k; the level that sees at most 256 keys writes the ids.
+constexpr int kTopkGroup = 256;
 
-__global__ __launch_bounds__(256) void topk_kernel(
-    const float* __restrict__ piecemax, int B, int h_r, int N, int P,
-    const int32_t* __restrict__ doc_piece0, const uint32_t* exclude, int W,
-    uint32_t* exclude_out, int k, int32_t* __restrict__ ids,
-    float* __restrict__ scores, uint64_t* __restrict__ keys) {
-  const int b = blockIdx.x, tid = threadIdx.x;
-  uint64_t* kb = keys + (size_t)b * N;
-  uint64_t best = 0;
-  for (int n = tid; n < N; n += 256) {
-    uint64_t key = 0;
-    const bool excl = exclude && ((exclude[(size_t)b * W + (n >> 5)] >> (n & 31)) & 1u);
-    if (!excl) {
-      const int p0 = doc_piece0[n], p1 = doc_piece0[n + 1];
-      float s = 0.f;
-      for (int h = 0; h < h_r; ++h) {
-        float m = -INFINITY;
-        for (int p = p0; p < p1; ++p) m = fmaxf(m, piecemax[((size_t)h * P + p) * B + b]);
-        s += m;
-      }
-      s = s / (float)h_r;
-      key = ((uint64_t)float_order_key(s) << 32) | (uint64_t)(~(uint32_t)n);
-    }
-    kb[n] = key;
-    best = umax64(best, key);
+__device__ __forceinline__ uint64_t doc_key(const float* __restrict__ pm, int h_r, int P,
+                                            const int32_t* __restrict__ doc_piece0,
+                                            const uint32_t* excl_row, int n) {
+  if (excl_row && ((excl_row[n >> 5] >> (n & 31)) & 1u)) return 0;
+  const int p0 = doc_piece0[n], p1 = doc_piece0[n + 1];
+  float m[16];
+#pragma unroll
+  for (int h = 0; h < 16; ++h)  // independent loads (heads past h_r re-read head 0)
+    m[h] = pm[(size_t)(h < h_r ? h : 0) * P + p0];
+  for (int p = p0 + 1; p < p1; ++p)
+#pragma unroll
+    for (int h = 0; h < 16; ++h) m[h] = fmaxf(m[h], pm[(size_t)(h < h_r ? h : 0) * P + p]);
+  float s = 0.f;
+#pragma unroll
+  for (int h = 0; h < 16; ++h)
+    if (h < h_r) s += m[h];
+  return ((uint64_t)float_order_key(s / (float)h_r) << 32) | (uint64_t)(~(uint32_t)n);
+}
+
+struct TopkLevel {
+  // level 0 input (keys from routing partials)
+  const float* piecemax;
+  int h_r, N, P;
+  const int32_t* doc_piece0;
+  const uint32_t* exclude;
+  int W;
+  // later levels: candidate lists [B][M_in]
+  const uint64_t* in;
+  int M_in;
+  int k;
+  // output: next lists [B][groups * k], or ids/scores when final
+  uint64_t* out;
+  int final_level;
+  int32_t* ids;
+  float* scores;
+  uint32_t* exclude_out;
+};
+
+__global__ __launch_bounds__(kTopkGroup) void topk_level_kernel(TopkLevel a) {
+  __shared__ __attribute__((aligned(16))) uint64_t s_key[kTopkGroup];
+  const int g = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  const int groups = gridDim.x;
+  const int i = g * kTopkGroup + t;
+  uint64_t key = 0;
+  if (a.in == nullptr) {
+    if (i < a.N)
+      key = doc_key(a.piecemax + (size_t)b * a.h_r * a.P, a.h_r, a.P, a.doc_piece0,
+                    a.exclude ? a.exclude + (size_t)b * a.W : nullptr, i);
+  } else if (i < a.M_in) {
+    key = a.in[(size_t)b * a.M_in + i];
   }
-  __shared__ uint64_t red[4];
-  const int wave = tid >> 6, lane = tid & 63;
-  for (int r = 0; r < k; ++r) {
-    uint64_t m = best;
-    for (int o = 32; o >= 1; o >>= 1) m = umax64(m, (uint64_t)__shfl_xor((long long)m, o, 64));
-    if (lane == 0) red[wave] = m;
-    __syncthreads();
-    const uint64_t win = umax64(umax64(red[0], red[1]), umax64(red[2], red[3]));
-    __syncthreads();
-    if (win == 0) {
-      if (tid == 0) {
-        ids[(size_t)b * k + r] = -1;
-        scores[(size_t)b * k + r] = -INFINITY;
-      }
-      continue;
+  s_key[t] = key;
+  if (a.final_level) {
+    if (t < a.k) {
+      a.ids[(size_t)b * a.k + t] = -1;
+      a.scores[(size_t)b * a.k + t] = -INFINITY;
     }
-    const int n = (int)(~(uint32_t)(win & 0xffffffffu));
-    if (tid == 0) {
-      ids[(size_t)b * k + r] = n;
-      scores[(size_t)b * k + r] = float_from_order_key((uint32_t)(win >> 32));
-      if (exclude_out) atomicOr(&exclude_out[(size_t)b * W + (n >> 5)], 1u << (n & 31));
-    }
-    if ((n & 255) == tid) {
-      kb[n] = 0;
-      best = 0;
-      for (int j = tid; j < N; j += 256) best = umax64(best, kb[j]);
-    }
+  } else if (t < a.k) {
+    a.out[((size_t)b * groups + g) * a.k + t] = 0;
+  }
+  __syncthreads();
+  if (key == 0) return;
+  int rank = 0;
+#pragma unroll 8
+  for (int j = 0; j < kTopkGroup; j += 2) {
+    const ulonglong2 v = *reinterpret_cast<const ulonglong2*>(s_key + j);
+    rank += (v.x > key) + (v.y > key);
+  }
+  if (rank >= a.k) return;
+  if (a.final_level) {
+    const int n = (int)(~(uint32_t)(key & 0xffffffffu));
+    a.ids[(size_t)b * a.k + rank] = n;
+    a.scores[(size_t)b * a.k + rank] = float_from_order_key((uint32_t)(key >> 32));
+    if (a.exclude_out) atomicOr(&a.exclude_out[(size_t)b * a.W + (n >> 5)], 1u << (n & 31));
+  } else {
+    a.out[((size_t)b * groups + g) * a.k + rank] = key;
   }
 }
 
@@ -239,28 +324,58 @@ __global__ __launch_bounds__(256) void project_kernel(const float* __restrict__ 
 
 hipError_t launch_route_scan(const Bank& bk, const float* q_route, int B, float* piecemax,
                              hipStream_t s) {
-  const dim3 grid((unsigned)((bk.n_tiles + 3) / 4), (unsigned)bk.desc.h_r);
-  if (bk.desc.dtype == MSA_BF16)
-    hipLaunchKernelGGL(route_scan_kernel<uint16_t>, grid, dim3(256), 0, s,
-                       (const uint16_t*)bk.desc.kr, bk.desc.inv_norm, q_route, B, bk.desc.h_r,
-                       bk.n_chunks, bk.n_tiles, bk.d_chunk_doc, bk.d_tile_piece0, bk.n_pieces,
-                       piecemax);
-  else
-    hipLaunchKernelGGL(route_scan_kernel<float>, grid, dim3(256), 0, s,
-                       (const float*)bk.desc.kr, bk.desc.inv_norm, q_route, B, bk.desc.h_r,
-                       bk.n_chunks, bk.n_tiles, bk.d_chunk_doc, bk.d_tile_piece0, bk.n_pieces,
-                       piecemax);
+  const dim3 grid((unsigned)bk.n_tiles, (unsigned)bk.desc.h_r);
+  for (int bg = 0; bg < B; bg += 64) {
+    if (bk.desc.dtype == MSA_BF16)
+      hipLaunchKernelGGL(route_scan_kernel<uint16_t>, grid, dim3(256), 0, s,
+                         (const uint16_t*)bk.desc.kr, bk.desc.inv_norm, q_route, B, bg,
+                         bk.desc.h_r, bk.n_chunks, bk.d_chunk_doc, bk.d_tile_piece0,
+                         bk.n_pieces, piecemax);
+    else
+      hipLaunchKernelGGL(route_scan_kernel<float>, grid, dim3(256), 0, s,
+                         (const float*)bk.desc.kr, bk.desc.inv_norm, q_route, B, bg,
+                         bk.desc.h_r, bk.n_chunks, bk.d_chunk_doc, bk.d_tile_piece0,
+                         bk.n_pieces, piecemax);
+  }
   return hipGetLastError();
+}
+
+size_t topk_scratch_keys(int N, int k) {
+  // two ping-pong candidate buffers of (ceil(N/256) * k) keys per query
+  return 2 * (size_t)std::max(1, (N + kTopkGroup - 1) / kTopkGroup) * std::max(k, 1);
 }
 
 hipError_t launch_topk(const Bank& bk, const float* piecemax, int B, int k,
                        const uint32_t* exclude, uint32_t* exclude_out, int32_t* ids,
-                       float* scores, uint64_t* keys, hipStream_t s) {
+                       float* scores, uint64_t* cand, hipStream_t s) {
   const int N = bk.desc.n_docs;
-  const int W = (N + 31) / 32;
-  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)B), dim3(256), 0, s, piecemax, B,
-                     bk.desc.h_r, N, bk.n_pieces, bk.d_doc_piece0, exclude, W, exclude_out, k,
-                     ids, scores, keys);
+  TopkLevel a{};
+  a.piecemax = piecemax;
+  a.h_r = bk.desc.h_r;
+  a.N = N;
+  a.P = bk.n_pieces;
+  a.doc_piece0 = bk.d_doc_piece0;
+  a.exclude = exclude;
+  a.W = (N + 31) / 32;
+  a.k = k;
+  a.ids = ids;
+  a.scores = scores;
+  a.exclude_out = exclude_out;
+  const size_t half = topk_scratch_keys(N, k) / 2;
+  uint64_t* bufs[2] = {cand, cand + (size_t)B * half};
+  int M = N, lvl = 0;
+  for (;;) {
+    const int groups = (M + kTopkGroup - 1) / kTopkGroup;
+    a.final_level = groups == 1;
+    a.out = bufs[lvl & 1];
+    hipLaunchKernelGGL(topk_level_kernel, dim3((unsigned)groups, (unsigned)B), dim3(kTopkGroup), 0,
+                       s, a);
+    if (a.final_level) break;
+    a.in = a.out;
+    a.M_in = groups * k;
+    M = a.M_in;
+    ++lvl;
+  }
   return hipGetLastError();
 }
 

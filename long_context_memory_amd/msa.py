@@ -47,7 +47,7 @@ class BankInfo(C.Structure):
 class AttendArgs(C.Structure):
     _fields_ = [("mode", i32), ("n_q", i32), ("h_q", i32), ("q", vp), ("q_pos", i32),
                 ("ids", vp), ("k", i32), ("block", i32), ("k_loc", vp), ("v_loc", vp),
-                ("L_loc", i32), ("loc_stride", i32), ("out", vp), ("ws", vp),
+                ("L_loc", i32), ("out", vp), ("ws", vp),
                 ("ws_bytes", C.c_size_t), ("splits", i32), ("src_k", vp), ("src_v", vp),
                 ("src_off", vp), ("src_len", vp), ("n_src", i32)]
 
@@ -55,8 +55,7 @@ class AttendArgs(C.Structure):
 class StepArgs(C.Structure):
     _fields_ = [("mode", i32), ("n_q", i32), ("h_q", i32), ("k", i32), ("q", vp),
                 ("q_pos", i32), ("q_route", vp), ("route_tokens", vp), ("block", i32),
-                ("k_loc", vp), ("v_loc", vp), ("L_loc", i32), ("loc_stride", i32),
-                ("hops", i32), ("w_proj", vp), ("exclude_selected", i32), ("exclude", vp),
+                ("k_loc", vp), ("v_loc", vp), ("L_loc", i32), ("hops", i32), ("w_proj", vp), ("exclude_selected", i32), ("exclude", vp),
                 ("ids", vp), ("scores", vp), ("out", vp), ("ws", vp), ("ws_bytes", C.c_size_t),
                 ("staging", vp), ("staging_bytes", C.c_size_t), ("splits", i32)]
 
@@ -79,7 +78,7 @@ def _load():
     lib.msa_bank_destroy.argtypes = [vp]
     lib.msa_bank_get_info.argtypes = [vp, C.POINTER(BankInfo)]
     lib.msa_build_bank.argtypes = [vp, i32, i32, vp, vp, vp, vp]
-    lib.msa_prepare_local.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, i32, vp]
+    lib.msa_prepare_local.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, vp]
     lib.msa_workspace_bytes.restype = C.c_size_t
     lib.msa_workspace_bytes.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32]
     lib.msa_staging_bytes.restype = C.c_size_t
@@ -181,17 +180,17 @@ class Bank:
         _check(lib.msa_build_bank(self.handle, doc0, doc1, _ptr(route_vec), _ptr(k_raw),
                                   _ptr(v_raw), _stream(stream)), "msa_build_bank")
 
-    def prepare_local(self, k_raw, v_raw, pos0: int, loc_stride: Optional[int] = None,
-                      stream=None):
-        """k_raw, v_raw: [n_seq, L, h_kv, 128] -> (k_loc, v_loc, L, loc_stride)."""
+    def prepare_local(self, k_raw, v_raw, pos0: int, stream=None):
+        """k_raw, v_raw: [n_seq, L, h_kv, 128] -> (k_loc [n_seq, h_kv, L, 128],
+        v_loc [n_seq, h_kv, ceil(L/64), 128, 64], L)."""
         n_seq, L = int(k_raw.shape[0]), int(k_raw.shape[1])
-        ls = int(loc_stride) if loc_stride is not None else max(8, (L + 7) // 8 * 8)
+        tp = (L + 63) // 64
         k_loc = torch.empty((n_seq, self.h_kv, L, 128), dtype=self.dtype, device=self.device)
-        v_loc = torch.empty((n_seq, self.h_kv, 128, ls), dtype=self.dtype, device=self.device)
+        v_loc = torch.empty((n_seq, self.h_kv, tp, 128, 64), dtype=self.dtype, device=self.device)
         _check(lib.msa_prepare_local(self.handle, _ptr(k_raw), _ptr(v_raw), n_seq, L, int(pos0),
-                                     _ptr(k_loc), _ptr(v_loc), ls, _stream(stream)),
+                                     _ptr(k_loc), _ptr(v_loc), _stream(stream)),
                "msa_prepare_local")
-        return k_loc, v_loc, L, ls
+        return k_loc, v_loc, L
 
     # -- workspace ----------------------------------------------------------
     def workspace_bytes(self, mode, n_q, h_q, k, block=64, hops=1, splits=0) -> int:
@@ -216,8 +215,7 @@ class Bank:
                              _ptr(scores), _ptr(ws), ws.numel(), _stream(stream)), "msa_route")
         return ids, scores
 
-    def attend(self, q, q_pos: int, ids, k_loc, v_loc, L_loc: int, loc_stride: int,
-               mode=MSA_DECODE, block: int = 64, splits: int = 0, ws=None, src=None,
+    def attend(self, q, q_pos: int, ids, k_loc, v_loc, L_loc: int, mode=MSA_DECODE, block: int = 64, splits: int = 0, ws=None, src=None,
                out=None, stream=None):
         n_q, h_q = int(q.shape[0]), int(q.shape[1])
         k = 0 if ids is None else int(ids.shape[1])
@@ -227,14 +225,13 @@ class Bank:
             out = torch.empty((n_q, h_q, 128), dtype=torch.float32, device=self.device)
         sk, sv, so, sl = (None, None, None, None) if src is None else src
         a = AttendArgs(mode, n_q, h_q, _ptr(q), int(q_pos), _ptr(ids), k, block, _ptr(k_loc),
-                       _ptr(v_loc), int(L_loc), int(loc_stride), _ptr(out), _ptr(ws),
+                       _ptr(v_loc), int(L_loc), _ptr(out), _ptr(ws),
                        ws.numel(), splits, _ptr(sk), _ptr(sv), _ptr(so), _ptr(sl),
                        0 if sl is None else int(sl.numel()))
         _check(lib.msa_attend(self.handle, C.byref(a), _stream(stream)), "msa_attend")
         return out
 
-    def step(self, q, q_pos: int, k: int, k_loc, v_loc, L_loc: int, loc_stride: int,
-             q_route=None, route_tokens=None, mode=MSA_DECODE, block: int = 64, hops: int = 1,
+    def step(self, q, q_pos: int, k: int, k_loc, v_loc, L_loc: int, q_route=None, route_tokens=None, mode=MSA_DECODE, block: int = 64, hops: int = 1,
              w_proj=None, exclude_selected: bool = False, exclude=None, splits: int = 0,
              ws=None, staging=None, outputs=None, stream=None, copy_stream=None):
         """Returns (ids [hops, n_groups, k], scores, out [hops, n_q, h_q, 128], stats)."""
@@ -251,7 +248,7 @@ class Bank:
         else:
             ids, scores, out = outputs
         a = StepArgs(mode, n_q, h_q, k, _ptr(q), int(q_pos), _ptr(q_route), _ptr(route_tokens),
-                     block, _ptr(k_loc), _ptr(v_loc), int(L_loc), int(loc_stride), hops,
+                     block, _ptr(k_loc), _ptr(v_loc), int(L_loc), hops,
                      _ptr(w_proj), int(bool(exclude_selected)), _ptr(exclude), _ptr(ids),
                      _ptr(scores), _ptr(out), _ptr(ws), ws.numel(), _ptr(staging),
                      0 if staging is None else staging.numel(), splits)

@@ -123,10 +123,17 @@ def natural_from_store_k(bank, n, kv_off=None):
 
 
 def natural_from_store_v(bank, n, kv_off=None):
+    """Read document n's V from the tile-blocked store back into [L, h_kv, 128]."""
     L = bank.doc_len[n]
     o = (int(kv_off[n]) if kv_off is not None else sum(bank.doc_len[:n])) * bank.h_kv * 128
-    blk = bank.v_store[o:o + L * bank.h_kv * 128].view(bank.h_kv, 128, L)
-    return blk.permute(2, 0, 1)
+    blk = bank.v_store[o:o + L * bank.h_kv * 128].view(bank.h_kv, L // 64, 128, 64)
+    return blk.permute(1, 3, 0, 2).reshape(L, bank.h_kv, 128)
+
+
+def local_v_natural(v_loc_seq):
+    """One sequence of prepared local V [h_kv, Tp, 128, 64] -> [Tp*64, h_kv, 128]."""
+    h, tp = v_loc_seq.shape[0], v_loc_seq.shape[1]
+    return v_loc_seq.permute(1, 3, 0, 2).reshape(tp * 64, h, 128)
 
 
 def ulp_diff_bf16(a, b):

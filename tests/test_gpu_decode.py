@@ -38,10 +38,10 @@ def decode_case(msa, name):
         q_route = S.route_queries(w, DEV)
     q = S.queries(w, DEV)
     lk, lv = S.local_raw(w, DEV)
-    k_loc, v_loc, L, ls = bank.prepare_local(lk, lv, w.P0)
+    k_loc, v_loc, L = bank.prepare_local(lk, lv, w.P0)
     torch.cuda.synchronize()
     c = dict(w=w, r=r, k_raw=k_raw, v_raw=v_raw, bank=bank, kr_o=kr_o, inv_o=inv_o,
-             q_route=q_route, q=q, lk=lk, lv=lv, k_loc=k_loc, v_loc=v_loc, L=L, ls=ls,
+             q_route=q_route, q=q, lk=lk, lv=lv, k_loc=k_loc, v_loc=v_loc, L=L,
              target_doc=doc)
     _CACHE[name] = c
     return c
@@ -81,9 +81,9 @@ def test_prepare_local_matches_oracle(msa, name):
                                                 w.rope_base), w.dtype)
         kg = M.np64(c["k_loc"][b].permute(1, 0, 2))
         np.testing.assert_allclose(kg, lk_o, rtol=0, atol=(8e-3 if w.dtype == "bf16" else 1e-6))
-        vg = c["v_loc"][b]
-        np.testing.assert_array_equal(M.np64(vg[:, :, :L].permute(2, 0, 1)), M.np64(c["lv"][b]))
-        assert float(vg[:, :, L:].abs().max() if c["ls"] > L else 0.0) == 0.0
+        vg = M.local_v_natural(c["v_loc"][b])  # [Tp*64, h_kv, 128]
+        np.testing.assert_array_equal(M.np64(vg[:L]), M.np64(c["lv"][b]))
+        assert float(vg[L:].abs().max()) == 0.0 if vg.shape[0] > L else True
 
 
 def oracle_scores(c, exclude=None):
@@ -158,7 +158,7 @@ def test_decode_step_matches_oracle(msa, name):
     c = decode_case(msa, name)
     w = c["w"]
     ids, scores, out, _ = c["bank"].step(c["q"], w.q_pos, w.k, c["k_loc"], c["v_loc"], c["L"],
-                                         c["ls"], q_route=c["q_route"])
+                                         q_route=c["q_route"])
     torch.cuda.synchronize()
     so = oracle_scores(c)
     ids_np = ids[0].cpu().numpy()
@@ -173,7 +173,7 @@ def test_decode_power_wrong_document_is_caught(msa):
     c = decode_case(msa, "c2_small")
     w = c["w"]
     ids, scores, out, _ = c["bank"].step(c["q"], w.q_pos, w.k, c["k_loc"], c["v_loc"], c["L"],
-                                         c["ls"], q_route=c["q_route"])
+                                         q_route=c["q_route"])
     ids_np = ids[0].cpu().numpy().copy()
     so = oracle_scores(c)
     bad = ids_np.copy()
@@ -188,10 +188,9 @@ def test_decode_splits_and_determinism(msa, name):
     c = decode_case(msa, name)
     w = c["w"]
     ids, _ = c["bank"].route(c["q_route"], w.k)
-    outs = [c["bank"].attend(c["q"], w.q_pos, ids, c["k_loc"], c["v_loc"], c["L"], c["ls"],
-                             splits=s) for s in (4, 8, 64)]
-    again = c["bank"].attend(c["q"], w.q_pos, ids, c["k_loc"], c["v_loc"], c["L"], c["ls"],
-                             splits=8)
+    outs = [c["bank"].attend(c["q"], w.q_pos, ids, c["k_loc"], c["v_loc"], c["L"], splits=s)
+            for s in (4, 8, 64)]
+    again = c["bank"].attend(c["q"], w.q_pos, ids, c["k_loc"], c["v_loc"], c["L"], splits=8)
     torch.cuda.synchronize()
     assert torch.equal(outs[1], again)  # deterministic
     # different splits see different running maxima; fp32 agrees to rounding,
@@ -207,9 +206,9 @@ def test_decode_ragged_and_empty_local(msa, L_loc):
     c = decode_case(msa, "c2_small")
     w, bank = c["w"], c["bank"]
     lk, lv = c["lk"][:, :L_loc].contiguous(), c["lv"][:, :L_loc].contiguous()
-    k_loc, v_loc, L, ls = bank.prepare_local(lk, lv, w.P0)
+    k_loc, v_loc, L = bank.prepare_local(lk, lv, w.P0)
     ids, _ = bank.route(c["q_route"], w.k)
-    out = bank.attend(c["q"], w.P0 + max(L_loc, 1) - 1, ids, k_loc, v_loc, L, ls)
+    out = bank.attend(c["q"], w.P0 + max(L_loc, 1) - 1, ids, k_loc, v_loc, L)
     torch.cuda.synchronize()
     so = oracle_scores(c)
     ids_np = ids.cpu().numpy()
@@ -229,7 +228,7 @@ def test_decode_local_only_and_docs_only(msa):
     w, bank = c["w"], c["bank"]
     q = M.np64(c["q"])
     # k = 0: attention over the local context alone
-    out = bank.attend(c["q"], w.q_pos, None, c["k_loc"], c["v_loc"], c["L"], c["ls"])
+    out = bank.attend(c["q"], w.q_pos, None, c["k_loc"], c["v_loc"], c["L"])
     torch.cuda.synchronize()
     for b in range(w.B):
         ref = M.oracle_attend_decode(w, q[b], w.q_pos, [], {}, M.np64(c["lk"][b]),
@@ -239,8 +238,8 @@ def test_decode_local_only_and_docs_only(msa):
     ids = torch.full((w.B, 3), -1, dtype=torch.int32, device=DEV)
     ids[:, 1] = torch.arange(w.B, dtype=torch.int32, device=DEV) + 5
     e = torch.empty((w.B, 0, w.h_kv, 128), dtype=c["lk"].dtype, device=DEV)
-    k0, v0, L0, ls0 = bank.prepare_local(e, e, w.P0)
-    out = bank.attend(c["q"], w.q_pos, ids, k0, v0, L0, ls0)
+    k0, v0, L0 = bank.prepare_local(e, e, w.P0)
+    out = bank.attend(c["q"], w.q_pos, ids, k0, v0, L0)
     torch.cuda.synchronize()
     for b in range(w.B):
         n = b + 5
