@@ -1,14 +1,20 @@
 """Throughput of the MSA hot path on one MI355X.
 
-Default workload: routed decode at a 1M-token bank (2048 documents x 512
-tokens, bf16, 8 router heads, 32 query / 8 KV heads, d = 128), batch 16,
-top-16, 4096-token local context.  One step = route -> top-k -> gather ->
-split-K attention for one batch of 16 queries, through msa_step.  Prints one
-JSON line.
+Default workload (the headline metric): routed decode at a 1M-token bank --
+2048 documents x 512 tokens, bf16, 8 router heads, 32 query / 8 KV heads,
+d = 128, batch 16, top-16, 4096-token local context.  One step = route ->
+top-k -> gather -> split-K attention (msa_step) for one batch of 16 queries.
+Independent batches rotate over --batches query sets (so the 256 MB MALL
+cannot hold a step's data) and alternate over --streams HIP streams.
+
+Prints one JSON line: queries/s, the dominant kernel's roofline (decode
+attention, timed with HIP events around each launch on its stream), and the
+fp64 oracle timed on this host on a bounded sample of the same workload.
 """
 import argparse
 import json
 import os
+import platform
 import sys
 import time
 
@@ -19,17 +25,83 @@ METRIC = "routed decode queries/sec at 1M-token bank; % peak HBM GB/s; prefill M
 HBM_PEAK_GBS = 8000.0
 
 
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w, r_dev, k_raw_dev, v_raw_dev, batch_inputs, budget_s=12.0):
+    """The fp64 oracle on one 16-query decode step of the same bank.  Bank
+    build (pooling, document RoPE) and the local context's RoPE are set-up,
+    as on the GPU; the timed part is routing over every chunk, top-k, the
+    gather and the attention."""
+    import numpy as np
+    import torch
+    from oracle import msa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+
+    f64 = lambda t: t.detach().to("cpu", torch.float32).double().numpy()  # noqa: E731
+    off = np.concatenate([[0], np.cumsum(w.doc_len)])
+    keys = []
+    for n0 in range(0, w.n_docs, 256):
+        n1 = min(w.n_docs, n0 + 256)
+        keys.append(O.chunk_mean_pool(f64(r_dev[off[n0]:off[n1]]), w.doc_len[n0:n1]))
+    kr = O.round_to_storage(np.concatenate(keys), w.dtype)
+    inv = O.inverse_norms(kr)
+    q, q_route, lk, lv = batch_inputs
+    qn, qrn = f64(q), f64(q_route)
+    scores = O.cosine_doc_scores(qrn, kr, inv, w.doc_len)
+    ids, _ = O.select_topk(scores, w.k)
+    doc_kv = {}
+    for n in set(ids.ravel().tolist()):
+        a, b = off[n], off[n + 1]
+        doc_kv[n] = (O.bank_keys_rotated(f64(k_raw_dev[a:b]), [b - a], w.rope_base, w.dtype),
+                     f64(v_raw_dev[a:b]))
+    L = w.L_loc
+    lkr = [O.round_to_storage(O.rope_rotate(f64(lk[b]), (w.P0 + np.arange(L))[:, None],
+                                            w.rope_base), w.dtype) for b in range(w.B)]
+    lvn = [f64(lv[b]) for b in range(w.B)]
+
+    def one_step():
+        s = O.cosine_doc_scores(qrn, kr, inv, w.doc_len)
+        sel, _ = O.select_topk(s, w.k)
+        for b in range(w.B):
+            K = np.concatenate([doc_kv[n][0] for n in sel[b]] + [lkr[b]])
+            V = np.concatenate([doc_kv[n][1] for n in sel[b]] + [lvn[b]])
+            qr = O.rope_rotate(qn[b][None], np.full((1, w.h_q), w.q_pos), w.rope_base)
+            O.gqa_attention(qr, K, V)
+
+    n, t0 = 0, time.perf_counter()
+    while True:
+        one_step()
+        n += 1
+        dt = time.perf_counter() - t0
+        if dt >= budget_s or n >= 50:
+            break
+    return {"value": w.B * n / dt, "unit": "queries/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n} full 16-query decode step(s) of the 1M-token bank: cosine routing "
+                      "over all 4096 chunks x 8 heads, top-16, gather, GQA attention over "
+                      "12,288 tokens x 32 heads per query (bank build and local RoPE are "
+                      "set-up, as on the GPU)",
+            "seconds": dt, "processor": platform.processor() or platform.machine()}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--batches", type=int, default=4, help="rotating query batches")
+    ap.add_argument("--streams", type=int, default=2, help="HIP streams batches alternate over")
+    ap.add_argument("--splits", type=int, default=0, help="attention splits (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by document range; see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported here "
+              "(the path shards by document range across GPUs; see DESIGN.md)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -37,21 +109,26 @@ def main():
 
     dev = "cuda"
     w = S.workload("c2")
-    print(f"[bench] building {w.name}: {w.n_docs} docs, {w.T} tokens", file=sys.stderr, flush=True)
+    log(f"building {w.name}: {w.n_docs} docs, {w.T} tokens")
     r = S.route_vectors(w, dev)
     k_raw, v_raw = S.kv_raw(w, dev)
     bank = msa.Bank(w.doc_len, w.h_r, w.h_kv, w.dtype, dev, rope_base=w.rope_base)
+    torch.cuda.synchronize()
+    tb = time.perf_counter()
     bank.build(0, w.n_docs, r, k_raw, v_raw)
-    del r, k_raw, v_raw
-    batches = []
+    torch.cuda.synchronize()
+    build_s = time.perf_counter() - tb
+    batches, raw0 = [], None
     for i in range(args.batches):
         q = S.queries(w, dev, batch=i)
         q_route = S.route_queries(w, dev, batch=i)
         lk, lv = S.local_raw(w, dev, batch=i)
         k_loc, v_loc, L = bank.prepare_local(lk, lv, w.P0)
-        del lk, lv
+        if i == 0:
+            raw0 = (q, q_route, lk, lv)
         batches.append((q, q_route, k_loc, v_loc, L))
-    ws = bank.workspace(msa.MSA_DECODE, w.B, w.h_q, w.k)
+    streams = [torch.cuda.Stream() for _ in range(max(1, args.streams))]
+    ws = [bank.workspace(msa.MSA_DECODE, w.B, w.h_q, w.k) for _ in streams]
     outs = [(torch.empty((1, w.B, w.k), dtype=torch.int32, device=dev),
              torch.empty((1, w.B, w.k), dtype=torch.float32, device=dev),
              torch.empty((1, w.B, w.h_q, 128), dtype=torch.float32, device=dev))
@@ -59,34 +136,55 @@ def main():
     torch.cuda.synchronize()
 
     def step(i):
+        si = i % len(streams)
         q, q_route, k_loc, v_loc, L = batches[i % args.batches]
-        bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=q_route, ws=ws,
-                  outputs=outs[i % args.batches])
+        bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=q_route, ws=ws[si],
+                  outputs=outs[i % args.batches], stream=streams[si], splits=args.splits)
 
-    print("[bench] warmup", file=sys.stderr, flush=True)
+    log("warmup")
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    print("[bench] timed", file=sys.stderr, flush=True)
+    log("timed")
+    msa.timer_enable(True)
+    msa.timer_read(msa.MSA_TIMER_ATTENTION)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    att_ms, att_n = msa.timer_read(msa.MSA_TIMER_ATTENTION)
+    msa.timer_read(msa.MSA_TIMER_ROUTE)
+    msa.timer_enable(False)
+    log("done")
     ms = dt * 1e3 / args.steps
     qps = w.B * args.steps / dt
+
+    # algorithmic bytes: every K and V element of each query's union once
     kv_bytes = w.B * (w.k * 512 + w.L_loc) * w.h_kv * 128 * 2 * 2
-    step_bytes = kv_bytes + w.C * w.h_r * 128 * 2 + w.C * w.h_r * 4
+    att_avg_us = att_ms * 1e3 / max(att_n, 1)
+    achieved = kv_bytes / (att_avg_us * 1e-6) / 1e9
     res = {
         "metric": METRIC, "value": qps, "unit": "queries/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "1M-token bank decode: 2048 docs x 512 tokens, B=16, top-16, "
-                   "h_r=8, h_q=32, h_kv=8, d=128, local 4096, bf16", "batch": w.B,
-                   "bank_tokens": w.T},
-        "step_hbm_frac": step_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "config": {"workload": "1M-token bank decode: 2048 docs x 512 tokens (4096 chunks), "
+                   "B=16, top-16, h_r=8 router heads, h_q=32, h_kv=8, d=128, local 4096, bf16",
+                   "batch": w.B, "bank_tokens": w.T, "streams": len(streams),
+                   "rotating_batches": args.batches},
+        "roofline": {"kernel": "decode attention (split-K)", "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_launch": kv_bytes, "avg_launch_us": att_avg_us,
+                     "launches": att_n},
+        "tokens_attended_per_s": qps * (w.k * 512 + w.L_loc),
+        "bank_build_s": build_s,
     }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        res["cpu_baseline"] = cpu_baseline(w, r, k_raw, v_raw, raw0)
     print(json.dumps(res))
 
 

@@ -254,6 +254,17 @@ int msa_attend(const msa_bank* bank, const msa_attend_args* args, void* stream);
 int msa_step(const msa_bank* bank, const msa_step_args* args, void* stream,
              void* copy_stream, msa_step_stats* stats);
 
+/* Kernel timing for measurement.  While enabled on the calling thread, the
+ * library brackets every launch of the kernel class `which` with a pair of
+ * HIP events on the stream it launches on.  msa_timer_read synchronises
+ * those events, returns the accumulated milliseconds and the number of
+ * launches since the last read, and clears them.
+ *   which: MSA_TIMER_ATTENTION (decode or prefill attention kernel),
+ *          MSA_TIMER_ROUTE (routing scan). */
+enum { MSA_TIMER_ATTENTION = 0, MSA_TIMER_ROUTE = 1 };
+int msa_timer_enable(int on);
+int msa_timer_read(int which, double* total_ms, int64_t* launches);
+
 #ifdef __cplusplus
 }
 #endif

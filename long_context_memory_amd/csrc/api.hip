@@ -15,6 +15,39 @@ namespace msa {
 static thread_local std::string g_last_error;
 void set_error(const std::string& msg) { g_last_error = msg; }
 
+// ---- kernel timing (measurement only; off by default)
+struct TimerState {
+  bool on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> done[2];
+  std::vector<hipEvent_t> pool;
+  hipEvent_t open[2] = {nullptr, nullptr};
+};
+static thread_local TimerState g_timer;
+
+static hipEvent_t timer_event() {
+  if (!g_timer.pool.empty()) {
+    hipEvent_t e = g_timer.pool.back();
+    g_timer.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+void timer_mark(int which, bool begin, hipStream_t s) {
+  if (!g_timer.on || which < 0 || which > 1) return;
+  hipEvent_t e = timer_event();
+  if (!e) return;
+  (void)hipEventRecord(e, s);
+  if (begin) {
+    g_timer.open[which] = e;
+  } else if (g_timer.open[which]) {
+    g_timer.done[which].emplace_back(g_timer.open[which], e);
+    g_timer.open[which] = nullptr;
+  }
+}
+
 namespace {
 
 int fail(int code, const std::string& msg) {
@@ -114,6 +147,31 @@ const char* msa_status_string(int status) {
 const char* msa_last_error(void) { return g_last_error.c_str(); }
 
 int msa_version(void) { return 10000; }
+
+int msa_timer_enable(int on) {
+  g_timer.on = on != 0;
+  return MSA_OK;
+}
+
+int msa_timer_read(int which, double* total_ms, int64_t* launches) {
+  if (which < 0 || which > 1 || !total_ms || !launches) return fail(MSA_EINVAL, "timer_read");
+  double tot = 0.0;
+  int64_t n = 0;
+  for (auto& pr : g_timer.done[which]) {
+    float ms = 0.f;
+    if (hipEventSynchronize(pr.second) != hipSuccess ||
+        hipEventElapsedTime(&ms, pr.first, pr.second) != hipSuccess)
+      return fail(MSA_EHIP, "timer events");
+    tot += ms;
+    ++n;
+    g_timer.pool.push_back(pr.first);
+    g_timer.pool.push_back(pr.second);
+  }
+  g_timer.done[which].clear();
+  *total_ms = tot;
+  *launches = n;
+  return MSA_OK;
+}
 
 int msa_bank_create(const msa_bank_desc* d, msa_bank** out) {
   if (!d || !out) return fail(MSA_EINVAL, "NULL descriptor or output");

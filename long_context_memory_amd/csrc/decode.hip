@@ -379,7 +379,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 template <typename T, int G>
 hipError_t run_decode(const DecodeP& p, int B, float* out, hipStream_t s) {
   const dim3 grid((unsigned)(p.S / 4), (unsigned)p.h_kv, (unsigned)B);
+  timer_mark(0, true, s);
   hipLaunchKernelGGL((decode_kernel<T, G>), grid, dim3(256), 0, s, p);
+  timer_mark(0, false, s);
   hipLaunchKernelGGL((combine_kernel<G>), dim3((unsigned)p.h_kv, (unsigned)B), dim3(256), 0, s,
                      p.part, p.S, p.h_kv, p.h_q, out);
   return hipGetLastError();
@@ -392,12 +394,14 @@ size_t decode_partial_floats(int B, int h_kv, int G, int splits) {
 }
 
 int decode_auto_splits(const Bank& bk, int B, int k, int L_loc) {
-  // average union length -> tiles per (query, head); aim for >= ~4096 waves
-  // in flight and >= 2 tiles per wave
+  // About one long-running wave per SIMD (1024 waves on 256 CUs) streams
+  // best: each wave walks a long contiguous run of tiles.  Splits come in
+  // multiples of 4 (one workgroup = 4 waves) and never exceed the tiles.
   const double avg_doc = (double)bk.n_tokens / bk.desc.n_docs;
   const double tiles = k * avg_doc / kAttnTile + (L_loc + kAttnTile - 1) / kAttnTile;
-  const int want = (int)((4096 + (int64_t)B * bk.desc.h_kv - 1) / ((int64_t)B * bk.desc.h_kv));
-  int s = (int)std::min<double>(want, std::max(1.0, tiles / 2));
+  const int64_t pairs = std::max<int64_t>(1, (int64_t)B * bk.desc.h_kv);
+  int s = (int)((1024 + pairs - 1) / pairs);
+  s = (int)std::min<double>(s, std::max(4.0, tiles));
   s = std::max(4, ((s + 3) / 4) * 4);
   return std::min(s, 256);
 }

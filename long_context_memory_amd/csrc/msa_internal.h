@@ -45,6 +45,9 @@ struct Bank {
 // thread-local last error message
 void set_error(const std::string& msg);
 
+// optional event timing of one kernel class (see msa_timer_enable)
+void timer_mark(int which, bool begin, hipStream_t s);
+
 inline size_t dtype_size(msa_dtype t) { return t == MSA_BF16 ? 2 : 4; }
 
 // --------------------------------------------------------------------------

@@ -14,7 +14,7 @@ from typing import Optional
 import torch  # noqa: F401  (loads the HIP runtime the library binds to)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmsa.so")
+LIB_PATH = os.environ.get("MSA_LIBRARY") or os.path.join(_HERE, "libmsa.so")
 
 MSA_OK, MSA_EINVAL, MSA_ENOMEM, MSA_EHIP, MSA_EUNSUPPORTED = 0, 1, 2, 3, 4
 MSA_F32, MSA_BF16 = 0, 1
@@ -25,7 +25,9 @@ EXPORTS = [
     "msa_status_string", "msa_last_error", "msa_version", "msa_bank_create",
     "msa_bank_destroy", "msa_bank_get_info", "msa_build_bank", "msa_prepare_local",
     "msa_workspace_bytes", "msa_staging_bytes", "msa_route", "msa_attend", "msa_step",
+    "msa_timer_enable", "msa_timer_read",
 ]
+MSA_TIMER_ATTENTION, MSA_TIMER_ROUTE = 0, 1
 
 vp = C.c_void_p
 i32 = C.c_int32
@@ -86,6 +88,10 @@ def _load():
     lib.msa_route.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp, C.c_size_t, vp]
     lib.msa_attend.argtypes = [vp, C.POINTER(AttendArgs), vp]
     lib.msa_step.argtypes = [vp, C.POINTER(StepArgs), vp, vp, C.POINTER(StepStats)]
+    lib.msa_timer_enable.argtypes = [C.c_int]
+    lib.msa_timer_read.argtypes = [C.c_int, C.POINTER(C.c_double), C.POINTER(i64)]
+    for f in (lib.msa_timer_enable, lib.msa_timer_read):
+        f.restype = C.c_int
     for f in (lib.msa_bank_create, lib.msa_bank_destroy, lib.msa_bank_get_info,
               lib.msa_build_bank, lib.msa_prepare_local, lib.msa_route, lib.msa_attend,
               lib.msa_step):
@@ -94,6 +100,17 @@ def _load():
 
 
 lib = _load()
+
+
+def timer_enable(on: bool = True):
+    _check(lib.msa_timer_enable(int(bool(on))), "msa_timer_enable")
+
+
+def timer_read(which: int):
+    """(total milliseconds, launches) of kernel class `which` since the last read."""
+    ms, n = C.c_double(), i64()
+    _check(lib.msa_timer_read(which, C.byref(ms), C.byref(n)), "msa_timer_read")
+    return ms.value, n.value
 
 
 class MSAError(RuntimeError):
