@@ -23,6 +23,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "routed decode queries/sec at 1M-token bank; % peak HBM GB/s; prefill MFMA %"
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0  # dense bf16
 
 
 def log(msg):
@@ -89,6 +90,73 @@ def cpu_baseline(w, r_dev, k_raw_dev, v_raw_dev, batch_inputs, budget_s=12.0):
             "seconds": dt, "processor": platform.processor() or platform.machine()}
 
 
+def prefill_bench(steps, warmup):
+    """Blocked prefill on the 8M-token bank (4096 docs x 2048 tokens): 2048
+    query tokens in 32 blocks of 64, top-16 per block, causal 2048-token local
+    context, 32 query / 8 KV heads.  Returns tokens/s and the attention
+    kernel's MFMA utilisation (algorithmic flops / event-timed duration)."""
+    import torch
+    from long_context_memory_amd import msa, synth as S
+
+    dev = "cuda"
+    w = S.workload("c3")
+    log(f"prefill: building {w.name}: {w.n_docs} docs, {w.T} tokens")
+    bank = msa.Bank(w.doc_len, w.h_r, w.h_kv, w.dtype, dev, rope_base=w.rope_base)
+    step_docs = 1024
+    off = S.doc_token_offsets(w)
+    for n0 in range(0, w.n_docs, step_docs):
+        n1 = min(w.n_docs, n0 + step_docs)
+        r = S.route_vectors(w, dev, int(off[n0]), int(off[n1]))
+        k_raw, v_raw = S.kv_raw(w, dev, int(off[n0]), int(off[n1]))
+        bank.build(n0, n1, r, k_raw, v_raw)
+        torch.cuda.synchronize()
+        del r, k_raw, v_raw
+    q = S.queries(w, dev)
+    rt = S.prefill_route_tokens(w, dev)
+    lk, lv = S.local_raw(w, dev)
+    k_loc, v_loc, L = bank.prepare_local(lk[None], lv[None], w.P0)
+    q_pos = w.P0 + (w.L_loc - w.B)
+    ws = bank.workspace(msa.MSA_PREFILL, w.B, w.h_q, w.k, w.block)
+    nb = w.B // w.block
+    outs = (torch.empty((1, nb, w.k), dtype=torch.int32, device=dev),
+            torch.empty((1, nb, w.k), dtype=torch.float32, device=dev),
+            torch.empty((1, w.B, w.h_q, 128), dtype=torch.float32, device=dev))
+
+    def step():
+        bank.step(q, q_pos, w.k, k_loc, v_loc, L, route_tokens=rt, mode=msa.MSA_PREFILL,
+                  block=w.block, ws=ws, outputs=outs)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    msa.timer_enable(True)
+    msa.timer_read(msa.MSA_TIMER_ATTENTION)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    att_ms, att_n = msa.timer_read(msa.MSA_TIMER_ATTENTION)
+    msa.timer_enable(False)
+    # algorithmic flops: QK^T and PV over every unmasked (query, key) pair
+    doc_pairs = w.B * w.k * 2048
+    causal_pairs = sum(range(w.L_loc - w.B + 1, w.L_loc + 1))
+    flops = (doc_pairs + causal_pairs) * w.h_q * 128 * 4
+    # bytes: each block's selected documents' K/V once + the causal local prefix
+    kv_bytes = (nb * w.k * 2048 + sum(min(w.L_loc, (b + 1) * w.block) for b in range(nb))) \
+        * w.h_kv * 128 * 2 * 2
+    att_s = att_ms * 1e-3 / max(att_n, 1)
+    return {"workload": "blocked prefill: 8M-token bank (4096 docs x 2048 tokens), 2048 query "
+                        "tokens in 32 blocks of 64, top-16 per block, causal 2048-token local "
+                        "context, h_q=32, h_kv=8, d=128, bf16",
+            "tokens_per_s": w.B * steps / dt, "ms_per_step": dt * 1e3 / steps, "steps": steps,
+            "attention": {"bound": "mfma", "achieved": flops / att_s / 1e12,
+                          "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": flops / att_s / 1e12 / MFMA_PEAK_TFLOPS,
+                          "flops_per_launch": flops, "avg_launch_us": att_s * 1e6,
+                          "hbm_GBs": kv_bytes / att_s / 1e9}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -98,6 +166,7 @@ def main():
     ap.add_argument("--streams", type=int, default=2, help="HIP streams batches alternate over")
     ap.add_argument("--splits", type=int, default=0, help="attention splits (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-steps", type=int, default=20, help="0 skips the prefill leg")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported here "
@@ -185,6 +254,10 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(w, r, k_raw, v_raw, raw0)
+    if args.prefill_steps > 0:
+        del bank, batches, ws, outs, r, k_raw, v_raw, raw0
+        torch.cuda.empty_cache()
+        res["prefill"] = prefill_bench(args.prefill_steps, 3)
     print(json.dumps(res))
 
 

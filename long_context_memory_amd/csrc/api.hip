@@ -101,7 +101,12 @@ WsLayout ws_layout(const Bank& bk, int mode, int n_q, int h_q, int k, int block,
 
 constexpr int kMaxSplits = 256;
 
-int resolve_splits(const Bank& bk, int splits, int n_q, int k, int L_loc) {
+// Splits of the attention kernels: the MFMA prefill takes any count, the
+// split-K decode kernel (and the vector prefill) multiples of 4.
+int resolve_splits(const Bank& bk, int mode, int splits, int n_q, int h_q, int block, int k,
+                   int L_loc) {
+  if (mode == MSA_PREFILL && prefill_mfma_supported(bk, n_q, h_q, block))
+    return splits > 0 ? splits : prefill_auto_splits(bk, n_q, k, L_loc);
   if (splits > 0) return ((splits + 3) / 4) * 4;
   return decode_auto_splits(bk, n_q, k, L_loc);
 }
@@ -403,7 +408,8 @@ int msa_attend(const msa_bank* b, const msa_attend_args* a, void* stream) {
     return fail(MSA_EUNSUPPORTED, "host-resident bank: use msa_step or a source override");
   }
   if (a->splits < 0 || a->splits > kMaxSplits) return fail(MSA_EINVAL, "splits must be in [0, 256]");
-  const int splits = resolve_splits(bk, a->splits, a->n_q, a->k, a->L_loc);
+  const int splits =
+      resolve_splits(bk, a->mode, a->splits, a->n_q, a->h_q, a->block, a->k, a->L_loc);
   const WsLayout L = ws_layout(bk, a->mode, a->n_q, a->h_q, a->k, a->block, 1, splits);
   if (a->ws_bytes < L.total) return fail(MSA_ENOMEM, "workspace too small for msa_attend");
   char* w = (char*)a->ws;
@@ -446,7 +452,7 @@ int msa_step(const msa_bank* b, const msa_step_args* a, void* stream, void* copy
   const int n_groups = prefill ? a->n_q / a->block : a->n_q;
   const int k = a->k;
   if (a->splits < 0 || a->splits > kMaxSplits) return fail(MSA_EINVAL, "splits must be in [0, 256]");
-  const int splits = resolve_splits(bk, a->splits, a->n_q, k, a->L_loc);
+  const int splits = resolve_splits(bk, a->mode, a->splits, a->n_q, a->h_q, a->block, k, a->L_loc);
   const WsLayout L = ws_layout(bk, a->mode, a->n_q, a->h_q, k, a->block, a->hops, splits);
   if (a->ws_bytes < L.total) return fail(MSA_ENOMEM, "workspace too small for msa_step");
   const size_t esz = dtype_size(bk.desc.dtype);

@@ -208,7 +208,8 @@ hipError_t launch_prefill(const Bank& bk, const void* q_rot, int n_q, int h_q, c
 // sizes of the attention partial buffers
 size_t decode_partial_floats(int B, int h_kv, int G, int splits);
 int decode_auto_splits(const Bank& bk, int B, int k, int L_loc);
-size_t prefill_partial_floats(int n_q, int h_q, int block, int splits);
-int prefill_auto_splits(const Bank& bk, int n_q, int h_q, int block, int k, int L_loc);
+size_t prefill_partial_floats(int n_q, int h_kv, int splits);
+int prefill_auto_splits(const Bank& bk, int n_q, int k, int L_loc);
+bool prefill_mfma_supported(const Bank& bk, int n_q, int h_q, int block);
 
 }  // namespace msa
