@@ -90,7 +90,7 @@ def cpu_baseline(w, r_dev, k_raw_dev, v_raw_dev, batch_inputs, budget_s=12.0):
             "seconds": dt, "processor": platform.processor() or platform.machine()}
 
 
-def prefill_bench(steps, warmup):
+def prefill_bench(steps, warmup, splits=0):
     """Blocked prefill on the 8M-token bank (4096 docs x 2048 tokens): 2048
     query tokens in 32 blocks of 64, top-16 per block, causal 2048-token local
     context, 32 query / 8 KV heads.  Returns tokens/s and the attention
@@ -116,7 +116,7 @@ def prefill_bench(steps, warmup):
     lk, lv = S.local_raw(w, dev)
     k_loc, v_loc, L = bank.prepare_local(lk[None], lv[None], w.P0)
     q_pos = w.P0 + (w.L_loc - w.B)
-    ws = bank.workspace(msa.MSA_PREFILL, w.B, w.h_q, w.k, w.block)
+    ws = bank.workspace(msa.MSA_PREFILL, w.B, w.h_q, w.k, w.block, splits=splits)
     nb = w.B // w.block
     outs = (torch.empty((1, nb, w.k), dtype=torch.int32, device=dev),
             torch.empty((1, nb, w.k), dtype=torch.float32, device=dev),
@@ -124,7 +124,7 @@ def prefill_bench(steps, warmup):
 
     def step():
         bank.step(q, q_pos, w.k, k_loc, v_loc, L, route_tokens=rt, mode=msa.MSA_PREFILL,
-                  block=w.block, ws=ws, outputs=outs)
+                  block=w.block, ws=ws, outputs=outs, splits=splits)
 
     for _ in range(warmup):
         step()
@@ -167,6 +167,7 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="attention splits (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=20, help="0 skips the prefill leg")
+    ap.add_argument("--prefill-splits", type=int, default=0, help="token splits (0: automatic)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported here "
@@ -257,7 +258,7 @@ def main():
     if args.prefill_steps > 0:
         del bank, batches, ws, outs, r, k_raw, v_raw, raw0
         torch.cuda.empty_cache()
-        res["prefill"] = prefill_bench(args.prefill_steps, 3)
+        res["prefill"] = prefill_bench(args.prefill_steps, 3, args.prefill_splits)
     print(json.dumps(res))
 
 

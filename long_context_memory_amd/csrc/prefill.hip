@@ -7,16 +7,20 @@
 // (causal), with the 1/sqrt(d) scale (mlqm.cn MLA/CSA article, section 6.2).
 //
 // One workgroup = (block of 64 queries, KV head, token split): 256 rows
-// (64 queries x 4 query heads of the KV head), 4 waves of 64 rows.  Each
-// 64-token K/V tile is staged once in LDS (double-buffered, XOR-swizzled
-// 16-byte chunks) and shared by all 256 rows: 256 flop per byte of K/V.
-// Both contractions use v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
-// Scores are computed transposed, S^T = K . Q^T (tokens x rows), so the
-// accumulator layout of S^T is exactly the B-operand layout P^T needs for
-// O^T = V^T . P^T (the contraction order over the tile's tokens is permuted
-// consistently in both operands): probabilities never leave registers.
-// Online softmax in base 2 (queries are pre-scaled by log2 e / sqrt(d)).
+// (64 queries x 4 query heads of the KV head) in 8 waves of 32 rows, two
+// waves per SIMD so one wave's softmax overlaps the other's matrix work.
+// Each 64-token K/V tile is staged once in LDS and shared by all 256 rows:
+// 256 flop per byte of K/V.  Tiles stream through a 4-stage LDS ring filled
+// by direct global->LDS loads (no register staging), three tiles in flight
+// while one is consumed.  Both contractions use v_mfma_f32_32x32x16_bf16 with
+// fp32 accumulation.  Scores are computed transposed, S^T = K . Q^T (tokens
+// x rows), so the accumulator of S^T is already laid out as the B operand
+// P^T of O^T = V^T . P^T; K rows are permuted inside each 16-row group when
+// staged so that every lane's 8 probabilities of a 16-token k-step are 8
+// consecutive tokens, i.e. one 16-byte V^T read.  Online softmax in base 2
+// (queries are pre-scaled by log2 e / sqrt(d)).
 #include <algorithm>
+#include <type_traits>
 
 #include "msa_internal.h"
 
@@ -31,11 +35,15 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kRows = 256;          // rows per workgroup (64 queries x 4 heads)
-constexpr int kQBlock = 64;         // queries per routing block handled here
-constexpr int kPG = 4;              // query heads per KV head handled here
+constexpr int kRows = 256;           // rows per workgroup (64 queries x 4 heads)
+constexpr int kQBlock = 64;          // queries per routing block handled here
+constexpr int kPG = 4;               // query heads per KV head handled here
+constexpr int kWaves = 8;            // 32 rows each
+constexpr int kThreads = 64 * kWaves;
 constexpr int kTileB = 64 * kD * 2;  // bytes of one K (or V) tile in bf16
+constexpr int kStages = 4;           // LDS ring depth (K + V tile per stage)
 
 struct PrefillP {
   const uint16_t* q;  // [n_q][h_q][128] rotated, pre-scaled
@@ -56,21 +64,70 @@ __device__ __forceinline__ f32x16_t mfma32(const bf16x8_t& a, const bf16x8_t& b,
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) { return pack_bf16x2(lo, hi); }
+// hardware round-to-nearest-even pack of two floats into a bf16 pair
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
 
-__global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillP p) {
+// One 16-byte global->LDS copy per lane: lane l's bytes land at
+// lds_wave_base + 16*l (the base is wave-uniform).
+__device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+// LDS row r of a staged K tile holds token perm16(r): bits 2 and 3 swapped.
+__device__ __forceinline__ int perm16(int r) {
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+// s_waitcnt immediates that wait on the vector-memory counter only
+// (vmcnt in bits 3:0, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+constexpr int kWaitVm0 = 0xF70, kWaitVm8 = 0xF78;
+
+// Wait until the tile of the ring's oldest stage has landed -- two younger
+// tiles (8 loads per lane) may stay in flight -- then a workgroup barrier.
+// No memory fence: the loads being waited for write LDS only, and a fence's
+// wait for every outstanding load would drain the ring.  The wait goes
+// through the builtin (not asm) so the compiler's own wait insertion sees it
+// and adds none of its own.
+__device__ __forceinline__ void wait_oldest_tile_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWaitVm8);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+struct Tile {
+  const uint16_t* kb;
+  const uint16_t* vb;
+  int nvalid;
+  int t0;  // token offset inside the segment
+  bool local;
+};
+
+__global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillP p) {
   const int split = blockIdx.x, h = blockIdx.y, blk = blockIdx.z;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
   const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
   const int k = p.k;
   const int causal_base = p.L_loc - p.n_q;  // local index of query 0
 
   __shared__ int64_t s_koff[kMaxK + 1], s_voff[kMaxK + 1];
   __shared__ int s_len[kMaxK + 1], s_tile0[kMaxK + 2];
-  __shared__ __attribute__((aligned(16))) uint8_t s_k[2][kTileB];
-  __shared__ __attribute__((aligned(16))) uint8_t s_v[2][kTileB];
-  __shared__ __attribute__((aligned(16))) uint8_t s_q[kRows * kD * 2];  // [row][16 chunks], swizzled
+  // the ring: one array per stage (K tile, then V^T tile), so the compiler
+  // can tell the stages apart and wait only on the loads that fill a stage
+  __shared__ __attribute__((aligned(1024))) uint8_t s_kv0[2 * kTileB];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_kv1[2 * kTileB];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_kv2[2 * kTileB];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_kv3[2 * kTileB];
+  static_assert(kStages == 4, "one array per ring stage");
+  auto stage_buf = [&](auto st) -> uint8_t* {
+    constexpr int S = decltype(st)::value;
+    return S == 0 ? s_kv0 : S == 1 ? s_kv1 : S == 2 ? s_kv2 : s_kv3;
+  };
 
   if (tid < k) {
     const int id = p.ids[(size_t)blk * k + tid];
@@ -104,50 +161,32 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillP p) {
   const int u0 = (int)((int64_t)NT * split / p.S);
   const int u1 = (int)((int64_t)NT * (split + 1) / p.S);
 
-  // ---- Q rows of the workgroup staged in LDS: row R = 64*wave + n ->
-  // query 16*wave + n/4, head n%4; 16-byte chunk c at (c ^ (R & 15)).
-  const int l32 = lane & 31, hl = lane >> 5;
+  // ---- this lane's row: R = 32*wave + l32 -> query 8*wave + l32/4, head l32%4.
+  // Q^T B operand of k-step kk: channels 16*kk + 8*hl .. +7 of that row.
+  bf16x8_t qf[8];
+  {
+    const int qi = blk * kQBlock + 8 * wave + (l32 >> 2);
+    const uint16_t* qrow = p.q + ((size_t)qi * p.h_q + (size_t)h * kPG + (l32 & 3)) * kD + 8 * hl;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int f = tid + 256 * i;  // 256 rows x 16 chunks
-    const int R = f >> 4, c = f & 15;
-    const int qi = blk * kQBlock + (R >> 2);
-    const uint16_t* qrow = p.q + ((size_t)qi * p.h_q + (size_t)h * kPG + (R & 3)) * kD;
-    *reinterpret_cast<uint4*>(&s_q[R * 256 + ((c ^ (R & 15)) << 4)]) =
-        *reinterpret_cast<const uint4*>(qrow + 8 * c);
+    for (int kk = 0; kk < 8; ++kk)
+      qf[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qrow + 16 * kk));
   }
-  // Q^T B operand for row tile nt, k-step kk: row 32*nt + l32 of this wave,
-  // channels 16*kk + 8*hl .. +7
-  auto qfrag = [&](int nt, int kk) {
-    const int R = 64 * wave + 32 * nt + l32, c = 2 * kk + hl;
-    return __builtin_bit_cast(bf16x8_t,
-                              *reinterpret_cast<const uint4*>(&s_q[R * 256 + ((c ^ (R & 15)) << 4)]));
-  };
-  // local (causal) index of each of this lane's two rows; the wave's smallest
-  const int li_wave_min = causal_base + blk * kQBlock + 16 * wave;
-  int li[2];
+  // Q must have landed before the ring starts: its wait counts assume
+  // nothing else in flight (an asm use makes the compiler wait here).
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) li[nt] = causal_base + blk * kQBlock + 16 * wave + ((32 * nt + l32) >> 2);
+  for (int kk = 0; kk < 8; ++kk) asm volatile("" ::"v"(qf[kk]));
+  const int li_wave_min = causal_base + blk * kQBlock + 8 * wave;
+  const int li = li_wave_min + (l32 >> 2);  // local (causal) index of this lane's row
 
-  f32x16_t o[4][2];  // O^T: [channel tile 0..3][row tile 0..1]
+  f32x16_t o[4];  // O^T: [channel tile 0..3], column = this lane's row
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[dt][nt][e] = 0.f;
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+    for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
 
-  // ---- tile staging: 256 threads x (4 K + 4 V) 16-byte chunks
-  int r = 0;
-  struct Tile {
-    const uint16_t* kb;
-    const uint16_t* vb;
-    int nvalid;
-    int t0;     // token offset inside the segment
-    bool local;
-  };
-  auto tile_at = [&](int u) {
+  int r_issue = 0, r_comp = 0;
+  auto tile_at = [&](int& r, int u) {
     while (u >= __builtin_amdgcn_readfirstlane(s_tile0[r + 1])) ++r;
     Tile t;
     t.t0 = (u - __builtin_amdgcn_readfirstlane(s_tile0[r])) * 64;
@@ -161,164 +200,154 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillP p) {
     t.vb = (t.local ? p.vl : p.vs) + voff + (size_t)t.t0 * kD;
     return t;
   };
-  uint4 stg[8];
-  auto fetch = [&](const Tile& t) {
+  // Stage a tile: wave w's load i fills 1 KB j = w + 8*i of the K tile (LDS
+  // rows 4j..4j+3, 16-byte chunk c of row r at slot c ^ (r & 15)) and 1 KB j
+  // of the V^T tile (channel rows 8j..8j+7, chunk cv of row d at slot
+  // cv ^ (d & 7)).  K rows past the tile's valid tokens repeat its last
+  // valid row (their scores are masked); V^T tiles are zero-padded in memory.
+  auto issue = [&](const Tile& t, uint8_t* base) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int f = tid + 256 * i;
-      const int row = f >> 4, c = f & 15;  // K: 64 rows x 16 chunks
-      stg[i] = row < t.nvalid ? *reinterpret_cast<const uint4*>(t.kb + row * kD + c * 8)
-                              : make_uint4(0, 0, 0, 0);
-      const int d = f >> 3, cv = f & 7;  // V^T: 128 rows x 8 chunks (zero-padded tiles)
-      stg[4 + i] = *reinterpret_cast<const uint4*>(t.vb + d * 64 + cv * 8);
+    for (int i = 0; i < 2; ++i) {
+      const int j = wave + kWaves * i;
+      const int r = 4 * j + (lane >> 4);
+      const int tok = min(perm16(r), t.nvalid - 1);
+      const int c = (lane & 15) ^ (r & 15);
+      dma16(t.kb + (size_t)tok * kD + 8 * c, base + 1024 * j);
     }
-  };
-  auto stash = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int f = tid + 256 * i;
-      const int row = f >> 4, c = f & 15;
-      *reinterpret_cast<uint4*>(&s_k[buf][row * 256 + ((c ^ (row & 15)) << 4)]) = stg[i];
-      const int d = f >> 3, cv = f & 7;
-      *reinterpret_cast<uint4*>(&s_v[buf][d * 128 + ((cv ^ (d & 7)) << 4)]) = stg[4 + i];
+    for (int i = 0; i < 2; ++i) {
+      const int j = wave + kWaves * i;
+      const int d = 8 * j + (lane >> 3);
+      const int cv = (lane & 7) ^ (d & 7);
+      dma16(t.vb + d * 64 + 8 * cv, base + kTileB + 1024 * j);
     }
   };
 
-  Tile cur{};
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  // Every step issues exactly one tile (tile indices past the split's end
+  // repeat its last tile), so the ring's wait counts are the same on every
+  // path.
+  const int u_last = u1 - 1;
   if (u0 < u1) {
-    cur = tile_at(u0);
-    fetch(cur);
-    stash(0);
+    issue(tile_at(r_issue, u0), stage_buf(I0{}));
+    issue(tile_at(r_issue, min(u0 + 1, u_last)), stage_buf(I1{}));
+    issue(tile_at(r_issue, min(u0 + 2, u_last)), stage_buf(I2{}));
   }
-  __syncthreads();
-  for (int u = u0; u < u1; ++u) {
-    const int buf = (u - u0) & 1;
-    const bool has_next = u + 1 < u1;
-    Tile nxt{};
-    if (has_next) {
-      nxt = tile_at(u + 1);
-      fetch(nxt);  // in flight during this tile's math
-    }
-    const uint8_t* sk = s_k[buf];
-    const uint8_t* sv = s_v[buf];
 
-    // ---- two halves of 32 tokens (mt).  Each half: S^T = K . Q^T for the 2
-    // row tiles, mask, lazy-rescaled softmax, then O^T += V^T . P^T over the
-    // half's two 16-token k-steps.  Lazy rescaling: probabilities are taken
-    // relative to a per-row reference m_run that only moves (rescaling O and
-    // l) when a row max exceeds it by more than 8 in log2 units, so p <= 256;
-    // O otherwise stays untouched in the accumulators.
-    // Element e of s[nt]: token 32*mt + 8*(e/4) + 4*hl + (e%4), row 32*nt + l32.
-    const bool need_mask = cur.nvalid < 64 || (cur.local && cur.t0 + 63 > li_wave_min);
+  // one ring step: tile u sits in stage st; tile u + 3 goes to stage st + 3
+  auto step = [&](auto st, int u) {
+    constexpr int S = decltype(st)::value;
+    wait_oldest_tile_barrier();
+    issue(tile_at(r_issue, min(u + kStages - 1, u_last)),
+          stage_buf(std::integral_constant<int, (S + kStages - 1) % kStages>{}));
+    if (u >= u1) return;  // ring steps past the split's end only keep the waits uniform
+    const Tile cur = tile_at(r_comp, u);
+    const uint8_t* sk = stage_buf(st);
+    const uint8_t* sv = sk + kTileB;
+
+    // ---- S^T - m_use = K . Q^T - m_use for both 32-token halves (mt).
+    // Element e of s[mt] is token 32*mt + 16*(e/8) + 8*hl + e%8 (the staged
+    // row permutation), column = this lane's row.
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    f32x16_t s[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      f32x16_t s[2];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[nt][e] = 0.f;
+      for (int e = 0; e < 16; ++e) s[mt][e] = -m_use;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
         const int row = 32 * mt + l32, c = 2 * kk + hl;
         const bf16x8_t a = __builtin_bit_cast(
             bf16x8_t, *reinterpret_cast<const uint4*>(&sk[row * 256 + ((c ^ (row & 15)) << 4)]));
-        s[0] = mfma32(a, qfrag(0, kk), s[0]);
-        s[1] = mfma32(a, qfrag(1, kk), s[1]);
-      }
-      float mx[2];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        float m = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float v = s[nt][e];
-          if (need_mask) {
-            const int t = 32 * mt + 8 * (e >> 2) + 4 * hl + (e & 3);
-            const bool ok = t < cur.nvalid && (!cur.local || cur.t0 + t <= li[nt]);
-            v = ok ? v : -INFINITY;
-            s[nt][e] = v;
-          }
-          m = fmaxf(m, v);
-        }
-        mx[nt] = fmaxf(m, __shfl_xor(m, 32, 64));
-      }
-      const bool grow = mx[0] > m_run[0] + 8.f || mx[1] > m_run[1] + 8.f;
-      if (__builtin_amdgcn_readfirstlane((int)(__ballot(grow) != 0))) {
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const float m_new = mx[nt] > m_run[nt] + 8.f ? mx[nt] : m_run[nt];
-          const float alpha =
-              m_new == m_run[nt] ? 1.f : __builtin_amdgcn_exp2f(m_run[nt] - m_new);
-          m_run[nt] = m_new;
-          l_run[nt] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) o[dt][nt][e] *= alpha;
-        }
-      }
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const float m_use = m_run[nt] == -INFINITY ? 0.f : m_run[nt];
-        float ls = 0.f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float pe = __builtin_amdgcn_exp2f(s[nt][e] - m_use);
-          s[nt][e] = pe;
-          ls += pe;
-        }
-        l_run[nt] += ls;
-      }
-      // O^T += V^T . P^T: k-step hh covers tokens 32mt+16hh+4hl+[0..3], +8+[0..3]
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        bf16x8_t pb[2];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          uint4 w;
-          w.x = pack2(s[nt][8 * hh + 0], s[nt][8 * hh + 1]);
-          w.y = pack2(s[nt][8 * hh + 2], s[nt][8 * hh + 3]);
-          w.z = pack2(s[nt][8 * hh + 4], s[nt][8 * hh + 5]);
-          w.w = pack2(s[nt][8 * hh + 6], s[nt][8 * hh + 7]);
-          pb[nt] = __builtin_bit_cast(bf16x8_t, w);
-        }
-        const int tk = 32 * mt + 16 * hh + 4 * hl;
-        const int c0 = tk >> 3, c1 = (tk + 8) >> 3, half = (tk >> 2) & 1;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const int d = 32 * dt + l32;
-          const uint2 lo =
-              *reinterpret_cast<const uint2*>(&sv[d * 128 + ((c0 ^ (d & 7)) << 4) + 8 * half]);
-          const uint2 hi =
-              *reinterpret_cast<const uint2*>(&sv[d * 128 + ((c1 ^ (d & 7)) << 4) + 8 * half]);
-          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-          o[dt][0] = mfma32(a, pb[0], o[dt][0]);
-          o[dt][1] = mfma32(a, pb[1], o[dt][1]);
-        }
+        s[mt] = mfma32(a, qf[kk], s[mt]);
       }
     }
-
-    if (has_next) stash(buf ^ 1);
-    __syncthreads();
-    cur = nxt;
-  }
-
-  // ---- partials: row n of this wave (lane holds row 32*nt + l32)
+    // Tile tokens past the segment's end, and local tokens after this row's
+    // own position, are masked: token t is kept iff t < lim.
+    if (cur.nvalid < 64 || (cur.local && cur.t0 + 63 > li_wave_min)) {
+      const int lim = (cur.local ? min(cur.nvalid, li - cur.t0 + 1) : cur.nvalid) - 8 * hl;
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) l_run[nt] += __shfl_xor(l_run[nt], 32, 64);
-  const size_t pbase = ((((size_t)blk * p.h_kv + h) * p.S + split) * kRows + 64 * wave) * (kD + 2);
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    float* pr = p.part + pbase + (size_t)(32 * nt + l32) * (kD + 2);
-    if (hl == 0) {
-      pr[0] = m_run[nt];
-      pr[1] = l_run[nt];
+        for (int e = 0; e < 16; ++e)
+          s[mt][e] = 32 * mt + 16 * (e >> 3) + (e & 7) < lim ? s[mt][e] : -INFINITY;
     }
+    float mx = -INFINITY;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) pr[2 + 32 * dt + 8 * (e >> 2) + 4 * hl + (e & 3)] = o[dt][nt][e];
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mt][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // Lazy rescaling: probabilities are relative to a per-row reference
+    // m_run that moves (rescaling O and l) only when a row max exceeds it by
+    // more than 8 in log2 units, so p <= 256 and O is rarely touched.
+    // mx is relative to m_use.
+    const bool grow = mx + m_use > m_run + 8.f;
+    if (__builtin_amdgcn_readfirstlane((int)(__ballot(grow) != 0))) {
+      if (grow) {
+        const float m_new = mx + m_use;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) s[mt][e] -= mx;
+      }
+    }
+    // ---- P^T = exp2(S^T - m_run) as bf16, and O^T += V^T . P^T over four
+    // 16-token k-steps (ks): lane's k-elements are tokens 16*ks + 8*hl .. +7,
+    // elements 8*(ks%2) .. +7 of s[ks/2].  The row sum takes the rounded p.
+    const uint32_t ones = 0x3f803f80u;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = 8 * (ks & 1) + 2 * i;
+        w[i] = cvt_pk_bf16(__builtin_amdgcn_exp2f(s[ks >> 1][e]),
+                           __builtin_amdgcn_exp2f(s[ks >> 1][e + 1]));
+        l_run = dot2_bf16(w[i], ones, l_run);
+      }
+      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+      const int cv = 2 * ks + hl;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int d = 32 * dt + l32;
+        const bf16x8_t a = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const uint4*>(&sv[d * 128 + ((cv ^ (d & 7)) << 4)]));
+        o[dt] = mfma32(a, pb, o[dt]);
+      }
+    }
+  };
+  for (int u = u0; u < u1; u += kStages) {
+    // all four steps run on every pass, so every wave meets the same
+    // barriers and the wait counts hold on every path
+    step(I0{}, u);
+    step(I1{}, u + 1);
+    step(I2{}, u + 2);
+    step(I3{}, u + 3);
   }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no load may still write LDS after the workgroup ends
+
+  // ---- partials of this lane's row (both lane halves hold half the tokens' l)
+  l_run += __shfl_xor(l_run, 32, 64);
+  float* pr = p.part + ((((size_t)blk * p.h_kv + h) * p.S + split) * kRows + 32 * wave + l32) * (kD + 2);
+  if (hl == 0) {
+    pr[0] = m_run;
+    pr[1] = l_run;
+  }
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) pr[2 + 32 * dt + 8 * (e >> 2) + 4 * hl + (e & 3)] = o[dt][e];
 }
 
 // merge the S partials of each (block, KV head): base-2 log-sum-exp per row
@@ -340,9 +369,9 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(const float* __res
       acc = fmaf(w, ps[2 + d], acc);
     }
   }
-  const int wave = row >> 6, n = row & 63;
-  const int qi = blk * kQBlock + 16 * wave + (n >> 2);
-  out[((size_t)qi * h_q + (size_t)h * kPG + (n & 3)) * kD + d] = L > 0.f ? acc / L : 0.f;
+  // row R -> query R/4, head R%4 of this KV head
+  const int qi = blk * kQBlock + (row >> 2);
+  out[((size_t)qi * h_q + (size_t)h * kPG + (row & 3)) * kD + d] = L > 0.f ? acc / L : 0.f;
 }
 
 }  // namespace
@@ -352,12 +381,12 @@ size_t prefill_partial_floats(int n_q, int h_kv, int splits) {
 }
 
 int prefill_auto_splits(const Bank& bk, int n_q, int k, int L_loc) {
-  // enough workgroups to cover the GPU twice over
+  // one workgroup per compute unit (a workgroup holds 128 KiB of LDS)
   const int n_blocks = std::max(1, n_q / kQBlock);
   const int64_t wg = (int64_t)n_blocks * bk.desc.h_kv;
   const double avg_doc = (double)bk.n_tokens / bk.desc.n_docs;
   const int tiles = (int)std::max(1.0, k * avg_doc / 64 + (L_loc + 63) / 64);
-  int s = (int)((512 + wg - 1) / wg);
+  int s = (int)((256 + wg - 1) / wg);
   return std::max(1, std::min({s, tiles, 64}));
 }
 
@@ -393,7 +422,7 @@ hipError_t launch_prefill(const Bank& bk, const void* q_rot, int n_q, int h_q, c
   const int n_blocks = n_q / kQBlock;
   timer_mark(0, true, s);
   hipLaunchKernelGGL(prefill_mfma_kernel, dim3((unsigned)splits, (unsigned)p.h_kv, (unsigned)n_blocks),
-                     dim3(256), 0, s, p);
+                     dim3(kThreads), 0, s, p);
   timer_mark(0, false, s);
   hipLaunchKernelGGL(prefill_combine_kernel, dim3(kRows / 2, (unsigned)p.h_kv, (unsigned)n_blocks),
                      dim3(256), 0, s, part, splits, p.h_kv, h_q, out);
