@@ -84,17 +84,17 @@ __device__ __forceinline__ int perm16(int r) {
 
 // s_waitcnt immediates that wait on the vector-memory counter only
 // (vmcnt in bits 3:0, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
-constexpr int kWaitVm0 = 0xF70, kWaitVm8 = 0xF78;
+constexpr int kWaitVm0 = 0xF70, kWaitVm4 = 0xF74, kWaitVm8 = 0xF78;
 
-// Wait until the tile of the ring's oldest stage has landed -- two younger
-// tiles (8 loads per lane) may stay in flight -- then a workgroup barrier.
-// No memory fence: the loads being waited for write LDS only, and a fence's
-// wait for every outstanding load would drain the ring.  The wait goes
-// through the builtin (not asm) so the compiler's own wait insertion sees it
-// and adds none of its own.
-__device__ __forceinline__ void wait_oldest_tile_barrier() {
+// Workgroup barrier after waiting until at most WAIT_IMM's count of this
+// lane's ring loads are in flight.  No memory fence: the loads being waited
+// for write LDS only, and a fence's wait for every outstanding load would
+// drain the ring.  The wait goes through the builtin (not asm) so the
+// compiler's own wait insertion sees it and adds none of its own.
+template <int WAIT_IMM>
+__device__ __forceinline__ void wait_ring_barrier() {
   asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(kWaitVm8);
+  __builtin_amdgcn_s_waitcnt(WAIT_IMM);
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillP p) {
     for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  int r_issue = 0, r_comp = 0;
+  int r_issue = 0;
   auto tile_at = [&](int& r, int u) {
     while (u >= __builtin_amdgcn_readfirstlane(s_tile0[r + 1])) ++r;
     Tile t;
@@ -227,44 +227,33 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillP p) {
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  // Every step issues exactly one tile (tile indices past the split's end
-  // repeat its last tile), so the ring's wait counts are the same on every
-  // path.
-  const int u_last = u1 - 1;
-  if (u0 < u1) {
-    issue(tile_at(r_issue, u0), stage_buf(I0{}));
-    issue(tile_at(r_issue, min(u0 + 1, u_last)), stage_buf(I1{}));
-    issue(tile_at(r_issue, min(u0 + 2, u_last)), stage_buf(I2{}));
-  }
+  // K fragment (A operand) of the staged tile for token half mt, k-step kk:
+  // LDS row 32*mt + l32, channels 16*kk + 8*hl .. +7
+  auto kfrag = [&](const uint8_t* sk, int mt, int kk) __attribute__((always_inline)) {
+    const int row = 32 * mt + l32, c = 2 * kk + hl;
+    return __builtin_bit_cast(
+        bf16x8_t, *reinterpret_cast<const uint4*>(&sk[row * 256 + ((c ^ (row & 15)) << 4)]));
+  };
+  // V^T fragment (A operand) for channel tile dt, 16-token k-step ks: channel
+  // 32*dt + l32, tokens 16*ks + 8*hl .. +7
+  auto vfrag = [&](const uint8_t* sv, int ks, int dt) __attribute__((always_inline)) {
+    const int d = 32 * dt + l32, cv = 2 * ks + hl;
+    return __builtin_bit_cast(
+        bf16x8_t, *reinterpret_cast<const uint4*>(&sv[d * 128 + ((cv ^ (d & 7)) << 4)]));
+  };
+  auto ref_of = [](float m) { return m == -INFINITY ? 0.f : m; };
 
-  // one ring step: tile u sits in stage st; tile u + 3 goes to stage st + 3
-  auto step = [&](auto st, int u) {
-    constexpr int S = decltype(st)::value;
-    wait_oldest_tile_barrier();
-    issue(tile_at(r_issue, min(u + kStages - 1, u_last)),
-          stage_buf(std::integral_constant<int, (S + kStages - 1) % kStages>{}));
-    if (u >= u1) return;  // ring steps past the split's end only keep the waits uniform
-    const Tile cur = tile_at(r_comp, u);
-    const uint8_t* sk = stage_buf(st);
-    const uint8_t* sv = sk + kTileB;
-
-    // ---- S^T - m_use = K . Q^T - m_use for both 32-token halves (mt).
-    // Element e of s[mt] is token 32*mt + 16*(e/8) + 8*hl + e%8 (the staged
-    // row permutation), column = this lane's row.
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    f32x16_t s[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[mt][e] = -m_use;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const int row = 32 * mt + l32, c = 2 * kk + hl;
-        const bf16x8_t a = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const uint4*>(&sk[row * 256 + ((c ^ (row & 15)) << 4)]));
-        s[mt] = mfma32(a, qf[kk], s[mt]);
-      }
-    }
+  // Scores of a tile, sc = S^T - m_ref, as two 32-token halves (mt).
+  // Element e of sc[mt] is token 32*mt + 16*(e/8) + 8*hl + e%8 (the staged
+  // row permutation), column = this lane's row.
+  //
+  // Before a tile's probabilities: mask, row max and the lazy rescale.
+  // Probabilities are relative to a per-row reference m_run that moves
+  // (rescaling O and l) only when a row max exceeds it by more than 8 in log2
+  // units, so p <= 256 and O is rarely touched.  The scores were taken
+  // relative to ref_of(m_run), which has not moved since.
+  auto softmax_pre = [&](const Tile& cur, f32x16_t(&sc)[2]) __attribute__((always_inline)) {
+    const float m_use = ref_of(m_run);
     // Tile tokens past the segment's end, and local tokens after this row's
     // own position, are masked: token t is kept iff t < lim.
     if (cur.nvalid < 64 || (cur.local && cur.t0 + 63 > li_wave_min)) {
@@ -273,18 +262,14 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillP p) {
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          s[mt][e] = 32 * mt + 16 * (e >> 3) + (e & 7) < lim ? s[mt][e] : -INFINITY;
+          sc[mt][e] = 32 * mt + 16 * (e >> 3) + (e & 7) < lim ? sc[mt][e] : -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mt][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // Lazy rescaling: probabilities are relative to a per-row reference
-    // m_run that moves (rescaling O and l) only when a row max exceeds it by
-    // more than 8 in log2 units, so p <= 256 and O is rarely touched.
-    // mx is relative to m_use.
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[mt][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));  // relative to m_use
     const bool grow = mx + m_use > m_run + 8.f;
     if (__builtin_amdgcn_readfirstlane((int)(__ballot(grow) != 0))) {
       if (grow) {
@@ -299,33 +284,82 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillP p) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) s[mt][e] -= mx;
+          for (int e = 0; e < 16; ++e) sc[mt][e] -= mx;
       }
     }
-    // ---- P^T = exp2(S^T - m_run) as bf16, and O^T += V^T . P^T over four
-    // 16-token k-steps (ks): lane's k-elements are tokens 16*ks + 8*hl .. +7,
-    // elements 8*(ks%2) .. +7 of s[ks/2].  The row sum takes the rounded p.
+  };
+
+  // Software pipeline: the scores of tile u + 1 go onto the matrix cores in
+  // the same straight-line block as tile u's exponentials and P.V, so the
+  // matrix and vector units overlap.  Every ring step issues exactly one
+  // tile (indices past the split's end repeat its last tile, and a score pass
+  // past the end is discarded), so the ring's wait counts are the same on
+  // every path.
+  const int u_last = u1 - 1;
+  f32x16_t sc[2];
+  Tile cur{};
+  int r_next = 0;
+  if (u0 < u1) {
+    issue(tile_at(r_issue, u0), stage_buf(I0{}));
+    issue(tile_at(r_issue, min(u0 + 1, u_last)), stage_buf(I1{}));
+    issue(tile_at(r_issue, min(u0 + 2, u_last)), stage_buf(I2{}));
+    wait_ring_barrier<kWaitVm8>();  // tile u0 landed
+    cur = tile_at(r_next, u0);
+    const uint8_t* sk = stage_buf(I0{});
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sc[mt][e] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) sc[mt] = mfma32(kfrag(sk, mt, kk), qf[kk], sc[mt]);
+    }
+  }
+
+  // ring step for tile u in stage st: tile u + 1 (stage st + 1) must have
+  // landed; tile u + 3 goes to stage st + 3, which held tile u - 1
+  auto step = [&](auto st, int u) __attribute__((always_inline)) {
+    constexpr int S = decltype(st)::value;
+    wait_ring_barrier<kWaitVm4>();
+    issue(tile_at(r_issue, min(u + kStages - 1, u_last)),
+          stage_buf(std::integral_constant<int, (S + kStages - 1) % kStages>{}));
+    if (u >= u1) return;
+    softmax_pre(cur, sc);
+    const Tile nxt = tile_at(r_next, min(u + 1, u_last));
+    const uint8_t* sk = stage_buf(std::integral_constant<int, (S + 1) % kStages>{});
+    const uint8_t* sv = stage_buf(st) + kTileB;
+    const float m_ref = ref_of(m_run);
+    f32x16_t sn[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sn[mt][e] = -m_ref;
+    // k-step ks: 4 score MFMAs of tile u + 1 (half ks/2, k-steps
+    // 4*(ks%2) .. +3), then tile u's probabilities for tokens 16*ks + 8*hl
+    // .. +7 (elements 8*(ks%2) .. +7 of sc[ks/2]) as bf16 and their 4 P.V
+    // MFMAs.  The row sum takes the rounded p.
     const uint32_t ones = 0x3f803f80u;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int mt = ks >> 1, kk = 4 * (ks & 1) + j;
+        sn[mt] = mfma32(kfrag(sk, mt, kk), qf[kk], sn[mt]);
+      }
       uint32_t w[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = 8 * (ks & 1) + 2 * i;
-        w[i] = cvt_pk_bf16(__builtin_amdgcn_exp2f(s[ks >> 1][e]),
-                           __builtin_amdgcn_exp2f(s[ks >> 1][e + 1]));
+        w[i] = cvt_pk_bf16(__builtin_amdgcn_exp2f(sc[ks >> 1][e]),
+                           __builtin_amdgcn_exp2f(sc[ks >> 1][e + 1]));
         l_run = dot2_bf16(w[i], ones, l_run);
       }
       const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
-      const int cv = 2 * ks + hl;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const int d = 32 * dt + l32;
-        const bf16x8_t a = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const uint4*>(&sv[d * 128 + ((cv ^ (d & 7)) << 4)]));
-        o[dt] = mfma32(a, pb, o[dt]);
-      }
+      for (int dt = 0; dt < 4; ++dt) o[dt] = mfma32(vfrag(sv, ks, dt), pb, o[dt]);
     }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) sc[mt] = sn[mt];
+    cur = nxt;
   };
   for (int u = u0; u < u1; u += kStages) {
     // all four steps run on every pass, so every wave meets the same
