@@ -156,6 +156,7 @@ class Bank:
         self.dtype = _tdt(dtype)
         self.device = torch.device(device)
         self.kv_host = kv_loc == "host"
+        self.rope_base = float(rope_base)
         T = sum(self.doc_len)
         self.C = T // 256
         self.kv_tokens = int(kv_tokens) if kv_tokens is not None else T
@@ -274,3 +275,33 @@ class Bank:
         _check(lib.msa_step(self.handle, C.byref(a), _stream(stream), cs, C.byref(st)),
                "msa_step")
         return ids, scores, out, st
+
+
+def fill_host_store(bank: "Bank", slot_len, raw_kv, slots_per_pass: int = 64, stream=None):
+    """Fill a host-resident bank's pinned K/V store, laid out as consecutive
+    documents of lengths ``slot_len`` (the physical slots its kv_off points
+    at): each pass builds a temporary device bank over a range of slots
+    (document RoPE and the store layouts), then copies its stores to the
+    pinned host store.  ``raw_kv(t0, t1)`` returns the raw K and V of slot
+    tokens [t0, t1) on the device, [t1 - t0, h_kv, 128] each."""
+    if not bank.kv_host:
+        raise ValueError("fill_host_store needs a host-resident bank")
+    slot_len = [int(x) for x in slot_len]
+    starts = [0]
+    for L in slot_len:
+        starts.append(starts[-1] + L)
+    if starts[-1] != bank.kv_tokens:
+        raise ValueError("slot lengths do not cover the bank's kv_tokens")
+    per_tok = bank.h_kv * 128
+    for s0 in range(0, len(slot_len), slots_per_pass):
+        s1 = min(len(slot_len), s0 + slots_per_pass)
+        t0, t1 = starts[s0], starts[s1]
+        dev = Bank(slot_len[s0:s1], 1, bank.h_kv, bank.dtype, bank.device, rope_base=bank.rope_base,
+                   kr=torch.zeros((1, (t1 - t0) // 256, 128), dtype=bank.dtype, device=bank.device))
+        k_raw, v_raw = raw_kv(t0, t1)
+        dev.build(0, s1 - s0, None, k_raw, v_raw, stream=stream)
+        bank.k_store[t0 * per_tok:t1 * per_tok].copy_(dev.k_store)
+        bank.v_store[t0 * per_tok:t1 * per_tok].copy_(dev.v_store)
+        torch.cuda.synchronize(bank.device)
+        del dev, k_raw, v_raw
+

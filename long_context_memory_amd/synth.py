@@ -193,6 +193,40 @@ def doc_token_offsets(w: Workload) -> np.ndarray:
     return np.concatenate([[0], np.cumsum(np.asarray(w.doc_len, dtype=np.int64))])
 
 
+def host_slot_layout(w: Workload):
+    """Physical layout of a host-resident bank backed by w.host_slots document
+    slots (a stand-in for a store too large for host memory: the bytes each
+    step copies are those of the full bank, the contents repeat).  Documents
+    of the longest length share the first slots round-robin; every shorter
+    document has a slot of its own after them.
+
+    Returns (slot_len [S] tokens, kv_off [n_docs] token offset of each
+    document's slot)."""
+    L = np.asarray(w.doc_len, dtype=np.int64)
+    lmax = int(L.max())
+    short = np.nonzero(L != lmax)[0]
+    long_ids = np.nonzero(L == lmax)[0]
+    n_long = int(w.host_slots) - len(short)
+    if n_long < 1:
+        raise ValueError("host_slots must exceed the number of shorter documents")
+    slot_len = [lmax] * n_long + [int(L[n]) for n in short]
+    starts = np.concatenate([[0], np.cumsum(np.asarray(slot_len, dtype=np.int64))])
+    kv_off = np.empty(len(L), dtype=np.int64)
+    kv_off[long_ids] = starts[np.arange(len(long_ids)) % n_long]
+    kv_off[short] = starts[n_long + np.arange(len(short))]
+    return slot_len, kv_off
+
+
+def host_kv_raw(w: Workload, device="cpu", t0: int = 0, t1: Optional[int] = None):
+    """Raw (pre-RoPE) K and V of the host slots' tokens [t0, t1) (token
+    indices of the slot store), [t1 - t0, h_kv, d] each."""
+    slot_len, _ = host_slot_layout(w)
+    total = int(sum(slot_len))
+    t1 = total if t1 is None else t1
+    return (token_rows(w, "host_k", (w.h_kv, w.d), t0, t1, device, total=total),
+            token_rows(w, "host_v", (w.h_kv, w.d), t0, t1, device, total=total))
+
+
 def planted_targets(w: Workload):
     """For "direction" planting: query b's k target documents (disjoint across
     the batch) and, for each, the chunk inside it that carries the planted

@@ -1,0 +1,219 @@
+"""GPU parity, through the C ABI, of the host-resident bank (top-k readback,
+per-document host->device copies into staging, attention over the staged
+documents) and of multi-hop interleaved retrieval (the next hop's router
+query projected from this hop's output), against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+from long_context_memory_amd import synth as S
+from oracle import msa_oracle as O
+import msa_cases as M
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def msa():
+    from long_context_memory_amd import msa as m
+    return m
+
+
+_CACHE = {}
+
+
+def host_case(msa, name):
+    if name in _CACHE:
+        return _CACHE[name]
+    w = S.workload(name)
+    slot_len, kv_off = S.host_slot_layout(w)
+    kr = S.keys_direct(w, DEV).to(w.torch_dtype)  # [C, h_r, 128], the stored keys
+    bank = msa.Bank(w.doc_len, w.h_r, w.h_kv, w.dtype, DEV, kv_loc="host", kv_off=kv_off,
+                    kv_tokens=int(sum(slot_len)), rope_base=w.rope_base,
+                    kr=kr.permute(1, 0, 2).contiguous())
+    bank.build(0, w.n_docs)  # inverse norms of the given keys
+    msa.fill_host_store(bank, slot_len, lambda t0, t1: S.host_kv_raw(w, DEV, t0, t1))
+    kr_o = M.np64(kr)
+    inv_o = O.inverse_norms(kr_o)
+    q = S.queries(w, DEV)
+    q_route = S.route_queries(w, DEV)
+    lk, lv = S.local_raw(w, DEV)
+    k_loc, v_loc, L = bank.prepare_local(lk, lv, w.P0)
+    torch.cuda.synchronize()
+    c = dict(w=w, bank=bank, kr=kr, kr_o=kr_o, inv_o=inv_o, kv_off=kv_off, slot_len=slot_len,
+             q=q, q_route=q_route, lk=lk, lv=lv, k_loc=k_loc, v_loc=v_loc, L=L)
+    _CACHE[name] = c
+    return c
+
+
+def host_doc_kv(c, n):
+    """Oracle K (document-RoPE'd, rounded) and V of document n, from the raw
+    rows of the slot its kv_off points at."""
+    w = c["w"]
+    t0, L = int(c["kv_off"][n]), int(w.doc_len[n])
+    k_raw, v_raw = S.host_kv_raw(w, DEV, t0, t0 + L)
+    return (O.bank_keys_rotated(M.np64(k_raw), [L], w.rope_base, w.dtype), M.np64(v_raw))
+
+
+def test_host_bank_norms(msa):
+    c = host_case(msa, "c4_small")
+    inv = M.np64(c["bank"].inv_norm.t())
+    np.testing.assert_allclose(inv, c["inv_o"], rtol=2e-7, atol=0)
+
+
+def test_host_bank_step_matches_oracle(msa):
+    c = host_case(msa, "c4_small")
+    w, bank = c["w"], c["bank"]
+    ids, scores, out, st = bank.step(c["q"], w.q_pos, w.k, c["k_loc"], c["v_loc"], c["L"],
+                                     q_route=c["q_route"])
+    torch.cuda.synchronize()
+    so = O.cosine_doc_scores(M.np64(c["q_route"]), c["kr_o"], c["inv_o"], w.doc_len)
+    ids_np = ids[0].cpu().numpy()
+    M.check_topk(ids_np, scores[0].cpu().numpy(), so, w.k)
+    o_ids, _ = O.select_topk(so, w.k)
+    q, lk, lv = M.np64(c["q"]), M.np64(c["lk"]), M.np64(c["lv"])
+    cache, refs = {}, []
+    for b in range(w.B):
+        sel = o_ids[b] if set(o_ids[b].tolist()) == set(ids_np[b].tolist()) else ids_np[b]
+        for n in sel:
+            if n not in cache:
+                cache[n] = host_doc_kv(c, n)
+        refs.append(M.oracle_attend_decode(w, q[b], w.q_pos, sel, cache, lk[b], lv[b], w.P0))
+    mx, rel = M.check_out(out[0].cpu().numpy(), np.stack(refs), w.dtype, "host bank")
+    print(f"host bank: max abs {mx:.3e} rel rms {rel:.3e}")
+    # every distinct selected document is copied once, K and V
+    distinct = sorted(set(ids_np.ravel().tolist()))
+    tok_bytes = w.h_kv * 128 * 2
+    assert st.docs_copied == len(distinct)
+    assert st.bytes_copied == sum(2 * w.doc_len[n] * tok_bytes for n in distinct)
+
+
+def test_host_bank_equals_device_bank(msa):
+    """The same stores resident on the device give bit-identical results:
+    staging changes where the kernels read, not what they compute."""
+    c = host_case(msa, "c4_small")
+    w, hb = c["w"], c["bank"]
+    db = msa.Bank(w.doc_len, w.h_r, w.h_kv, w.dtype, DEV, kv_loc="device", kv_off=c["kv_off"],
+                  kv_tokens=hb.kv_tokens, rope_base=w.rope_base, kr=hb.kr,
+                  k_store=hb.k_store.to(DEV), v_store=hb.v_store.to(DEV))
+    db.build(0, w.n_docs)
+    args = (c["q"], w.q_pos, w.k, c["k_loc"], c["v_loc"], c["L"])
+    ids_h, sc_h, out_h, _ = hb.step(*args, q_route=c["q_route"])
+    ids_d, sc_d, out_d, st = db.step(*args, q_route=c["q_route"])
+    torch.cuda.synchronize()
+    assert torch.equal(ids_h, ids_d) and torch.equal(sc_h, sc_d)
+    assert torch.equal(out_h, out_d)
+    assert st.docs_copied == 0 and st.bytes_copied == 0
+
+
+def test_host_bank_copy_stream(msa):
+    """Copies on a separate stream, ordered before the attention by an event."""
+    c = host_case(msa, "c4_small")
+    w, bank = c["w"], c["bank"]
+    args = (c["q"], w.q_pos, w.k, c["k_loc"], c["v_loc"], c["L"])
+    _, _, ref, _ = bank.step(*args, q_route=c["q_route"])
+    cs = torch.cuda.Stream()
+    _, _, out, _ = bank.step(*args, q_route=c["q_route"], copy_stream=cs)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
+# --------------------------------------------------------------------------
+# interleaved multi-hop retrieval
+# --------------------------------------------------------------------------
+def interleave_case(msa, name):
+    key = "il/" + name
+    if key in _CACHE:
+        return _CACHE[key]
+    w = S.workload(name)
+    r = S.route_vectors(w, DEV)
+    k_raw, v_raw = S.kv_raw(w, DEV)
+    bank = msa.Bank(w.doc_len, w.h_r, w.h_kv, w.dtype, DEV, rope_base=w.rope_base)
+    bank.build(0, w.n_docs, r, k_raw, v_raw)
+    kr_o, inv_o = M.pool_oracle(w, r)
+    q = S.queries(w, DEV)
+    q_route = S.route_queries(w, DEV)
+    lk, lv = S.local_raw(w, DEV)
+    k_loc, v_loc, L = bank.prepare_local(lk, lv, w.P0)
+    wp = S.interleave_projection(w, DEV)
+    torch.cuda.synchronize()
+    c = dict(w=w, bank=bank, k_raw=k_raw, v_raw=v_raw, kr_o=kr_o, inv_o=inv_o, q=q,
+             q_route=q_route, lk=lk, lv=lv, k_loc=k_loc, v_loc=v_loc, L=L, wp=wp)
+    _CACHE[key] = c
+    return c
+
+
+def oracle_hop(c, qr, excl, ids_gpu):
+    """Oracle routing scores and attention outputs of one hop for router
+    queries qr [B, 1, d_r] (fp64) with exclusion mask excl (or None)."""
+    w = c["w"]
+    so = O.cosine_doc_scores(qr, c["kr_o"], c["inv_o"], w.doc_len, excl)
+    o_ids, _ = O.select_topk(so, w.k)
+    q, lk, lv = M.np64(c["q"]), M.np64(c["lk"]), M.np64(c["lv"])
+    cache, refs = c.setdefault("kv_cache", {}), []
+    for b in range(w.B):
+        sel = o_ids[b] if set(o_ids[b].tolist()) == set(ids_gpu[b].tolist()) else ids_gpu[b]
+        for n in sel:
+            if n not in cache:
+                cache[n] = M.oracle_doc_kv(w, c["k_raw"], c["v_raw"], n)
+        refs.append(M.oracle_attend_decode(w, q[b], w.q_pos, sel, cache, lk[b], lv[b], w.P0))
+    return so, o_ids, np.stack(refs)
+
+
+@pytest.mark.parametrize("exclude_selected", [False, True])
+def test_interleave_teacher_forced(msa, exclude_selected):
+    """Each hop against the oracle, the oracle's hop h + 1 taking the GPU's
+    hop-h output (and, with exclusion, the GPU's earlier selections)."""
+    c = interleave_case(msa, "c5_small")
+    w = c["w"]
+    ids, scores, out, _ = c["bank"].step(c["q"], w.q_pos, w.k, c["k_loc"], c["v_loc"], c["L"],
+                                         q_route=c["q_route"], hops=w.hops, w_proj=c["wp"],
+                                         exclude_selected=exclude_selected)
+    torch.cuda.synchronize()
+    ids_np, sc_np, out_np = ids.cpu().numpy(), scores.cpu().numpy(), out.cpu().numpy()
+    excl = np.zeros((w.B, w.n_docs), dtype=bool)
+    for h in range(w.hops):
+        qr = M.np64(c["q_route"]) if h == 0 else O.interleave_project(out_np[h - 1], M.np64(c["wp"]))
+        so, _, ref = oracle_hop(c, qr, excl if exclude_selected else None, ids_np[h])
+        M.check_topk(ids_np[h], sc_np[h], so, w.k)
+        mx, rel = M.check_out(out_np[h], ref, w.dtype, f"hop {h}")
+        print(f"hop {h}: max abs {mx:.3e} rel rms {rel:.3e}")
+        if exclude_selected:
+            for b in range(w.B):
+                assert not excl[b, ids_np[h][b]].any(), f"hop {h} row {b} reselected a document"
+                excl[b, ids_np[h][b]] = True
+
+
+def test_interleave_free_running(msa):
+    """The oracle running its own hops selects the same documents (barring a
+    near-tie at some hop, which is reported)."""
+    c = interleave_case(msa, "c5_small")
+    w = c["w"]
+    ids, _, out, _ = c["bank"].step(c["q"], w.q_pos, w.k, c["k_loc"], c["v_loc"], c["L"],
+                                    q_route=c["q_route"], hops=w.hops, w_proj=c["wp"])
+    torch.cuda.synchronize()
+    ids_np = ids.cpu().numpy()
+    qr = M.np64(c["q_route"])
+    for h in range(w.hops):
+        g = ids_np[h]
+        so, o_ids, ref = oracle_hop(c, qr, None, g)
+        srt = np.sort(so, axis=1)[:, ::-1]
+        gap = srt[:, w.k - 1] - srt[:, w.k] if w.n_docs > w.k else np.full(w.B, np.inf)
+        for b in range(w.B):
+            if gap[b] >= M.TOPK_TIE:
+                assert set(o_ids[b].tolist()) == set(g[b].tolist()), f"hop {h} row {b}"
+            else:
+                print(f"hop {h} row {b}: near-tie ({gap[b]:.2e}); free-running paths may part")
+        qr = O.interleave_project(ref, M.np64(c["wp"]))
+
+
+def test_interleave_hop1_equals_single_step(msa):
+    """Hop 1 of a multi-hop step is exactly the single-hop step."""
+    c = interleave_case(msa, "c5_small")
+    w = c["w"]
+    args = (c["q"], w.q_pos, w.k, c["k_loc"], c["v_loc"], c["L"])
+    ids3, sc3, out3, _ = c["bank"].step(*args, q_route=c["q_route"], hops=w.hops, w_proj=c["wp"])
+    ids1, sc1, out1, _ = c["bank"].step(*args, q_route=c["q_route"])
+    torch.cuda.synchronize()
+    assert torch.equal(ids3[0], ids1[0]) and torch.equal(out3[0], out1[0])
