@@ -30,6 +30,43 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def _sources_sha256(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(name):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter
+    record profiles/<name>.json (FETCH_SIZE and WRITE_SIZE per dispatch, each
+    scaled by the same counter's reading on a plain copy of known size), or
+    None when there is no record or the kernel's sources changed since the
+    counters were taken."""
+    path = os.path.join(ROOT, "profiles", name + ".json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if _sources_sha256(rec["sources"]) != rec["sources_sha256"]:
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
+def calibrate_copy(n_bytes=1 << 30, reps=10):
+    """A plain device copy of known size (reads and writes n_bytes each), run
+    under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE to scale those counters."""
+    import torch
+    src = torch.ones(n_bytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n_bytes, "copy_bytes_written": n_bytes, "reps": reps}))
+
+
 def cpu_baseline(w, r_dev, k_raw_dev, v_raw_dev, batch_inputs, budget_s=12.0):
     """The fp64 oracle on one 16-query decode step of the same bank.  Bank
     build (pooling, document RoPE) and the local context's RoPE are set-up,
@@ -153,6 +190,7 @@ def prefill_bench(steps, warmup, splits=0):
             "attention": {"bound": "mfma", "achieved": flops / att_s / 1e12,
                           "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                           "frac": flops / att_s / 1e12 / MFMA_PEAK_TFLOPS,
+                          "traffic": measured_traffic("prefill_c3_counters"),
                           "flops_per_launch": flops, "avg_launch_us": att_s * 1e6,
                           "hbm_GBs": kv_bytes / att_s / 1e9}}
 
@@ -168,10 +206,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=20, help="0 skips the prefill leg")
     ap.add_argument("--prefill-splits", type=int, default=0, help="token splits (0: automatic)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported here "
-              "(the path shards by document range across GPUs; see DESIGN.md)", file=sys.stderr)
+              "(the path would shard by document range across GPUs)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -246,7 +289,7 @@ def main():
                    "rotating_batches": args.batches},
         "roofline": {"kernel": "decode attention (split-K)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic("decode_c2_counters"),
                      "bytes_per_launch": kv_bytes, "avg_launch_us": att_avg_us,
                      "launches": att_n},
         "tokens_attended_per_s": qps * (w.k * 512 + w.L_loc),
