@@ -20,8 +20,11 @@
  * Conventions for every call
  *   - Every pointer is caller-owned.  "device" pointers are HIP device
  *     memory on the current device; "host" pointers are ordinary CPU memory.
- *     The library allocates only in msa_bank_create (small per-bank tables)
- *     and frees them in msa_bank_destroy.  No hot-path call allocates.
+ *     The library allocates only in msa_bank_create (small per-bank tables;
+ *     for a host-resident bank also pinned id buffers for 4096 selections and
+ *     two events) and frees them in msa_bank_destroy.  The one exception on
+ *     the hot path: msa_step on a host-resident bank regrows those pinned id
+ *     buffers once when a call selects more documents than they hold.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Calls are asynchronous on that stream unless stated; results are valid
  *     once the stream has completed the work.
@@ -37,7 +40,10 @@
  *     outputs are always float32.  Arithmetic accumulates in float32 (the
  *     routing-key pooling and norms in float64).
  *   - A bank handle is immutable after msa_bank_create; calls on one bank may
- *     run concurrently on different streams if their workspaces differ.
+ *     run concurrently on different streams if their workspaces (and staging
+ *     buffers) differ.  On a host-resident bank the host part of msa_step
+ *     (id readback, copy issue) runs one call at a time under a lock held in
+ *     the bank.
  *
  * Layouts (row-major; the last index is contiguous)
  *   Routing keys      kr       [h_r][C][d_r]        (C = total chunks)

@@ -132,6 +132,27 @@ int check_attend_common(const Bank& bk, int mode, int n_q, int h_q, int k, int b
 }
 
 }  // namespace
+
+hipError_t host_buffers_reserve(Bank& bk, size_t cap) {
+  if (bk.h_ids_cap >= cap) return hipSuccess;
+  if (bk.h_ids) (void)hipHostFree(bk.h_ids);
+  if (bk.h_src) (void)hipHostFree(bk.h_src);
+  if (bk.h_src_off) (void)hipHostFree(bk.h_src_off);
+  bk.h_ids = nullptr;
+  bk.h_src = nullptr;
+  bk.h_src_off = nullptr;
+  bk.h_ids_cap = 0;
+  hipError_t e = hipHostMalloc((void**)&bk.h_ids, cap * 4, 0);
+  if (e == hipSuccess) e = hipHostMalloc((void**)&bk.h_src, cap * 8, 0);
+  if (e == hipSuccess) e = hipHostMalloc((void**)&bk.h_src_off, cap * 8, 0);
+  if (e == hipSuccess) bk.h_ids_cap = cap;
+  return e;
+}
+
+// initial capacity of a host-resident bank's pinned id buffers (selections
+// per msa_step); a larger step regrows them once
+constexpr size_t kHostIdsInitial = 4096;
+
 }  // namespace msa
 
 using namespace msa;
@@ -299,6 +320,15 @@ int msa_bank_create(const msa_bank_desc* d, msa_bank** out) {
     delete bk;
     return fail(MSA_EHIP, std::string("uploading bank tables: ") + hipGetErrorString(e));
   }
+  if (d->kv_loc == MSA_KV_HOST) {
+    e = host_buffers_reserve(*bk, kHostIdsInitial);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&bk->copies_done, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&bk->tables_done, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      msa_bank_destroy(reinterpret_cast<msa_bank*>(bk));
+      return fail(MSA_EHIP, std::string("host-bank buffers: ") + hipGetErrorString(e));
+    }
+  }
   *out = reinterpret_cast<msa_bank*>(bk);
   return MSA_OK;
 }
@@ -306,6 +336,9 @@ int msa_bank_create(const msa_bank_desc* d, msa_bank** out) {
 int msa_bank_destroy(msa_bank* b) {
   if (!b) return MSA_OK;
   Bank* bk = reinterpret_cast<Bank*>(b);
+  if (bk->tables_pending) (void)hipEventSynchronize(bk->tables_done);
+  if (bk->copies_done) (void)hipEventDestroy(bk->copies_done);
+  if (bk->tables_done) (void)hipEventDestroy(bk->tables_done);
   if (bk->dev_mem) (void)hipFree(bk->dev_mem);
   if (bk->h_ids) (void)hipHostFree(bk->h_ids);
   if (bk->h_src) (void)hipHostFree(bk->h_src);
@@ -461,21 +494,19 @@ int msa_step(const msa_bank* b, const msa_step_args* a, void* stream, void* copy
     if (!a->staging) return fail(MSA_EINVAL, "host-resident bank needs a staging buffer");
     if (a->staging_bytes < msa_staging_bytes(b, n_groups, k))
       return fail(MSA_ENOMEM, "staging buffer too small");
-    const size_t cap = (size_t)n_groups * k;
-    if (bk.h_ids_cap < cap) {
-      if (bk.h_ids) (void)hipHostFree(bk.h_ids);
-      if (bk.h_src) (void)hipHostFree(bk.h_src);
-      if (bk.h_src_off) (void)hipHostFree(bk.h_src_off);
-      bk.h_ids = nullptr;
-      bk.h_src = nullptr;
-      bk.h_src_off = nullptr;
-      bk.h_ids_cap = 0;
-      if (hipHostMalloc((void**)&bk.h_ids, cap * 4, 0) != hipSuccess ||
-          hipHostMalloc((void**)&bk.h_src, cap * 8, 0) != hipSuccess ||
-          hipHostMalloc((void**)&bk.h_src_off, cap * 8, 0) != hipSuccess)
-        return fail(MSA_ENOMEM, "pinned id buffers");
-      bk.h_ids_cap = cap;
+  }
+  // The host part of a host-resident bank's step (id readback, copy issue,
+  // remap tables) uses the bank's pinned buffers: one step at a time.
+  std::unique_lock<std::mutex> host_lock;
+  if (host) {
+    host_lock = std::unique_lock<std::mutex>(bk.host_mu);
+    // the previous step's remap tables must have left the pinned buffers
+    if (bk.tables_pending) {
+      MSA_CHECK_HIP(hipEventSynchronize(bk.tables_done));
+      bk.tables_pending = false;
     }
+    if (host_buffers_reserve(bk, (size_t)n_groups * k) != hipSuccess)
+      return fail(MSA_ENOMEM, "pinned id buffers");
   }
   char* w = (char*)a->ws;
   hipStream_t s = (hipStream_t)stream;
@@ -557,12 +588,11 @@ int msa_step(const msa_bank* b, const msa_step_args* a, void* stream, void* copy
         MSA_CHECK_HIP(hipMemcpyAsync(d_off, slot_off, (size_t)n_slots * 8, hipMemcpyHostToDevice, s));
         MSA_CHECK_HIP(hipMemcpyAsync(d_len, slot_len, (size_t)n_slots * 4, hipMemcpyHostToDevice, s));
       }
+      MSA_CHECK_HIP(hipEventRecord(bk.tables_done, s));
+      bk.tables_pending = true;
       if (cs != s) {
-        hipEvent_t ev;
-        MSA_CHECK_HIP(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
-        MSA_CHECK_HIP(hipEventRecord(ev, cs));
-        MSA_CHECK_HIP(hipStreamWaitEvent(s, ev, 0));
-        MSA_CHECK_HIP(hipEventDestroy(ev));
+        MSA_CHECK_HIP(hipEventRecord(bk.copies_done, cs));
+        MSA_CHECK_HIP(hipStreamWaitEvent(s, bk.copies_done, 0));
       }
       src = AttnSources{stg, stg + half, d_off, d_len, n_slots};
       att_ids = d_ids;

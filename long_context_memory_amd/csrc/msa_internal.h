@@ -7,6 +7,7 @@
 #include <stddef.h>
 
 #include <string>
+#include <mutex>
 #include <vector>
 
 #include "../../include/msa.h"
@@ -35,12 +36,22 @@ struct Bank {
   int32_t* d_tile_piece0 = nullptr;  // [n_tiles + 1]
   int32_t* d_doc_piece0 = nullptr;   // [N + 1]
   double* d_inv_freq = nullptr;      // [64]
-  // pinned host buffer for reading back selected ids (host-resident banks)
+  // host-resident banks: pinned buffers for reading back selected ids and
+  // staging the remap tables, and the events that order the copies.  The
+  // host part of msa_step holds host_mu while it uses them.
   int32_t* h_ids = nullptr;
   size_t h_ids_cap = 0;
   int32_t* h_src = nullptr;  // pinned [2 * cap] remap table staging
   int64_t* h_src_off = nullptr;
+  hipEvent_t copies_done = nullptr;  // document copies on the copy stream
+  hipEvent_t tables_done = nullptr;  // remap tables read out of h_src / h_src_off
+  bool tables_pending = false;
+  std::mutex host_mu;
 };
+
+// (Re)allocate a host-resident bank's pinned id/table buffers for `cap`
+// selections.  Called with host_mu held (or before the bank is published).
+hipError_t host_buffers_reserve(Bank& bk, size_t cap);
 
 // thread-local last error message
 void set_error(const std::string& msg);

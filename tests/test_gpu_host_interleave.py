@@ -119,6 +119,39 @@ def test_host_bank_copy_stream(msa):
     assert torch.equal(out, ref)
 
 
+def test_host_bank_concurrent_steps(msa):
+    """Two threads stepping one host-resident bank on their own streams,
+    workspaces and staging buffers: every result equals the serial one."""
+    import threading
+    c = host_case(msa, "c4_small")
+    w, bank = c["w"], c["bank"]
+    args = (c["q"], w.q_pos, w.k, c["k_loc"], c["v_loc"], c["L"])
+    _, _, ref, _ = bank.step(*args, q_route=c["q_route"])
+    torch.cuda.synchronize()
+    results, errors = [[], []], []
+
+    def run(t):
+        try:
+            st = torch.cuda.Stream()
+            ws = bank.workspace(msa.MSA_DECODE, w.B, w.h_q, w.k)
+            stg = bank.staging(w.B, w.k)
+            for _ in range(4):
+                _, _, out, _ = bank.step(*args, q_route=c["q_route"], ws=ws, staging=stg, stream=st)
+                st.synchronize()
+                results[t].append(out.clone())
+        except Exception as e:  # reported below
+            errors.append(e)
+
+    th = [threading.Thread(target=run, args=(t,)) for t in range(2)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    assert not errors, errors
+    for r in results:
+        assert len(r) == 4 and all(torch.equal(o, ref) for o in r)
+
+
 # --------------------------------------------------------------------------
 # interleaved multi-hop retrieval
 # --------------------------------------------------------------------------
