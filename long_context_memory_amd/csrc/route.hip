@@ -5,14 +5,10 @@
 // router queries of the blocked prefill and the Memory Interleave projection
 // that forms the next hop's router query.
 //
-// route_scan: one wave per (router head, tile of 64 chunks).  The wave stages
-// its 64 key rows (16 KiB of bf16, coalesced 1 KiB loads) through LDS, each
-// lane takes one row into registers (float32), and dots it with every query
-// of the batch (query values are wave-uniform, so they arrive as scalar
-// loads).  Cosines go back through LDS transposed, and lane b folds its
-// query's cosines into per-document maxima over the tile's chunks: one
-// "piece" per (document, tile) it overlaps.  top-k later takes the max over a
-// document's pieces, so no atomics and no initialisation are needed.
+// route_scan produces, per (query, router head), the maximum cosine of every
+// "piece" -- a run of one document's chunks inside a tile of 64 chunks.
+// top-k later takes the max over a document's pieces and the mean over
+// heads, so no atomics and no initialisation are needed.
 #include <algorithm>
 
 #include "msa_internal.h"
