@@ -152,3 +152,49 @@ def seeded_subset(n, m, seed):
 
 def math_isclose(a, b, tol):
     return math.isclose(a, b, abs_tol=tol)
+
+
+def pool_oracle_sliced(w, rows, slice_docs=64):
+    """Like pool_oracle, with the routing vectors of documents [n0, n1)
+    produced on demand by rows(t0, t1) (so 8M+ token banks need not be held
+    in memory at once)."""
+    off = S.doc_token_offsets(w)
+    keys = []
+    for n0 in range(0, w.n_docs, slice_docs):
+        n1 = min(w.n_docs, n0 + slice_docs)
+        rs = np64(rows(int(off[n0]), int(off[n1])))
+        keys.append(O.chunk_mean_pool(rs, w.doc_len[n0:n1]))
+        del rs
+    kr = O.round_to_storage(np.concatenate(keys), w.dtype)
+    return kr, O.inverse_norms(kr)
+
+
+def doc_kv_from_rows(w, rows, n):
+    """Oracle K (document-RoPE'd, rounded) and V of document n, the raw rows
+    produced on demand by rows(t0, t1) -> (k_raw, v_raw)."""
+    off = S.doc_token_offsets(w)
+    a, b = int(off[n]), int(off[n + 1])
+    k_raw, v_raw = rows(a, b)
+    return (O.bank_keys_rotated(np64(k_raw), [b - a], w.rope_base, w.dtype), np64(v_raw))
+
+
+def oracle_prefill_rows(w, q, lk, lv, doc_kv, sel, blk, queries):
+    """Oracle prefill outputs of the given queries (indices inside block
+    blk) attending to the documents `sel` (ids; doc_kv[id] = (K_rot, V)) and
+    the causal local context.  q: [B, h_q, d] raw; lk, lv: [L_loc, h_kv, d]."""
+    L, Lq, bsz = w.L_loc, w.B, w.block
+    lkr = O.round_to_storage(O.rope_rotate(lk, (w.P0 + np.arange(L))[:, None], w.rope_base),
+                             w.dtype)
+    K = np.concatenate([doc_kv[n][0] for n in sel] + [lkr])
+    V = np.concatenate([doc_kv[n][1] for n in sel] + [lv])
+    n_doc = K.shape[0] - L
+    outs = []
+    for i in queries:
+        qi = blk * bsz + i
+        li = L - Lq + qi
+        mask = np.ones((1, K.shape[0]), dtype=bool)
+        mask[0, n_doc:] = np.arange(L) <= li
+        qr = O.rope_rotate(q[qi][None], np.full((1, w.h_q), w.P0 + li), w.rope_base)
+        outs.append(O.gqa_attention(qr, K, V, mask)[0])
+    return np.stack(outs)
+

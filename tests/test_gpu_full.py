@@ -1,0 +1,150 @@
+"""GPU parity at the full workload sizes, on sampled outputs the fp64 oracle
+computes one by one:
+
+- the 8M-token blocked prefill, in the launch configuration the benchmark
+  times (automatic splits);
+- the 100M-token host-resident bank (slot-backed pinned store);
+- three interleaved hops over a 32 Mi-token bank of lognormal documents.
+
+For each, routing (top-k and scores) is checked for every query or block, and
+attention outputs for a seeded sample of queries.  Banks are built, and the
+oracle's routing keys pooled, slice by slice.
+"""
+import numpy as np
+import pytest
+import torch
+
+from long_context_memory_amd import synth as S
+from oracle import msa_oracle as O
+import msa_cases as M
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def msa():
+    from long_context_memory_amd import msa as m
+    return m
+
+
+def build_sliced(msa, w, docs_per_slice):
+    bank = msa.Bank(w.doc_len, w.h_r, w.h_kv, w.dtype, DEV, rope_base=w.rope_base)
+    off = S.doc_token_offsets(w)
+    for n0 in range(0, w.n_docs, docs_per_slice):
+        n1 = min(w.n_docs, n0 + docs_per_slice)
+        a, b = int(off[n0]), int(off[n1])
+        r = S.route_vectors(w, DEV, a, b)
+        k_raw, v_raw = S.kv_raw(w, DEV, a, b)
+        bank.build(n0, n1, r, k_raw, v_raw)
+        torch.cuda.synchronize()
+        del r, k_raw, v_raw
+    return bank
+
+
+def pick(ids_gpu_row, oracle_scores_row, k):
+    """The oracle's selection, or the GPU's when it is a valid alternative
+    inside a near-tie (check_topk has already accepted it)."""
+    o_ids, _ = O.select_topk(oracle_scores_row[None], k)
+    o = o_ids[0]
+    return o if set(o.tolist()) == set(ids_gpu_row.tolist()) else ids_gpu_row
+
+
+def test_prefill_full_sampled(msa):
+    w = S.workload("c3")
+    bank = build_sliced(msa, w, 512)
+    q = S.queries(w, DEV)
+    rt = S.prefill_route_tokens(w, DEV)
+    lk, lv = S.local_raw(w, DEV)
+    k_loc, v_loc, L = bank.prepare_local(lk[None], lv[None], w.P0)
+    q_pos = w.P0 + (w.L_loc - w.B)
+    ids, scores, out, _ = bank.step(q, q_pos, w.k, k_loc, v_loc, L, route_tokens=rt,
+                                    mode=msa.MSA_PREFILL, block=w.block)
+    torch.cuda.synchronize()
+    ids_np, sc_np, out_np = ids[0].cpu().numpy(), scores[0].cpu().numpy(), out[0].cpu().numpy()
+    del out
+    kr_o, inv_o = M.pool_oracle_sliced(w, lambda a, b: S.route_vectors(w, DEV, a, b), 64)
+    so = O.cosine_doc_scores(O.block_mean_queries(M.np64(rt), w.block), kr_o, inv_o, w.doc_len)
+    near = M.check_topk(ids_np, sc_np, so, w.k)
+    print(f"prefill routing: {so.shape[0]} blocks, {near} near-tie")
+    q64, lk64, lv64 = M.np64(q), M.np64(lk), M.np64(lv)
+    rows = lambda a, b: S.kv_raw(w, DEV, a, b)  # noqa: E731
+    for blk in (0, 17, 31):
+        sel = pick(ids_np[blk], so[blk], w.k)
+        doc_kv = {n: M.doc_kv_from_rows(w, rows, n) for n in sel}
+        qs = M.seeded_subset(w.block, 4, 100 + blk)
+        ref = M.oracle_prefill_rows(w, q64, lk64, lv64, doc_kv, sel, blk, qs)
+        got = out_np[blk * w.block + qs]
+        mx, rel = M.check_out(got, ref, w.dtype, f"prefill block {blk}")
+        print(f"prefill block {blk} queries {qs.tolist()}: max abs {mx:.3e} rel rms {rel:.3e}")
+
+
+def test_host_bank_full_sampled(msa):
+    w = S.workload("c4")
+    slot_len, kv_off = S.host_slot_layout(w)
+    kr = S.keys_direct(w, DEV).to(w.torch_dtype)
+    bank = msa.Bank(w.doc_len, w.h_r, w.h_kv, w.dtype, DEV, kv_loc="host", kv_off=kv_off,
+                    kv_tokens=int(sum(slot_len)), rope_base=w.rope_base,
+                    kr=kr.permute(1, 0, 2).contiguous())
+    bank.build(0, w.n_docs)
+    msa.fill_host_store(bank, slot_len, lambda t0, t1: S.host_kv_raw(w, DEV, t0, t1),
+                        slots_per_pass=32)
+    q = S.queries(w, DEV)
+    q_route = S.route_queries(w, DEV)
+    lk, lv = S.local_raw(w, DEV)
+    k_loc, v_loc, L = bank.prepare_local(lk, lv, w.P0)
+    ids, scores, out, st = bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=q_route)
+    torch.cuda.synchronize()
+    ids_np, sc_np, out_np = ids[0].cpu().numpy(), scores[0].cpu().numpy(), out[0].cpu().numpy()
+    kr_o = M.np64(kr)
+    del kr
+    so = O.cosine_doc_scores(M.np64(q_route), kr_o, O.inverse_norms(kr_o), w.doc_len)
+    near = M.check_topk(ids_np, sc_np, so, w.k)
+    print(f"host bank routing: {w.B} queries over {w.n_docs} documents, {near} near-tie")
+    distinct = sorted(set(ids_np.ravel().tolist()))
+    assert st.docs_copied == len(distinct)
+    assert st.bytes_copied == sum(2 * w.doc_len[n] * w.h_kv * 128 * 2 for n in distinct)
+    q64, lk64, lv64 = M.np64(q), M.np64(lk), M.np64(lv)
+    for b in M.seeded_subset(w.B, 2, 41):
+        sel = pick(ids_np[b], so[b], w.k)
+        doc_kv = {}
+        for n in sel:
+            t0, Ln = int(kv_off[n]), int(w.doc_len[n])
+            k_raw, v_raw = S.host_kv_raw(w, DEV, t0, t0 + Ln)
+            doc_kv[n] = (O.bank_keys_rotated(M.np64(k_raw), [Ln], w.rope_base, w.dtype),
+                         M.np64(v_raw))
+        ref = M.oracle_attend_decode(w, q64[b], w.q_pos, sel, doc_kv, lk64[b], lv64[b], w.P0)
+        mx, rel = M.check_out(out_np[b][None], ref[None], w.dtype, f"host bank query {b}")
+        print(f"host bank query {b}: max abs {mx:.3e} rel rms {rel:.3e}")
+
+
+def test_interleave_full_sampled(msa):
+    w = S.workload("c5")
+    bank = build_sliced(msa, w, 256)
+    q = S.queries(w, DEV)
+    q_route = S.route_queries(w, DEV)
+    lk, lv = S.local_raw(w, DEV)
+    k_loc, v_loc, L = bank.prepare_local(lk, lv, w.P0)
+    wp = S.interleave_projection(w, DEV)
+    ids, scores, out, _ = bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=q_route,
+                                    hops=w.hops, w_proj=wp)
+    torch.cuda.synchronize()
+    ids_np, sc_np, out_np = ids.cpu().numpy(), scores.cpu().numpy(), out.cpu().numpy()
+    kr_o, inv_o = M.pool_oracle_sliced(w, lambda a, b: S.route_vectors(w, DEV, a, b), 256)
+    q64, lk64, lv64, wp64 = M.np64(q), M.np64(lk), M.np64(lv), M.np64(wp)
+    rows = lambda a, b: S.kv_raw(w, DEV, a, b)  # noqa: E731
+    cache = {}
+    sample = M.seeded_subset(w.B, 2, 55)
+    for h in range(w.hops):
+        qr = M.np64(q_route) if h == 0 else O.interleave_project(out_np[h - 1], wp64)
+        so = O.cosine_doc_scores(qr, kr_o, inv_o, w.doc_len)
+        near = M.check_topk(ids_np[h], sc_np[h], so, w.k)
+        for b in sample:
+            sel = pick(ids_np[h][b], so[b], w.k)
+            for n in sel:
+                if n not in cache:
+                    cache[n] = M.doc_kv_from_rows(w, rows, n)
+            ref = M.oracle_attend_decode(w, q64[b], w.q_pos, sel, cache, lk64[b], lv64[b], w.P0)
+            mx, rel = M.check_out(out_np[h][b][None], ref[None], w.dtype, f"hop {h} query {b}")
+            print(f"hop {h} query {b}: max abs {mx:.3e} rel rms {rel:.3e}")
+        print(f"hop {h}: {w.B} queries routed, {near} near-tie")
