@@ -28,6 +28,10 @@ FLAGS = [
 ]
 
 
+# Per-file extra hipcc flags (none at present).
+FILE_FLAGS = {}
+
+
 def _hipcc():
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", "hipcc"):
         if c and (os.path.isabs(c) and os.path.exists(c) or not os.path.isabs(c)):
@@ -51,7 +55,7 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-        out = _run([hipcc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        out = _run([hipcc, *FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
         return obj, out
 
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:

@@ -203,8 +203,13 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillP p) {
   // Stage a tile: wave w's load i fills 1 KB j = w + 8*i of the K tile (LDS
   // rows 4j..4j+3, 16-byte chunk c of row r at slot c ^ (r & 15)) and 1 KB j
   // of the V^T tile (channel rows 8j..8j+7, chunk cv of row d at slot
-  // cv ^ (d & 7)).  K rows past the tile's valid tokens repeat its last
-  // valid row (their scores are masked); V^T tiles are zero-padded in memory.
+  // cv ^ ((d >> 1) & 7)).  The LDS has 64 four-byte banks and serves a
+  // 16-byte-per-lane read 16 lanes at a time: K rows are 256 bytes, so 16
+  // consecutive rows must use 16 different slots; V^T rows are 128 bytes, so
+  // rows d and d + 1 already sit in different halves of the banks and the
+  // slot must differ across rows of equal parity.  K rows past the tile's
+  // valid tokens repeat its last valid row (their scores are masked); V^T
+  // tiles are zero-padded in memory.
   auto issue = [&](const Tile& t, uint8_t* base) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -218,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillP p) {
     for (int i = 0; i < 2; ++i) {
       const int j = wave + kWaves * i;
       const int d = 8 * j + (lane >> 3);
-      const int cv = (lane & 7) ^ (d & 7);
+      const int cv = (lane & 7) ^ ((d >> 1) & 7);
       dma16(t.vb + d * 64 + 8 * cv, base + kTileB + 1024 * j);
     }
   };
@@ -239,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillP p) {
   auto vfrag = [&](const uint8_t* sv, int ks, int dt) __attribute__((always_inline)) {
     const int d = 32 * dt + l32, cv = 2 * ks + hl;
     return __builtin_bit_cast(
-        bf16x8_t, *reinterpret_cast<const uint4*>(&sv[d * 128 + ((cv ^ (d & 7)) << 4)]));
+        bf16x8_t, *reinterpret_cast<const uint4*>(&sv[d * 128 + ((cv ^ ((d >> 1) & 7)) << 4)]));
   };
   auto ref_of = [](float m) { return m == -INFINITY ? 0.f : m; };
 
