@@ -195,6 +195,133 @@ def prefill_bench(steps, warmup, splits=0):
                           "hbm_GBs": kv_bytes / att_s / 1e9}}
 
 
+def host_bank_bench(steps, warmup):
+    """The 100M-token host-resident bank (12,207 x 8192 + one 256-token
+    document; routing keys in HBM, K/V in pinned host memory backed by 384
+    document slots): 8-query decode steps, each copying its selected
+    documents' K/V to the GPU.  Reports queries/s, the host-to-device rate
+    of those copies and, for reference, a plain pinned 1 GiB copy."""
+    import torch
+    from long_context_memory_amd import msa, synth as S
+
+    dev = "cuda"
+    w = S.workload("c4")
+    log(f"host bank: {w.n_docs} docs, {w.T} tokens, {w.host_slots} slots")
+    slot_len, kv_off = S.host_slot_layout(w)
+    kr = S.keys_direct(w, dev).to(w.torch_dtype).permute(1, 0, 2).contiguous()
+    bank = msa.Bank(w.doc_len, w.h_r, w.h_kv, w.dtype, dev, kv_loc="host", kv_off=kv_off,
+                    kv_tokens=int(sum(slot_len)), rope_base=w.rope_base, kr=kr)
+    bank.build(0, w.n_docs)
+    msa.fill_host_store(bank, slot_len, lambda t0, t1: S.host_kv_raw(w, dev, t0, t1),
+                        slots_per_pass=32)
+    batches = []
+    for i in range(2):
+        q = S.queries(w, dev, batch=i)
+        q_route = S.route_queries(w, dev, batch=i)
+        lk, lv = S.local_raw(w, dev, batch=i)
+        k_loc, v_loc, L = bank.prepare_local(lk, lv, w.P0)
+        batches.append((q, q_route, k_loc, v_loc, L))
+    ws = bank.workspace(msa.MSA_DECODE, w.B, w.h_q, w.k)
+    stg = bank.staging(w.B, w.k)
+    cs = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    copied = [0, 0]
+
+    def step(i, count):
+        q, q_route, k_loc, v_loc, L = batches[i % len(batches)]
+        _, _, _, st = bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=q_route, ws=ws,
+                                staging=stg, copy_stream=cs)
+        if count:
+            copied[0] += st.bytes_copied
+            copied[1] += st.docs_copied
+
+    for i in range(warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    # a plain pinned host -> device copy of 1 GiB, for the link's own rate
+    hsrc = torch.empty(1 << 28, dtype=torch.float32, pin_memory=True)
+    ddst = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    ddst.copy_(hsrc, non_blocking=True)
+    torch.cuda.synchronize()
+    tc = time.perf_counter()
+    for _ in range(5):
+        ddst.copy_(hsrc, non_blocking=True)
+    torch.cuda.synchronize()
+    link = 5 * (1 << 30) / (time.perf_counter() - tc) / 1e9
+    return {"workload": "100M-token host-resident bank: 12,207 docs x 8192 + one 256-token doc "
+                        "(390,625 chunks, bf16 keys in HBM), K/V in pinned host memory (384 "
+                        "document slots), B=8, top-16, local 4096",
+            "queries_per_s": w.B * steps / dt, "ms_per_step": dt * 1e3 / steps, "steps": steps,
+            "h2d_GBs": copied[0] / dt / 1e9, "docs_copied_per_step": copied[1] / steps,
+            "bytes_copied_per_step": copied[0] / steps, "pinned_copy_GBs": link,
+            "h2d_frac_of_pinned_copy": copied[0] / dt / 1e9 / link}
+
+
+def interleave_bench(steps, warmup):
+    """Three Memory Interleave hops over a 32 Mi-token bank of lognormal
+    documents (K/V resident in HBM), 64 queries, top-8 per hop.  Reports
+    queries/s per 3-hop step and the attention launches' HBM rate from the
+    bytes of the documents actually selected."""
+    import numpy as np
+    import torch
+    from long_context_memory_amd import msa, synth as S
+
+    dev = "cuda"
+    w = S.workload("c5")
+    log(f"interleave: building {w.n_docs} docs, {w.T} tokens")
+    bank = msa.Bank(w.doc_len, w.h_r, w.h_kv, w.dtype, dev, rope_base=w.rope_base)
+    off = S.doc_token_offsets(w)
+    for n0 in range(0, w.n_docs, 256):
+        n1 = min(w.n_docs, n0 + 256)
+        a, b = int(off[n0]), int(off[n1])
+        bank.build(n0, n1, S.route_vectors(w, dev, a, b), *S.kv_raw(w, dev, a, b))
+        torch.cuda.synchronize()
+    q = S.queries(w, dev)
+    q_route = S.route_queries(w, dev)
+    lk, lv = S.local_raw(w, dev)
+    k_loc, v_loc, L = bank.prepare_local(lk, lv, w.P0)
+    wp = S.interleave_projection(w, dev)
+    ws = bank.workspace(msa.MSA_DECODE, w.B, w.h_q, w.k, hops=w.hops)
+    outs = (torch.empty((w.hops, w.B, w.k), dtype=torch.int32, device=dev),
+            torch.empty((w.hops, w.B, w.k), dtype=torch.float32, device=dev),
+            torch.empty((w.hops, w.B, w.h_q, 128), dtype=torch.float32, device=dev))
+
+    def step():
+        bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=q_route, hops=w.hops, w_proj=wp,
+                  ws=ws, outputs=outs)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    msa.timer_enable(True)
+    msa.timer_read(msa.MSA_TIMER_ATTENTION)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    att_ms, att_n = msa.timer_read(msa.MSA_TIMER_ATTENTION)
+    msa.timer_enable(False)
+    ids = outs[0].cpu().numpy()
+    lens = np.asarray(w.doc_len, dtype=np.int64)
+    tok = int(lens[ids].sum()) + w.hops * w.B * w.L_loc  # union tokens over the 3 hops
+    att_bytes = tok * w.h_kv * 128 * 2 * 2
+    att_s = att_ms * 1e-3 / max(att_n, 1) * w.hops
+    return {"workload": "Memory Interleave x3 over a 32 Mi-token bank (lognormal document "
+                        "lengths, median 4096, 1024..65536), B=64, top-8 per hop, h_r=1, "
+                        "local 4096",
+            "queries_per_s": w.B * steps / dt, "ms_per_step": dt * 1e3 / steps, "steps": steps,
+            "attention": {"bound": "hbm", "bytes_per_step": att_bytes,
+                          "avg_launch_us": att_s / w.hops * 1e6,
+                          "achieved": att_bytes / att_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": att_bytes / att_s / 1e9 / HBM_PEAK_GBS}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -206,6 +333,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=20, help="0 skips the prefill leg")
     ap.add_argument("--prefill-splits", type=int, default=0, help="token splits (0: automatic)")
+    ap.add_argument("--c4-steps", type=int, default=0,
+                    help="also run the 100M-token host-bank leg (0 skips it)")
+    ap.add_argument("--c5-steps", type=int, default=0,
+                    help="also run the 3-hop interleave leg over 32 Mi tokens (0 skips it)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -302,6 +433,12 @@ def main():
         del bank, batches, ws, outs, r, k_raw, v_raw, raw0
         torch.cuda.empty_cache()
         res["prefill"] = prefill_bench(args.prefill_steps, 3, args.prefill_splits)
+    if args.c4_steps > 0:
+        torch.cuda.empty_cache()
+        res["host_bank"] = host_bank_bench(args.c4_steps, 2)
+    if args.c5_steps > 0:
+        torch.cuda.empty_cache()
+        res["interleave"] = interleave_bench(args.c5_steps, 2)
     print(json.dumps(res))
 
 
