@@ -22,6 +22,7 @@
 //   - the "gather" is an indirection: per (query, head) the workgroup reads
 //     the k selected ids and the document table and walks the tiles in place.
 #include <algorithm>
+#include <cmath>
 
 #include "msa_internal.h"
 
@@ -394,13 +395,18 @@ size_t decode_partial_floats(int B, int h_kv, int G, int splits) {
 }
 
 int decode_auto_splits(const Bank& bk, int B, int k, int L_loc) {
-  // About one long-running wave per SIMD (1024 waves on 256 CUs) streams
-  // best: each wave walks a long contiguous run of tiles.  Splits come in
-  // multiples of 4 (one workgroup = 4 waves) and never exceed the tiles.
+  // At least one long-running wave per SIMD (1024 waves on 256 CUs): each
+  // wave walks a long contiguous run of tiles, which streams best when the
+  // unions are of equal length.  With documents of mixed lengths the unions
+  // differ from query to query, and a wave per about 32 tiles of the
+  // expected union lets short unions' waves finish and make room for the
+  // rest of the long ones.  Splits come in multiples of 4 (one workgroup =
+  // 4 waves) and never exceed the tiles.
   const double avg_doc = (double)bk.n_tokens / bk.desc.n_docs;
   const double tiles = k * avg_doc / kAttnTile + (L_loc + kAttnTile - 1) / kAttnTile;
   const int64_t pairs = std::max<int64_t>(1, (int64_t)B * bk.desc.h_kv);
   int s = (int)((1024 + pairs - 1) / pairs);
+  s = std::max(s, (int)std::ceil(tiles / 32.0));
   s = (int)std::min<double>(s, std::max(4.0, tiles));
   s = std::max(4, ((s + 3) / 4) * 4);
   return std::min(s, 256);

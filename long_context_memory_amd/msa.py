@@ -184,7 +184,7 @@ class Bank:
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h is not None and h.value:
+        if h is not None and h.value and lib is not None:  # lib is None at interpreter exit
             lib.msa_bank_destroy(h)
             self.handle = None
 
