@@ -195,7 +195,7 @@ def prefill_bench(steps, warmup, splits=0):
                           "hbm_GBs": kv_bytes / att_s / 1e9}}
 
 
-def host_bank_bench(steps, warmup):
+def host_bank_bench(steps, warmup, cache_gb=0.0):
     """The 100M-token host-resident bank (12,207 x 8192 + one 256-token
     document; routing keys in HBM, K/V in pinned host memory backed by 384
     document slots): 8-query decode steps, each copying its selected
@@ -214,35 +214,44 @@ def host_bank_bench(steps, warmup):
     bank.build(0, w.n_docs)
     msa.fill_host_store(bank, slot_len, lambda t0, t1: S.host_kv_raw(w, dev, t0, t1),
                         slots_per_pass=32)
-    batches = []
-    for i in range(2):
-        q = S.queries(w, dev, batch=i)
-        q_route = S.route_queries(w, dev, batch=i)
-        lk, lv = S.local_raw(w, dev, batch=i)
-        k_loc, v_loc, L = bank.prepare_local(lk, lv, w.P0)
-        batches.append((q, q_route, k_loc, v_loc, L))
+    q = S.queries(w, dev)
+    lk, lv = S.local_raw(w, dev)
+    k_loc, v_loc, L = bank.prepare_local(lk, lv, w.P0)
     ws = bank.workspace(msa.MSA_DECODE, w.B, w.h_q, w.k)
-    stg = bank.staging(w.B, w.k)
+    stg = None
+    slots = 0
+    if cache_gb > 0:
+        # device document cache: each step routes fresh queries, so hits
+        # come from the cache holding a share of the bank, not from repeats
+        slot = bank.cache_slot_bytes()
+        slots = int(cache_gb * 1e9) // slot
+        bank.set_cache(torch.empty(slots * slot, dtype=torch.uint8, device=dev))
+        warmup = max(warmup, -(-slots // (w.B * w.k)) + 4)
+    else:
+        stg = bank.staging(w.B, w.k)
     cs = torch.cuda.Stream()
     torch.cuda.synchronize()
-    copied = [0, 0]
+    copied = [0, 0, 0]
 
     def step(i, count):
-        q, q_route, k_loc, v_loc, L = batches[i % len(batches)]
+        q_route = S.route_queries(w, dev, batch=i)
         _, _, _, st = bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=q_route, ws=ws,
                                 staging=stg, copy_stream=cs)
         if count:
             copied[0] += st.bytes_copied
             copied[1] += st.docs_copied
+            copied[2] += st.docs_cached
 
+    log(f"host bank: {warmup} warm-up steps, cache slots {slots}")
     for i in range(warmup):
         step(i, False)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(i, True)
+        step(warmup + i, True)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    bank.set_cache(None)
     # a plain pinned host -> device copy of 1 GiB, for the link's own rate
     hsrc = torch.empty(1 << 28, dtype=torch.float32, pin_memory=True)
     ddst = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -259,7 +268,10 @@ def host_bank_bench(steps, warmup):
             "queries_per_s": w.B * steps / dt, "ms_per_step": dt * 1e3 / steps, "steps": steps,
             "h2d_GBs": copied[0] / dt / 1e9, "docs_copied_per_step": copied[1] / steps,
             "bytes_copied_per_step": copied[0] / steps, "pinned_copy_GBs": link,
-            "h2d_frac_of_pinned_copy": copied[0] / dt / 1e9 / link}
+            "h2d_frac_of_pinned_copy": copied[0] / dt / 1e9 / link,
+            "cache": {"slots": slots, "bytes": slots * bank.cache_slot_bytes(),
+                      "share_of_documents": slots / w.n_docs,
+                      "hit_rate": copied[2] / max(1, copied[1] + copied[2])} if slots else None}
 
 
 def interleave_bench(steps, warmup):
@@ -335,6 +347,8 @@ def main():
     ap.add_argument("--prefill-splits", type=int, default=0, help="token splits (0: automatic)")
     ap.add_argument("--c4-steps", type=int, default=0,
                     help="also run the 100M-token host-bank leg (0 skips it)")
+    ap.add_argument("--c4-cache-gb", type=float, default=0.0,
+                    help="device document cache for the host-bank leg, GB (0: none)")
     ap.add_argument("--c5-steps", type=int, default=0,
                     help="also run the 3-hop interleave leg over 32 Mi tokens (0 skips it)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -436,6 +450,8 @@ def main():
     if args.c4_steps > 0:
         torch.cuda.empty_cache()
         res["host_bank"] = host_bank_bench(args.c4_steps, 2)
+        if args.c4_cache_gb > 0:
+            res["host_bank_cached"] = host_bank_bench(args.c4_steps, 2, args.c4_cache_gb)
     if args.c5_steps > 0:
         torch.cuda.empty_cache()
         res["interleave"] = interleave_bench(args.c5_steps, 2)

@@ -179,6 +179,8 @@ typedef struct {
 typedef struct {
   int64_t docs_copied;       /* host banks: distinct documents copied host->device */
   int64_t bytes_copied;      /* host banks: bytes copied host->device */
+  int64_t docs_cached;       /* host banks with a device cache: distinct selected
+                                documents found in the cache (no copy) */
 } msa_step_stats;
 
 const char* msa_status_string(int status);
@@ -249,14 +251,35 @@ int msa_route(const msa_bank* bank, const float* q_route, int32_t B, int32_t k,
  * j <= L_loc - n_q + i (the queries are the last n_q local tokens). */
 int msa_attend(const msa_bank* bank, const msa_attend_args* args, void* stream);
 
+/* Device (HBM) document cache of a host-resident bank (intelliparadigm.com,
+ * section 5.2: keep frequently used memory in HBM; "MSA" card, "Pułapki
+ * implementacyjne": the CPU-GPU link is the bottleneck of large banks).
+ *   cache: device memory the caller owns (NULL detaches), cache_bytes of it,
+ *     divided into msa_cache_slot_bytes() slots, each holding one document's
+ *     K then V in the store layouts.
+ * While a cache is attached, msa_step keeps recently selected documents
+ * resident: a selected document already in a slot is read from there, any
+ * other is copied from the host store into the least recently used slot
+ * that the same hop does not need (its `staging` is then unused and may be
+ * NULL).  Before a slot is overwritten, the previous step's attention on
+ * this bank has completed.  Results are identical with and without a cache.
+ * Errors: MSA_EINVAL for a device-resident bank; MSA_ENOMEM if no slot
+ * fits; msa_step fails with MSA_ENOMEM when one hop selects more distinct
+ * documents than there are slots.  Resets the cache's contents; not to be
+ * called while an msa_step on this bank is running.  Synchronous. */
+int msa_bank_set_cache(msa_bank* bank, void* cache, size_t cache_bytes);
+size_t msa_cache_slot_bytes(const msa_bank* bank);
+
 /* Route + top-k + gather + attend for one batch, `hops` times ("MSA" card,
  * "Równoległość": top-k then K/V fetch, sequential in each decode step;
  * "Komponenty": Memory Interleave).  Prefill: each block of `block` query
  * tokens routes with the mean of its router vectors and shares one top-k set.
  * Host-resident banks: after top-k the ids are read back (the call blocks
  * once per hop on `stream`), each distinct selected document is copied into
- * `staging` on `copy_stream` (NULL = `stream`), and attention waits for the
- * copies.  `stats` (host, may be NULL) receives copy counts. */
+ * `staging` -- or, with a device cache attached, found in the cache or
+ * copied into a cache slot -- on `copy_stream` (NULL = `stream`), and
+ * attention waits for the copies.  `stats` (host, may be NULL) receives copy
+ * and cache-hit counts. */
 int msa_step(const msa_bank* bank, const msa_step_args* args, void* stream,
              void* copy_stream, msa_step_stats* stats);
 

@@ -172,7 +172,7 @@ const char* msa_status_string(int status) {
 
 const char* msa_last_error(void) { return g_last_error.c_str(); }
 
-int msa_version(void) { return 10000; }
+int msa_version(void) { return 10100; }
 
 int msa_timer_enable(int on) {
   g_timer.on = on != 0;
@@ -324,6 +324,7 @@ int msa_bank_create(const msa_bank_desc* d, msa_bank** out) {
     e = host_buffers_reserve(*bk, kHostIdsInitial);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&bk->copies_done, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&bk->tables_done, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&bk->attn_done, hipEventDisableTiming);
     if (e != hipSuccess) {
       msa_bank_destroy(reinterpret_cast<msa_bank*>(bk));
       return fail(MSA_EHIP, std::string("host-bank buffers: ") + hipGetErrorString(e));
@@ -339,6 +340,8 @@ int msa_bank_destroy(msa_bank* b) {
   if (bk->tables_pending) (void)hipEventSynchronize(bk->tables_done);
   if (bk->copies_done) (void)hipEventDestroy(bk->copies_done);
   if (bk->tables_done) (void)hipEventDestroy(bk->tables_done);
+  if (bk->attn_pending) (void)hipEventSynchronize(bk->attn_done);
+  if (bk->attn_done) (void)hipEventDestroy(bk->attn_done);
   if (bk->dev_mem) (void)hipFree(bk->dev_mem);
   if (bk->h_ids) (void)hipHostFree(bk->h_ids);
   if (bk->h_src) (void)hipHostFree(bk->h_src);
@@ -400,6 +403,41 @@ size_t msa_staging_bytes(const msa_bank* b, int32_t n_groups, int32_t k) {
   const Bank& bk = *as_bank(b);
   return (size_t)2 * n_groups * k * bk.max_doc_len * bk.desc.h_kv * kD *
          dtype_size(bk.desc.dtype);
+}
+
+size_t msa_cache_slot_bytes(const msa_bank* b) {
+  if (!b) return 0;
+  const Bank& bk = *as_bank(b);
+  return (size_t)2 * bk.max_doc_len * bk.desc.h_kv * kD * dtype_size(bk.desc.dtype);
+}
+
+int msa_bank_set_cache(msa_bank* b, void* cache, size_t cache_bytes) {
+  if (!b) return fail(MSA_EINVAL, "NULL bank");
+  Bank& bk = *reinterpret_cast<Bank*>(b);
+  if (bk.desc.kv_loc != MSA_KV_HOST) return fail(MSA_EINVAL, "a device cache needs a host-resident bank");
+  std::lock_guard<std::mutex> lock(bk.host_mu);
+  if (bk.attn_pending) {  // the previous cached step's attention may still read the old cache
+    MSA_CHECK_HIP(hipEventSynchronize(bk.attn_done));
+    bk.attn_pending = false;
+  }
+  bk.cache = nullptr;
+  bk.cache_slots = 0;
+  bk.cache_doc.clear();
+  bk.cache_epoch.clear();
+  bk.cache_lru.clear();
+  bk.cache_pos.clear();
+  bk.cache_slot_of.clear();
+  if (!cache) return MSA_OK;
+  const size_t slot = msa_cache_slot_bytes(b);
+  const int64_t n = (int64_t)(cache_bytes / slot);
+  if (n < 1) return fail(MSA_ENOMEM, "cache smaller than one document slot");
+  bk.cache = (char*)cache;
+  bk.cache_slots = n;
+  bk.cache_doc.assign(n, -1);
+  bk.cache_epoch.assign(n, 0);
+  bk.cache_pos.resize(n);
+  for (int64_t i = 0; i < n; ++i) bk.cache_pos[i] = bk.cache_lru.insert(bk.cache_lru.end(), (int32_t)i);
+  return MSA_OK;
 }
 
 int msa_route(const msa_bank* b, const float* q_route, int32_t B, int32_t k,
@@ -476,6 +514,7 @@ int msa_step(const msa_bank* b, const msa_step_args* a, void* stream, void* copy
   if (stats) {
     stats->docs_copied = 0;
     stats->bytes_copied = 0;
+    stats->docs_cached = 0;
   }
   if (a->n_q == 0) return MSA_OK;
   if (!a->q || !a->ids || !a->scores || !a->out || !a->ws) return fail(MSA_EINVAL, "NULL pointer");
@@ -490,11 +529,6 @@ int msa_step(const msa_bank* b, const msa_step_args* a, void* stream, void* copy
   if (a->ws_bytes < L.total) return fail(MSA_ENOMEM, "workspace too small for msa_step");
   const size_t esz = dtype_size(bk.desc.dtype);
   const size_t tok_bytes = (size_t)bk.desc.h_kv * kD * esz;
-  if (host) {
-    if (!a->staging) return fail(MSA_EINVAL, "host-resident bank needs a staging buffer");
-    if (a->staging_bytes < msa_staging_bytes(b, n_groups, k))
-      return fail(MSA_ENOMEM, "staging buffer too small");
-  }
   // The host part of a host-resident bank's step (id readback, copy issue,
   // remap tables) uses the bank's pinned buffers: one step at a time.
   std::unique_lock<std::mutex> host_lock;
@@ -507,6 +541,11 @@ int msa_step(const msa_bank* b, const msa_step_args* a, void* stream, void* copy
     }
     if (host_buffers_reserve(bk, (size_t)n_groups * k) != hipSuccess)
       return fail(MSA_ENOMEM, "pinned id buffers");
+    if (!bk.cache) {
+      if (!a->staging) return fail(MSA_EINVAL, "host-resident bank needs a staging buffer");
+      if (a->staging_bytes < msa_staging_bytes(b, n_groups, k))
+        return fail(MSA_ENOMEM, "staging buffer too small");
+    }
   }
   char* w = (char*)a->ws;
   hipStream_t s = (hipStream_t)stream;
@@ -536,19 +575,18 @@ int msa_step(const msa_bank* b, const msa_step_args* a, void* stream, void* copy
     AttnSources src{bk.desc.k_store, bk.desc.v_store, bk.d_kv_off, bk.d_doc_len, N};
     const int32_t* att_ids = ids;
     if (host) {
-      // top-k -> K/V fetch is sequential: read the ids back, copy each
-      // distinct selected document into staging, remap ids to staging slots
+      // top-k -> K/V fetch is sequential: read the ids back, then make each
+      // distinct selected document resident on the device (a cache hit, or
+      // a copy into a cache slot or into staging) and remap the ids to a
+      // compact table of those documents
       MSA_CHECK_HIP(hipMemcpyAsync(bk.h_ids, ids, (size_t)n_groups * k * 4,
                                    hipMemcpyDeviceToHost, s));
       MSA_CHECK_HIP(hipStreamSynchronize(s));
-      std::unordered_map<int32_t, int32_t> slot_of;
-      int32_t* slot_ids = bk.h_src;                       // [n_groups*k]
-      int32_t* slot_len = bk.h_src + (size_t)n_groups * k; // [n_slots]
-      int64_t* slot_off = bk.h_src_off;                   // [n_slots]
-      int64_t tok = 0;
-      int32_t n_slots = 0;
-      char* stg = (char*)a->staging;
-      const size_t half = a->staging_bytes / 2;
+      std::unordered_map<int32_t, int32_t> slot_of;  // document -> compact index
+      std::vector<int32_t> docs;                      // compact index -> document
+      int32_t* slot_ids = bk.h_src;                        // [n_groups*k]
+      int32_t* slot_len = bk.h_src + (size_t)n_groups * k;  // [n_slots]
+      int64_t* slot_off = bk.h_src_off;                    // [n_slots]
       for (size_t i = 0; i < (size_t)n_groups * k; ++i) {
         const int32_t id = bk.h_ids[i];
         if (id < 0 || id >= N) {
@@ -557,26 +595,86 @@ int msa_step(const msa_bank* b, const msa_step_args* a, void* stream, void* copy
         }
         auto it = slot_of.find(id);
         if (it == slot_of.end()) {
-          const int64_t Ld = bk.doc_len[id];
-          slot_of.emplace(id, n_slots);
-          slot_off[n_slots] = tok;
-          slot_len[n_slots] = (int32_t)Ld;
-          const size_t bytes = (size_t)Ld * tok_bytes;
-          const size_t src_o = (size_t)bk.kv_off[id] * tok_bytes;
-          MSA_CHECK_HIP(hipMemcpyAsync(stg + (size_t)tok * tok_bytes,
-                                       (const char*)bk.desc.k_store + src_o, bytes,
-                                       hipMemcpyHostToDevice, cs));
-          MSA_CHECK_HIP(hipMemcpyAsync(stg + half + (size_t)tok * tok_bytes,
-                                       (const char*)bk.desc.v_store + src_o, bytes,
-                                       hipMemcpyHostToDevice, cs));
-          if (stats) {
-            stats->docs_copied += 1;
-            stats->bytes_copied += (int64_t)(2 * bytes);
+          it = slot_of.emplace(id, (int32_t)docs.size()).first;
+          docs.push_back(id);
+        }
+        slot_ids[i] = it->second;
+      }
+      const int32_t n_slots = (int32_t)docs.size();
+      auto copy_doc = [&](int32_t id, char* kdst, char* vdst) -> hipError_t {
+        const size_t bytes = (size_t)bk.doc_len[id] * tok_bytes;
+        const size_t src_o = (size_t)bk.kv_off[id] * tok_bytes;
+        hipError_t e = hipMemcpyAsync(kdst, (const char*)bk.desc.k_store + src_o, bytes,
+                                      hipMemcpyHostToDevice, cs);
+        if (e == hipSuccess)
+          e = hipMemcpyAsync(vdst, (const char*)bk.desc.v_store + src_o, bytes,
+                             hipMemcpyHostToDevice, cs);
+        if (stats) {
+          stats->docs_copied += 1;
+          stats->bytes_copied += (int64_t)(2 * bytes);
+        }
+        return e;
+      };
+      char* kbase;
+      char* vbase;
+      if (bk.cache) {
+        if (n_slots > bk.cache_slots)
+          return fail(MSA_ENOMEM, "one hop selects more distinct documents than the cache has slots");
+        const size_t slot_k = (size_t)bk.max_doc_len * tok_bytes;
+        kbase = bk.cache;
+        vbase = bk.cache + (size_t)bk.cache_slots * slot_k;
+        const uint64_t ep = ++bk.hop_epoch;
+        auto touch = [&](int32_t slot) {
+          bk.cache_lru.splice(bk.cache_lru.begin(), bk.cache_lru, bk.cache_pos[slot]);
+          bk.cache_epoch[slot] = ep;
+        };
+        std::vector<int32_t> where(n_slots, -1);
+        bool evict = false;
+        // hits first: they move to the front, so no miss of this hop evicts them
+        for (int32_t j = 0; j < n_slots; ++j) {
+          auto h = bk.cache_slot_of.find(docs[j]);
+          if (h != bk.cache_slot_of.end()) {
+            where[j] = h->second;
+            touch(h->second);
+            if (stats) stats->docs_cached += 1;
+          } else {
+            evict = true;
           }
-          slot_ids[i] = n_slots++;
-          tok += Ld;
-        } else {
-          slot_ids[i] = it->second;
+        }
+        if (evict && bk.attn_pending) {  // no earlier attention may still read a victim
+          MSA_CHECK_HIP(hipEventSynchronize(bk.attn_done));
+          bk.attn_pending = false;
+        }
+        for (int32_t j = 0; j < n_slots; ++j) {
+          if (where[j] >= 0) continue;
+          const int32_t victim = bk.cache_lru.back();
+          if (bk.cache_epoch[victim] == ep) return fail(MSA_ENOMEM, "cache slots exhausted");
+          if (bk.cache_doc[victim] >= 0) bk.cache_slot_of.erase(bk.cache_doc[victim]);
+          bk.cache_doc[victim] = docs[j];
+          bk.cache_slot_of[docs[j]] = victim;
+          touch(victim);
+          where[j] = victim;
+          MSA_CHECK_HIP(copy_doc(docs[j], kbase + (size_t)victim * slot_k,
+                                 vbase + (size_t)victim * slot_k));
+        }
+        for (int32_t j = 0; j < n_slots; ++j) {
+          slot_off[j] = (int64_t)where[j] * bk.max_doc_len;
+          slot_len[j] = (int32_t)bk.doc_len[docs[j]];
+        }
+      } else {
+        if (!a->staging) return fail(MSA_EINVAL, "host-resident bank needs a staging buffer");
+        if (a->staging_bytes < msa_staging_bytes(b, n_groups, k))
+          return fail(MSA_ENOMEM, "staging buffer too small");
+        const size_t half = a->staging_bytes / 2;
+        kbase = (char*)a->staging;
+        vbase = kbase + half;
+        int64_t tok = 0;
+        for (int32_t j = 0; j < n_slots; ++j) {
+          slot_off[j] = tok;
+          slot_len[j] = (int32_t)bk.doc_len[docs[j]];
+          MSA_CHECK_HIP(copy_doc(docs[j], kbase + (size_t)tok * tok_bytes,
+                                 vbase + (size_t)tok * tok_bytes));
+          tok += bk.doc_len[docs[j]];
         }
       }
       int32_t* d_ids = (int32_t*)(w + L.srcids);
@@ -594,7 +692,7 @@ int msa_step(const msa_bank* b, const msa_step_args* a, void* stream, void* copy
         MSA_CHECK_HIP(hipEventRecord(bk.copies_done, cs));
         MSA_CHECK_HIP(hipStreamWaitEvent(s, bk.copies_done, 0));
       }
-      src = AttnSources{stg, stg + half, d_off, d_len, n_slots};
+      src = AttnSources{kbase, vbase, d_off, d_len, n_slots};
       att_ids = d_ids;
     }
     if (prefill)
@@ -604,6 +702,10 @@ int msa_step(const msa_bank* b, const msa_step_args* a, void* stream, void* copy
     else
       MSA_CHECK_HIP(launch_decode(bk, w + L.qrot, a->n_q, a->h_q, att_ids, k, src, a->k_loc,
                                   a->v_loc, a->L_loc, splits, (float*)(w + L.part), out, s));
+    if (host && bk.cache) {
+      MSA_CHECK_HIP(hipEventRecord(bk.attn_done, s));
+      bk.attn_pending = true;
+    }
     if (hop + 1 < a->hops) {
       MSA_CHECK_HIP(launch_project(out, a->w_proj, a->n_q, a->h_q * kD, kD, q_route, s));
       qr = q_route;

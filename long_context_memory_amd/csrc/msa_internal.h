@@ -7,7 +7,9 @@
 #include <stddef.h>
 
 #include <string>
+#include <list>
 #include <mutex>
+#include <unordered_map>
 #include <vector>
 
 #include "../../include/msa.h"
@@ -46,6 +48,19 @@ struct Bank {
   hipEvent_t copies_done = nullptr;  // document copies on the copy stream
   hipEvent_t tables_done = nullptr;  // remap tables read out of h_src / h_src_off
   bool tables_pending = false;
+  // device document cache of a host-resident bank (msa_bank_set_cache):
+  // slot s holds one document's K at cache + s * slot K bytes and its V in
+  // the second half; an LRU list of slots, most recently used first
+  char* cache = nullptr;
+  int64_t cache_slots = 0;
+  std::vector<int32_t> cache_doc;     // [slots] document in the slot, or -1
+  std::vector<uint64_t> cache_epoch;  // [slots] last hop that used the slot
+  std::list<int32_t> cache_lru;
+  std::vector<std::list<int32_t>::iterator> cache_pos;
+  std::unordered_map<int32_t, int32_t> cache_slot_of;  // document -> slot
+  uint64_t hop_epoch = 0;
+  hipEvent_t attn_done = nullptr;  // the last cached step's attention
+  bool attn_pending = false;
   std::mutex host_mu;
 };
 

@@ -25,7 +25,7 @@ EXPORTS = [
     "msa_status_string", "msa_last_error", "msa_version", "msa_bank_create",
     "msa_bank_destroy", "msa_bank_get_info", "msa_build_bank", "msa_prepare_local",
     "msa_workspace_bytes", "msa_staging_bytes", "msa_route", "msa_attend", "msa_step",
-    "msa_timer_enable", "msa_timer_read",
+    "msa_timer_enable", "msa_timer_read", "msa_bank_set_cache", "msa_cache_slot_bytes",
 ]
 MSA_TIMER_ATTENTION, MSA_TIMER_ROUTE = 0, 1
 
@@ -63,7 +63,7 @@ class StepArgs(C.Structure):
 
 
 class StepStats(C.Structure):
-    _fields_ = [("docs_copied", i64), ("bytes_copied", i64)]
+    _fields_ = [("docs_copied", i64), ("bytes_copied", i64), ("docs_cached", i64)]
 
 
 def _load():
@@ -85,6 +85,10 @@ def _load():
     lib.msa_workspace_bytes.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32]
     lib.msa_staging_bytes.restype = C.c_size_t
     lib.msa_staging_bytes.argtypes = [vp, i32, i32]
+    lib.msa_cache_slot_bytes.restype = C.c_size_t
+    lib.msa_cache_slot_bytes.argtypes = [vp]
+    lib.msa_bank_set_cache.restype = C.c_int
+    lib.msa_bank_set_cache.argtypes = [vp, vp, C.c_size_t]
     lib.msa_route.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp, C.c_size_t, vp]
     lib.msa_attend.argtypes = [vp, C.POINTER(AttendArgs), vp]
     lib.msa_step.argtypes = [vp, C.POINTER(StepArgs), vp, vp, C.POINTER(StepStats)]
@@ -218,6 +222,16 @@ class Bank:
         n = self.workspace_bytes(mode, n_q, h_q, k, block, hops, splits)
         return torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
 
+    def cache_slot_bytes(self) -> int:
+        return int(lib.msa_cache_slot_bytes(self.handle))
+
+    def set_cache(self, cache=None):
+        """Attach a device document cache (a uint8 device tensor, kept alive
+        by the bank) to this host-resident bank, or detach it (None)."""
+        nbytes = 0 if cache is None else cache.numel() * cache.element_size()
+        _check(lib.msa_bank_set_cache(self.handle, _ptr(cache), nbytes), "msa_bank_set_cache")
+        self.cache = cache
+
     def staging(self, n_groups, k):
         n = int(lib.msa_staging_bytes(self.handle, n_groups, k))
         return torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
@@ -257,7 +271,7 @@ class Bank:
         n_groups = n_q // block if mode == MSA_PREFILL else n_q
         if ws is None:
             ws = self.workspace(mode, n_q, h_q, k, block, hops, splits)
-        if self.kv_host and staging is None:
+        if self.kv_host and staging is None and getattr(self, "cache", None) is None:
             staging = self.staging(n_groups, k)
         if outputs is None:
             ids = torch.empty((hops, n_groups, k), dtype=torch.int32, device=self.device)

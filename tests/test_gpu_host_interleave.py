@@ -152,6 +152,115 @@ def test_host_bank_concurrent_steps(msa):
         assert len(r) == 4 and all(torch.equal(o, ref) for o in r)
 
 
+def host_batches(c, n):
+    """n query batches for the host-bank workload (batch 0 = the case's)."""
+    w, bank = c["w"], c["bank"]
+    out = []
+    for i in range(n):
+        q = S.queries(w, DEV, batch=i)
+        qr = S.route_queries(w, DEV, batch=i)
+        lk, lv = S.local_raw(w, DEV, batch=i)
+        k_loc, v_loc, L = bank.prepare_local(lk, lv, w.P0)
+        out.append((q, qr, k_loc, v_loc, L))
+    return out
+
+
+def test_host_cache_identical_results_and_counts(msa):
+    """A device document cache smaller than the bank (forcing evictions)
+    gives bit-identical results to the uncached copy path; every step's
+    distinct documents are either hits or copies, and a repeated batch is
+    served from the cache alone."""
+    c = host_case(msa, "c4_small")
+    w, bank = c["w"], c["bank"]
+    batches = host_batches(c, 3)
+    ref = []
+    for q, qr, k_loc, v_loc, L in batches:
+        ids, _, out, _ = bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=qr)
+        ref.append((ids.clone(), out.clone()))
+    n_slots = 10  # < 24 documents, >= one step's <= 8 distinct selections
+    cache = torch.empty(n_slots * bank.cache_slot_bytes(), dtype=torch.uint8, device=DEV)
+    bank.set_cache(cache)
+    try:
+        order = [0, 1, 2, 0, 0, 2, 1, 1]
+        prev = None
+        for i in order:
+            q, qr, k_loc, v_loc, L = batches[i]
+            ids, _, out, st = bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=qr)
+            torch.cuda.synchronize()
+            assert torch.equal(ids, ref[i][0]) and torch.equal(out, ref[i][1]), f"batch {i}"
+            distinct = len(set(ids[0].cpu().numpy().ravel().tolist()))
+            assert st.docs_cached + st.docs_copied == distinct
+            if prev == i:
+                assert st.docs_copied == 0 and st.docs_cached == distinct, "repeat not served from cache"
+            prev = i
+    finally:
+        bank.set_cache(None)
+    # detached: the staging path again
+    q, qr, k_loc, v_loc, L = batches[0]
+    _, _, out, st = bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=qr)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref[0][1]) and st.docs_cached == 0
+
+
+def test_host_cache_too_small_for_a_step(msa):
+    c = host_case(msa, "c4_small")
+    w, bank = c["w"], c["bank"]
+    cache = torch.empty(2 * bank.cache_slot_bytes(), dtype=torch.uint8, device=DEV)
+    bank.set_cache(cache)
+    try:
+        with pytest.raises(msa.MSAError, match="cache"):
+            bank.step(c["q"], w.q_pos, w.k, c["k_loc"], c["v_loc"], c["L"], q_route=c["q_route"])
+    finally:
+        bank.set_cache(None)
+    with pytest.raises(msa.MSAError):
+        bank.set_cache(torch.empty(16, dtype=torch.uint8, device=DEV))  # smaller than a slot
+    dev_bank = interleave_case(msa, "c5_small")["bank"]
+    with pytest.raises(msa.MSAError):  # device-resident banks take no cache
+        dev_bank.set_cache(torch.empty(dev_bank.cache_slot_bytes(), dtype=torch.uint8, device=DEV))
+
+
+def test_host_cache_concurrent_streams(msa):
+    """Two threads stepping one cached host bank on their own streams and
+    workspaces (evictions fenced against the other's attention)."""
+    import threading
+    c = host_case(msa, "c4_small")
+    w, bank = c["w"], c["bank"]
+    batches = host_batches(c, 3)
+    refs = []
+    for q, qr, k_loc, v_loc, L in batches:
+        _, _, out, _ = bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=qr)
+        refs.append(out.clone())
+    torch.cuda.synchronize()
+    cache = torch.empty(9 * bank.cache_slot_bytes(), dtype=torch.uint8, device=DEV)
+    bank.set_cache(cache)
+    results, errors = [[], []], []
+
+    def run(t):
+        try:
+            st = torch.cuda.Stream()
+            ws = bank.workspace(msa.MSA_DECODE, w.B, w.h_q, w.k)
+            for r in range(6):
+                i = (r + t) % 3
+                q, qr, k_loc, v_loc, L = batches[i]
+                _, _, out, _ = bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=qr, ws=ws, stream=st)
+                st.synchronize()
+                results[t].append((i, out.clone()))
+        except Exception as e:  # reported below
+            errors.append(e)
+
+    try:
+        th = [threading.Thread(target=run, args=(t,)) for t in range(2)]
+        for t in th:
+            t.start()
+        for t in th:
+            t.join()
+    finally:
+        bank.set_cache(None)
+    assert not errors, errors
+    for r in results:
+        assert len(r) == 6 and all(torch.equal(o, refs[i]) for i, o in r)
+
+
 # --------------------------------------------------------------------------
 # interleaved multi-hop retrieval
 # --------------------------------------------------------------------------
