@@ -46,8 +46,9 @@
  *     the bank.
  *
  * Layouts (row-major; the last index is contiguous)
- *   Routing keys      kr       [h_r][C][d_r]        (C = total chunks)
- *   Key norms         inv_norm [h_r][C] float32     (1/||key||, 0 for a zero key)
+ *   Routing keys      kr       [h_r][C_cap][d_r]    (C = total chunks in use,
+ *                                                    C_cap >= C the capacity)
+ *   Key norms         inv_norm [h_r][C_cap] float32 (1/||key||, 0 for a zero key)
  *   Document K store  per document n at token offset kv_off[n]:
  *                     k_store + kv_off[n]*h_kv*d  ->  [h_kv][L_n][d]
  *                     (rotated at document-local positions 0..L_n-1)
@@ -100,10 +101,13 @@ typedef struct {
   int32_t d;                 /* 128 */
   double rope_base;          /* RoPE base (10000) */
   msa_kv_loc kv_loc;         /* where k_store / v_store live */
-  void* kr;                  /* device [h_r][C][d_r], dtype */
-  float* inv_norm;           /* device [h_r][C] */
+  void* kr;                  /* device [h_r][C_cap][d_r], dtype (rows [0, C) in use) */
+  float* inv_norm;           /* device [h_r][C_cap] */
   void* k_store;             /* device or pinned host, kv_tokens*h_kv*d elements */
   void* v_store;             /* device or pinned host, kv_tokens*h_kv*d elements */
+  int64_t chunk_cap;         /* C_cap, routing-key rows per head the kr / inv_norm
+                                allocations hold (room for msa_bank_append);
+                                0 = exactly the chunks of the initial documents */
 } msa_bank_desc;
 
 typedef struct {
@@ -192,6 +196,21 @@ int msa_version(void);
  * Does not touch kr / inv_norm / the K/V stores.  Synchronous. */
 int msa_bank_create(const msa_bank_desc* desc, msa_bank** out);
 int msa_bank_destroy(msa_bank* bank);
+
+/* Incremental bank growth ("MSA" card, "Pułapki implementacyjne": the memory
+ * bank is built ahead of inference; new documents join it without rebuilding
+ * the rest).  Appends n_new documents after the current ones (ids N ..
+ * N + n_new - 1): doc_len (host, each a positive multiple of 256) and
+ * kv_off (host, or NULL = packed after the current tokens) as in the
+ * descriptor.  The routing-key and K/V allocations must already hold them
+ * (chunk_cap, kv_tokens), else MSA_EINVAL.  Their keys and K/V are then
+ * written by msa_build_bank(bank, N, N + n_new, ...) (a device-resident
+ * store) or by the caller (a host-resident store).  Workspace and staging
+ * sizes may grow: query them again.  A document longer than an attached
+ * cache's slots is refused (detach the cache first).  Not to be called
+ * concurrently with other calls on this bank.  Synchronous. */
+int msa_bank_append(msa_bank* bank, int32_t n_new, const int64_t* doc_len,
+                    const int64_t* kv_off);
 int msa_bank_get_info(const msa_bank* bank, msa_bank_info* info);
 
 /* Offline bank build for documents [doc_begin, doc_end) ("MSA" card,

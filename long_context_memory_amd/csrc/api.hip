@@ -199,6 +199,121 @@ int msa_timer_read(int which, double* total_ms, int64_t* launches) {
   return MSA_OK;
 }
 
+namespace {
+
+// Append documents to the bank's host tables (document and token/chunk
+// offsets), checking the store capacities.  On error nothing is changed.
+int bank_add_docs(Bank* bk, int n_new, const int64_t* doc_len, const int64_t* kv_off) {
+  const int N0 = (int)bk->doc_len.size();
+  if ((int64_t)N0 + n_new >= ((int64_t)1 << 31)) return fail(MSA_EUNSUPPORTED, "too many documents");
+  int64_t tok = bk->n_tokens, lmax = bk->max_doc_len;
+  std::vector<int64_t> kvo(n_new);
+  for (int i = 0; i < n_new; ++i) {
+    const int64_t L = doc_len[i];
+    if (L <= 0 || L % kChunk || L > (int64_t)1 << 30)
+      return fail(MSA_EINVAL, "doc_len[" + std::to_string(N0 + i) + "] must be a positive multiple of 256");
+    const int64_t o = kv_off ? kv_off[i] : tok;
+    if (o < 0 || o + L > bk->desc.kv_tokens)
+      return fail(MSA_EINVAL, "kv_off[" + std::to_string(N0 + i) + "] + doc_len exceeds kv_tokens");
+    kvo[i] = o;
+    tok += L;
+    lmax = std::max(lmax, L);
+  }
+  if (tok / kChunk > bk->chunk_stride)
+    return fail(MSA_EINVAL, "documents exceed the routing-key capacity (chunk_cap)");
+  if (tok / kChunk >= ((int64_t)1 << 31)) return fail(MSA_EUNSUPPORTED, "too many chunks");
+  if (bk->cache && lmax > bk->max_doc_len)
+    return fail(MSA_EINVAL, "a document longer than the cache slots: detach the cache first");
+  if (bk->tok_off.empty()) {
+    bk->tok_off.push_back(0);
+    bk->chunk_off.push_back(0);
+  }
+  for (int i = 0; i < n_new; ++i) {
+    bk->doc_len.push_back(doc_len[i]);
+    bk->kv_off.push_back(kvo[i]);
+    bk->tok_off.push_back(bk->tok_off.back() + doc_len[i]);
+    bk->chunk_off.push_back((int32_t)(bk->tok_off.back() / kChunk));
+  }
+  bk->n_tokens = tok;
+  bk->n_chunks = tok / kChunk;
+  bk->max_doc_len = lmax;
+  bk->desc.n_docs = (int32_t)bk->doc_len.size();
+  return MSA_OK;
+}
+
+// (Re)build the device tables from the host tables: document lengths and
+// offsets, the chunk -> document map, the routing tiles' pieces (document x
+// 64-chunk tile overlaps) and the RoPE frequencies, in one allocation.
+int bank_upload_tables(Bank* bk) {
+  const int N = bk->desc.n_docs;
+  const int64_t C = bk->n_chunks;
+  const int32_t n_tiles = (int32_t)((C + kRouteTile - 1) / kRouteTile);
+  std::vector<int32_t> chunk_doc(C), tile_piece0(n_tiles + 1), doc_piece0(N + 1);
+  for (int n = 0; n < N; ++n)
+    for (int64_t c = bk->chunk_off[n]; c < bk->chunk_off[n + 1]; ++c) chunk_doc[c] = n;
+  int32_t piece = 0;
+  int last_doc = -1;
+  for (int t = 0; t < n_tiles; ++t) {
+    tile_piece0[t] = piece;
+    const int64_t c0 = (int64_t)t * kRouteTile, c1 = std::min(C, c0 + kRouteTile);
+    for (int64_t c = c0; c < c1; ++c) {
+      const int n = chunk_doc[c];
+      if (c == c0 || n != chunk_doc[c - 1]) {
+        if (n != last_doc) {
+          for (int m = last_doc + 1; m <= n; ++m) doc_piece0[m] = piece;
+          last_doc = n;
+        }
+        ++piece;
+      }
+    }
+  }
+  tile_piece0[n_tiles] = piece;
+  for (int m = last_doc + 1; m <= N; ++m) doc_piece0[m] = piece;
+  std::vector<int32_t> dl32(N);
+  for (int n = 0; n < N; ++n) dl32[n] = (int32_t)bk->doc_len[n];
+  double inv_freq[kD / 2];
+  for (int i = 0; i < kD / 2; ++i) inv_freq[i] = std::pow(bk->desc.rope_base, -2.0 * i / kD);
+
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const size_t o_dl = take(N * 4), o_kv = take(N * 8), o_tok = take((N + 1) * 8),
+               o_cd = take(C * 4), o_tp = take((n_tiles + 1) * 4),
+               o_dp = take((N + 1) * 4), o_if = take(sizeof(inv_freq));
+  void* mem = nullptr;
+  if (hipMalloc(&mem, off) != hipSuccess) return fail(MSA_ENOMEM, "hipMalloc of bank tables failed");
+  char* base = (char*)mem;
+  hipError_t e = hipMemcpy(base + o_dl, dl32.data(), N * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(base + o_kv, bk->kv_off.data(), N * 8, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(base + o_tok, bk->tok_off.data(), (N + 1) * 8, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(base + o_cd, chunk_doc.data(), C * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess)
+    e = hipMemcpy(base + o_tp, tile_piece0.data(), (n_tiles + 1) * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(base + o_dp, doc_piece0.data(), (N + 1) * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(base + o_if, inv_freq, sizeof(inv_freq), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(mem);
+    return fail(MSA_EHIP, std::string("uploading bank tables: ") + hipGetErrorString(e));
+  }
+  if (bk->dev_mem) (void)hipFree(bk->dev_mem);
+  bk->dev_mem = mem;
+  bk->n_tiles = n_tiles;
+  bk->n_pieces = piece;
+  bk->d_doc_len = (int32_t*)(base + o_dl);
+  bk->d_kv_off = (int64_t*)(base + o_kv);
+  bk->d_tok_off = (int64_t*)(base + o_tok);
+  bk->d_chunk_doc = (int32_t*)(base + o_cd);
+  bk->d_tile_piece0 = (int32_t*)(base + o_tp);
+  bk->d_doc_piece0 = (int32_t*)(base + o_dp);
+  bk->d_inv_freq = (double*)(base + o_if);
+  return MSA_OK;
+}
+
+}  // namespace
+
 int msa_bank_create(const msa_bank_desc* d, msa_bank** out) {
   if (!d || !out) return fail(MSA_EINVAL, "NULL descriptor or output");
   *out = nullptr;
@@ -213,115 +328,25 @@ int msa_bank_create(const msa_bank_desc* d, msa_bank** out) {
   if (d->kv_loc != MSA_KV_DEVICE && d->kv_loc != MSA_KV_HOST) return fail(MSA_EINVAL, "kv_loc");
   if (!d->kr || !d->inv_norm) return fail(MSA_EINVAL, "kr / inv_norm are NULL");
   if (!d->k_store || !d->v_store) return fail(MSA_EINVAL, "k_store / v_store are NULL");
+  if (d->chunk_cap < 0) return fail(MSA_EINVAL, "chunk_cap < 0");
 
   Bank* bk = new Bank();
   bk->desc = *d;
   bk->desc.doc_len = nullptr;
   bk->desc.kv_off = nullptr;
-  const int N = d->n_docs;
-  bk->doc_len.resize(N);
-  bk->kv_off.resize(N);
-  bk->tok_off.resize(N + 1);
-  bk->chunk_off.resize(N + 1);
-  bk->tok_off[0] = 0;
-  bk->chunk_off[0] = 0;
-  for (int n = 0; n < N; ++n) {
-    const int64_t L = d->doc_len[n];
-    if (L <= 0 || L % kChunk || L > (int64_t)1 << 30) {
-      delete bk;
-      return fail(MSA_EINVAL, "doc_len[" + std::to_string(n) + "] must be a positive multiple of 256");
-    }
-    bk->doc_len[n] = L;
-    bk->tok_off[n + 1] = bk->tok_off[n] + L;
-    bk->chunk_off[n + 1] = (int32_t)(bk->tok_off[n + 1] / kChunk);
-    bk->max_doc_len = std::max(bk->max_doc_len, L);
-  }
-  bk->n_tokens = bk->tok_off[N];
-  bk->n_chunks = bk->n_tokens / kChunk;
-  if (bk->n_chunks >= ((int64_t)1 << 31)) {
+  bk->desc.n_docs = 0;
+  int64_t chunks = 0;
+  for (int n = 0; n < d->n_docs; ++n) chunks += std::max<int64_t>(0, d->doc_len[n]) / kChunk;
+  bk->chunk_stride = d->chunk_cap > 0 ? d->chunk_cap : chunks;
+  int st = bank_add_docs(bk, d->n_docs, d->doc_len, d->kv_off);
+  if (st == MSA_OK && hipGetDevice(&bk->device) != hipSuccess) st = fail(MSA_EHIP, "hipGetDevice");
+  if (st == MSA_OK) st = bank_upload_tables(bk);
+  if (st != MSA_OK) {
     delete bk;
-    return fail(MSA_EUNSUPPORTED, "too many chunks");
-  }
-  for (int n = 0; n < N; ++n) {
-    const int64_t o = d->kv_off ? d->kv_off[n] : bk->tok_off[n];
-    if (o < 0 || o + bk->doc_len[n] > d->kv_tokens) {
-      delete bk;
-      return fail(MSA_EINVAL, "kv_off[" + std::to_string(n) + "] + doc_len exceeds kv_tokens");
-    }
-    bk->kv_off[n] = o;
-  }
-  // routing tiles (64 chunks) and pieces (document x tile overlaps)
-  const int64_t C = bk->n_chunks;
-  bk->n_tiles = (int32_t)((C + kRouteTile - 1) / kRouteTile);
-  std::vector<int32_t> chunk_doc(C), tile_piece0(bk->n_tiles + 1), doc_piece0(N + 1);
-  for (int n = 0; n < N; ++n)
-    for (int64_t c = bk->chunk_off[n]; c < bk->chunk_off[n + 1]; ++c) chunk_doc[c] = n;
-  int32_t piece = 0;
-  int last_doc = -1;
-  for (int t = 0; t < bk->n_tiles; ++t) {
-    tile_piece0[t] = piece;
-    const int64_t c0 = (int64_t)t * kRouteTile, c1 = std::min(C, c0 + kRouteTile);
-    for (int64_t c = c0; c < c1; ++c) {
-      const int n = chunk_doc[c];
-      if (c == c0 || n != chunk_doc[c - 1]) {
-        if (n != last_doc) {
-          for (int m = last_doc + 1; m <= n; ++m) doc_piece0[m] = piece;
-          last_doc = n;
-        }
-        ++piece;
-      }
-    }
-  }
-  tile_piece0[bk->n_tiles] = piece;
-  for (int m = last_doc + 1; m <= N; ++m) doc_piece0[m] = piece;
-  bk->n_pieces = piece;
-  std::vector<int32_t> dl32(N);
-  for (int n = 0; n < N; ++n) dl32[n] = (int32_t)bk->doc_len[n];
-  double inv_freq[kD / 2];
-  for (int i = 0; i < kD / 2; ++i) inv_freq[i] = std::pow(d->rope_base, -2.0 * i / kD);
-
-  // one device allocation for every table
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    const size_t o = off;
-    off += align256(bytes);
-    return o;
-  };
-  const size_t o_dl = take(N * 4), o_kv = take(N * 8), o_tok = take((N + 1) * 8),
-               o_cd = take(C * 4), o_tp = take((bk->n_tiles + 1) * 4),
-               o_dp = take((N + 1) * 4), o_if = take(sizeof(inv_freq));
-  if (hipGetDevice(&bk->device) != hipSuccess || hipMalloc(&bk->dev_mem, off) != hipSuccess) {
-    delete bk;
-    return fail(MSA_ENOMEM, "hipMalloc of bank tables failed");
-  }
-  char* base = (char*)bk->dev_mem;
-  bk->d_doc_len = (int32_t*)(base + o_dl);
-  bk->d_kv_off = (int64_t*)(base + o_kv);
-  bk->d_tok_off = (int64_t*)(base + o_tok);
-  bk->d_chunk_doc = (int32_t*)(base + o_cd);
-  bk->d_tile_piece0 = (int32_t*)(base + o_tp);
-  bk->d_doc_piece0 = (int32_t*)(base + o_dp);
-  bk->d_inv_freq = (double*)(base + o_if);
-  hipError_t e = hipSuccess;
-  if (e == hipSuccess) e = hipMemcpy(bk->d_doc_len, dl32.data(), N * 4, hipMemcpyHostToDevice);
-  if (e == hipSuccess) e = hipMemcpy(bk->d_kv_off, bk->kv_off.data(), N * 8, hipMemcpyHostToDevice);
-  if (e == hipSuccess)
-    e = hipMemcpy(bk->d_tok_off, bk->tok_off.data(), (N + 1) * 8, hipMemcpyHostToDevice);
-  if (e == hipSuccess) e = hipMemcpy(bk->d_chunk_doc, chunk_doc.data(), C * 4, hipMemcpyHostToDevice);
-  if (e == hipSuccess)
-    e = hipMemcpy(bk->d_tile_piece0, tile_piece0.data(), (bk->n_tiles + 1) * 4,
-                  hipMemcpyHostToDevice);
-  if (e == hipSuccess)
-    e = hipMemcpy(bk->d_doc_piece0, doc_piece0.data(), (N + 1) * 4, hipMemcpyHostToDevice);
-  if (e == hipSuccess)
-    e = hipMemcpy(bk->d_inv_freq, inv_freq, sizeof(inv_freq), hipMemcpyHostToDevice);
-  if (e != hipSuccess) {
-    (void)hipFree(bk->dev_mem);
-    delete bk;
-    return fail(MSA_EHIP, std::string("uploading bank tables: ") + hipGetErrorString(e));
+    return st;
   }
   if (d->kv_loc == MSA_KV_HOST) {
-    e = host_buffers_reserve(*bk, kHostIdsInitial);
+    hipError_t e = host_buffers_reserve(*bk, kHostIdsInitial);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&bk->copies_done, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&bk->tables_done, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&bk->attn_done, hipEventDisableTiming);
@@ -332,6 +357,35 @@ int msa_bank_create(const msa_bank_desc* d, msa_bank** out) {
   }
   *out = reinterpret_cast<msa_bank*>(bk);
   return MSA_OK;
+}
+
+int msa_bank_append(msa_bank* b, int32_t n_new, const int64_t* doc_len, const int64_t* kv_off) {
+  if (!b) return fail(MSA_EINVAL, "NULL bank");
+  if (n_new < 0 || (n_new > 0 && !doc_len)) return fail(MSA_EINVAL, "n_new / doc_len");
+  if (n_new == 0) return MSA_OK;
+  Bank* bk = reinterpret_cast<Bank*>(b);
+  std::lock_guard<std::mutex> lock(bk->host_mu);
+  Bank saved_tables;  // roll back the host tables if the upload fails
+  saved_tables.doc_len = bk->doc_len;
+  saved_tables.kv_off = bk->kv_off;
+  saved_tables.tok_off = bk->tok_off;
+  saved_tables.chunk_off = bk->chunk_off;
+  const int64_t tok0 = bk->n_tokens, lmax0 = bk->max_doc_len;
+  const int32_t n0 = bk->desc.n_docs;
+  int st = bank_add_docs(bk, n_new, doc_len, kv_off);
+  if (st != MSA_OK) return st;
+  st = bank_upload_tables(bk);
+  if (st != MSA_OK) {
+    bk->doc_len.swap(saved_tables.doc_len);
+    bk->kv_off.swap(saved_tables.kv_off);
+    bk->tok_off.swap(saved_tables.tok_off);
+    bk->chunk_off.swap(saved_tables.chunk_off);
+    bk->n_tokens = tok0;
+    bk->n_chunks = tok0 / kChunk;
+    bk->max_doc_len = lmax0;
+    bk->desc.n_docs = n0;
+  }
+  return st;
 }
 
 int msa_bank_destroy(msa_bank* b) {

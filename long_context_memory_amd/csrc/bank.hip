@@ -243,11 +243,11 @@ hipError_t launch_pool_keys(const Bank& bk, int doc0, int doc1, const void* rv, 
   if (nc == 0) return hipSuccess;
   if (bk.desc.dtype == MSA_BF16)
     hipLaunchKernelGGL(pool_keys_kernel<uint16_t>, dim3((unsigned)nc), dim3(256), 0, s,
-                       (const uint16_t*)rv, c0, bk.desc.h_r, bk.n_chunks,
+                       (const uint16_t*)rv, c0, bk.desc.h_r, bk.chunk_stride,
                        (uint16_t*)bk.desc.kr, bk.desc.inv_norm);
   else
     hipLaunchKernelGGL(pool_keys_kernel<float>, dim3((unsigned)nc), dim3(256), 0, s,
-                       (const float*)rv, c0, bk.desc.h_r, bk.n_chunks, (float*)bk.desc.kr,
+                       (const float*)rv, c0, bk.desc.h_r, bk.chunk_stride, (float*)bk.desc.kr,
                        bk.desc.inv_norm);
   return hipGetLastError();
 }
@@ -259,11 +259,11 @@ hipError_t launch_key_norms(const Bank& bk, int doc0, int doc1, hipStream_t s) {
   const unsigned grid = (unsigned)((rows + 255) / 256);
   if (bk.desc.dtype == MSA_BF16)
     hipLaunchKernelGGL(key_norms_kernel<uint16_t>, dim3(grid), dim3(256), 0, s,
-                       (const uint16_t*)bk.desc.kr, c0, nc, bk.desc.h_r, bk.n_chunks,
+                       (const uint16_t*)bk.desc.kr, c0, nc, bk.desc.h_r, bk.chunk_stride,
                        bk.desc.inv_norm);
   else
     hipLaunchKernelGGL(key_norms_kernel<float>, dim3(grid), dim3(256), 0, s,
-                       (const float*)bk.desc.kr, c0, nc, bk.desc.h_r, bk.n_chunks,
+                       (const float*)bk.desc.kr, c0, nc, bk.desc.h_r, bk.chunk_stride,
                        bk.desc.inv_norm);
   return hipGetLastError();
 }

@@ -26,6 +26,7 @@ struct Bank {
   msa_bank_desc desc;  // host pointers inside are not retained
   int device = 0;
   int64_t n_tokens = 0, n_chunks = 0, max_doc_len = 0;
+  int64_t chunk_stride = 0;  // rows per head of kr / inv_norm (the chunk capacity)
   int32_t n_tiles = 0, n_pieces = 0;
   std::vector<int64_t> doc_len, kv_off, tok_off;  // host copies; tok_off has N+1 entries
   std::vector<int32_t> chunk_off;                 // N+1

@@ -34,7 +34,7 @@ constexpr int kQPerWave = 16;    // queries a wave scores per pass (64 per workg
 template <typename T>
 __global__ __launch_bounds__(256) void route_scan_kernel(
     const T* __restrict__ kr, const float* __restrict__ inv_norm, const float* __restrict__ q,
-    int B, int bg, int h_r, int64_t C, const int32_t* __restrict__ chunk_doc,
+    int B, int bg, int h_r, int64_t C, int64_t Cs, const int32_t* __restrict__ chunk_doc,
     const int32_t* __restrict__ tile_piece0, int P, float* __restrict__ piecemax) {
   // queries bg .. bg + min(64, B - bg) - 1 (one launch per group of 64)
   constexpr bool kBF = sizeof(T) == 2;
@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
   const int tile = blockIdx.x, h = blockIdx.y;
   const int64_t c0 = (int64_t)tile * kRouteTile;
   const int nc = (int)min((int64_t)kRouteTile, C - c0);
-  const T* rows = kr + ((size_t)h * C + c0) * kD;
+  const T* rows = kr + ((size_t)h * Cs + c0) * kD;  // Cs: rows per head (capacity)
 
   // stage the tile: 64 rows x VPR 16-byte vectors; rows past the end of the
   // bank read the last row and are stored as zero
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
   const int my_doc = lane < nc ? chunk_doc[c0 + lane] : -1;
   const int prev_doc = __shfl_up(my_doc, 1, 64);
   const uint64_t starts = __ballot(lane < nc && (lane == 0 || my_doc != prev_doc));
-  const float inv_k = lane < nc ? inv_norm[(size_t)h * C + c0 + lane] : 0.0f;
+  const float inv_k = lane < nc ? inv_norm[(size_t)h * Cs + c0 + lane] : 0.0f;
   const int piece0 = tile_piece0[tile];
   __syncthreads();
 
@@ -325,12 +325,12 @@ hipError_t launch_route_scan(const Bank& bk, const float* q_route, int B, float*
     if (bk.desc.dtype == MSA_BF16)
       hipLaunchKernelGGL(route_scan_kernel<uint16_t>, grid, dim3(256), 0, s,
                          (const uint16_t*)bk.desc.kr, bk.desc.inv_norm, q_route, B, bg,
-                         bk.desc.h_r, bk.n_chunks, bk.d_chunk_doc, bk.d_tile_piece0,
+                         bk.desc.h_r, bk.n_chunks, bk.chunk_stride, bk.d_chunk_doc, bk.d_tile_piece0,
                          bk.n_pieces, piecemax);
     else
       hipLaunchKernelGGL(route_scan_kernel<float>, grid, dim3(256), 0, s,
                          (const float*)bk.desc.kr, bk.desc.inv_norm, q_route, B, bg,
-                         bk.desc.h_r, bk.n_chunks, bk.d_chunk_doc, bk.d_tile_piece0,
+                         bk.desc.h_r, bk.n_chunks, bk.chunk_stride, bk.d_chunk_doc, bk.d_tile_piece0,
                          bk.n_pieces, piecemax);
   }
   return hipGetLastError();

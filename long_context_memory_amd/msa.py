@@ -26,6 +26,7 @@ EXPORTS = [
     "msa_bank_destroy", "msa_bank_get_info", "msa_build_bank", "msa_prepare_local",
     "msa_workspace_bytes", "msa_staging_bytes", "msa_route", "msa_attend", "msa_step",
     "msa_timer_enable", "msa_timer_read", "msa_bank_set_cache", "msa_cache_slot_bytes",
+    "msa_bank_append",
 ]
 MSA_TIMER_ATTENTION, MSA_TIMER_ROUTE = 0, 1
 
@@ -38,7 +39,8 @@ class BankDesc(C.Structure):
     _fields_ = [("dtype", C.c_int), ("n_docs", i32), ("doc_len", C.POINTER(i64)),
                 ("kv_off", C.POINTER(i64)), ("kv_tokens", i64), ("h_r", i32), ("d_r", i32),
                 ("h_kv", i32), ("d", i32), ("rope_base", C.c_double), ("kv_loc", C.c_int),
-                ("kr", vp), ("inv_norm", vp), ("k_store", vp), ("v_store", vp)]
+                ("kr", vp), ("inv_norm", vp), ("k_store", vp), ("v_store", vp),
+                ("chunk_cap", i64)]
 
 
 class BankInfo(C.Structure):
@@ -85,6 +87,8 @@ def _load():
     lib.msa_workspace_bytes.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32]
     lib.msa_staging_bytes.restype = C.c_size_t
     lib.msa_staging_bytes.argtypes = [vp, i32, i32]
+    lib.msa_bank_append.restype = C.c_int
+    lib.msa_bank_append.argtypes = [vp, i32, C.POINTER(i64), C.POINTER(i64)]
     lib.msa_cache_slot_bytes.restype = C.c_size_t
     lib.msa_cache_slot_bytes.argtypes = [vp]
     lib.msa_bank_set_cache.restype = C.c_int
@@ -153,7 +157,8 @@ class Bank:
 
     def __init__(self, doc_len, h_r: int, h_kv: int, dtype="bf16", device="cuda",
                  kv_loc: str = "device", kv_off=None, kv_tokens: Optional[int] = None,
-                 rope_base: float = 10000.0, kr=None, k_store=None, v_store=None):
+                 rope_base: float = 10000.0, kr=None, k_store=None, v_store=None,
+                 chunk_cap: Optional[int] = None, inv_norm=None):
         self.doc_len = [int(x) for x in doc_len]
         self.n_docs = len(self.doc_len)
         self.h_r, self.h_kv, self.d = int(h_r), int(h_kv), 128
@@ -163,10 +168,12 @@ class Bank:
         self.rope_base = float(rope_base)
         T = sum(self.doc_len)
         self.C = T // 256
+        self.chunk_cap = int(chunk_cap) if chunk_cap else self.C
         self.kv_tokens = int(kv_tokens) if kv_tokens is not None else T
         self.kr = kr if kr is not None else torch.empty(
-            (self.h_r, self.C, 128), dtype=self.dtype, device=self.device)
-        self.inv_norm = torch.empty((self.h_r, self.C), dtype=torch.float32, device=self.device)
+            (self.h_r, self.chunk_cap, 128), dtype=self.dtype, device=self.device)
+        self.inv_norm = inv_norm if inv_norm is not None else torch.empty(
+            (self.h_r, self.chunk_cap), dtype=torch.float32, device=self.device)
         n = self.kv_tokens * self.h_kv * 128
         if k_store is None:
             if self.kv_host:
@@ -177,11 +184,13 @@ class Bank:
                 v_store = torch.empty(n, dtype=self.dtype, device=self.device)
         self.k_store, self.v_store = k_store, v_store
         self._dl = (i64 * self.n_docs)(*self.doc_len)
-        self._ko = None if kv_off is None else (i64 * self.n_docs)(*[int(x) for x in kv_off])
+        self.kv_off = None if kv_off is None else [int(x) for x in kv_off]
+        self._ko = None if kv_off is None else (i64 * self.n_docs)(*self.kv_off)
         desc = BankDesc(_dt(self.dtype), self.n_docs, self._dl, self._ko, self.kv_tokens,
                         self.h_r, 128, self.h_kv, 128, float(rope_base),
                         MSA_KV_HOST if self.kv_host else MSA_KV_DEVICE, _ptr(self.kr),
-                        _ptr(self.inv_norm), _ptr(self.k_store), _ptr(self.v_store))
+                        _ptr(self.inv_norm), _ptr(self.k_store), _ptr(self.v_store),
+                        int(chunk_cap or 0))
         h = vp()
         _check(lib.msa_bank_create(C.byref(desc), C.byref(h)), "msa_bank_create")
         self.handle = h
@@ -196,6 +205,24 @@ class Bank:
         inf = BankInfo()
         _check(lib.msa_bank_get_info(self.handle, C.byref(inf)), "msa_bank_get_info")
         return inf
+
+    def append(self, doc_len, kv_off=None):
+        """Add documents after the current ones (their routing keys and K/V
+        then come from build(N, N + len(doc_len), ...) for a device store)."""
+        dl = [int(x) for x in doc_len]
+        arr = (i64 * len(dl))(*dl)
+        ko = None if kv_off is None else (i64 * len(dl))(*[int(x) for x in kv_off])
+        _check(lib.msa_bank_append(self.handle, len(dl), arr, ko), "msa_bank_append")
+        if self.kv_off is not None or kv_off is not None:  # keep an explicit offset table
+            if self.kv_off is None:
+                self.kv_off = [sum(self.doc_len[:n]) for n in range(self.n_docs)]
+            tok = sum(self.doc_len)
+            for i, L in enumerate(dl):
+                self.kv_off.append(int(kv_off[i]) if kv_off is not None else tok)
+                tok += L
+        self.doc_len += dl
+        self.n_docs = len(self.doc_len)
+        self.C = sum(self.doc_len) // 256
 
     # -- build --------------------------------------------------------------
     def build(self, doc0: int, doc1: int, route_vec=None, k_raw=None, v_raw=None, stream=None):
@@ -318,4 +345,60 @@ def fill_host_store(bank: "Bank", slot_len, raw_kv, slots_per_pass: int = 64, st
         bank.v_store[t0 * per_tok:t1 * per_tok].copy_(dev.v_store)
         torch.cuda.synchronize(bank.device)
         del dev, k_raw, v_raw
+
+
+def save_bank(bank: "Bank", path: str):
+    """Persist a bank: its document table, routing keys, key norms and K/V
+    stores (in the store layouts), as a safetensors file."""
+    from safetensors.torch import save_file
+    C = bank.C
+    tensors = {
+        "doc_len": torch.tensor(bank.doc_len, dtype=torch.int64),
+        "kr": bank.kr[:, :C].contiguous().cpu(),
+        "inv_norm": bank.inv_norm[:, :C].contiguous().cpu(),
+        "k_store": bank.k_store.contiguous().cpu(),
+        "v_store": bank.v_store.contiguous().cpu(),
+    }
+    if bank.kv_off is not None:
+        tensors["kv_off"] = torch.tensor(bank.kv_off, dtype=torch.int64)
+    meta = {"format": "msa-bank-1", "h_r": str(bank.h_r), "h_kv": str(bank.h_kv),
+            "dtype": "bf16" if bank.dtype == torch.bfloat16 else "f32",
+            "rope_base": repr(bank.rope_base), "kv_tokens": str(bank.kv_tokens)}
+    save_file(tensors, path, metadata=meta)
+
+
+def load_bank(path: str, device="cuda", kv_loc: str = "device",
+              chunk_cap: Optional[int] = None, kv_tokens: Optional[int] = None) -> "Bank":
+    """Load a bank written by save_bank (safetensors: nothing in the file is
+    executed).  kv_loc "host" puts the K/V stores in pinned host memory;
+    chunk_cap / kv_tokens may reserve room for appending."""
+    from safetensors import safe_open
+    with safe_open(path, framework="pt") as f:
+        meta = f.metadata()
+        if meta.get("format") != "msa-bank-1":
+            raise MSAError(MSA_EINVAL, "not a bank file")
+        doc_len = f.get_tensor("doc_len").tolist()
+        kv_off = f.get_tensor("kv_off").tolist() if "kv_off" in f.keys() else None
+        h_r, h_kv = int(meta["h_r"]), int(meta["h_kv"])
+        dt = _tdt(meta["dtype"])
+        C = sum(doc_len) // 256
+        cap = max(int(chunk_cap or 0), C)
+        kt = max(int(kv_tokens or 0), int(meta["kv_tokens"]))
+        kr = torch.zeros((h_r, cap, 128), dtype=dt, device=device)
+        kr[:, :C].copy_(f.get_tensor("kr"))
+        inv = torch.zeros((h_r, cap), dtype=torch.float32, device=device)
+        inv[:, :C].copy_(f.get_tensor("inv_norm"))
+        n = kt * h_kv * 128
+        ks, vs = f.get_tensor("k_store"), f.get_tensor("v_store")
+        if kv_loc == "host":
+            k_store = torch.zeros(n, dtype=dt, pin_memory=True)
+            v_store = torch.zeros(n, dtype=dt, pin_memory=True)
+        else:
+            k_store = torch.zeros(n, dtype=dt, device=device)
+            v_store = torch.zeros(n, dtype=dt, device=device)
+        k_store[:ks.numel()].copy_(ks)
+        v_store[:vs.numel()].copy_(vs)
+    return Bank(doc_len, h_r, h_kv, meta["dtype"], device, kv_loc=kv_loc, kv_off=kv_off,
+                kv_tokens=kt, rope_base=float(meta["rope_base"]), kr=kr, k_store=k_store,
+                v_store=v_store, chunk_cap=cap if cap > C else None, inv_norm=inv)
 
