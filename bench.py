@@ -136,7 +136,7 @@ def prefill_bench(steps, warmup, splits=0):
     from long_context_memory_amd import msa, synth as S
 
     dev = "cuda"
-    w = S.workload("c3")
+    w = S.workload("prefill_8m")
     log(f"prefill: building {w.name}: {w.n_docs} docs, {w.T} tokens")
     bank = msa.Bank(w.doc_len, w.h_r, w.h_kv, w.dtype, dev, rope_base=w.rope_base)
     step_docs = 1024
@@ -205,7 +205,7 @@ def host_bank_bench(steps, warmup, cache_gb=0.0):
     from long_context_memory_amd import msa, synth as S
 
     dev = "cuda"
-    w = S.workload("c4")
+    w = S.workload("host_100m")
     log(f"host bank: {w.n_docs} docs, {w.T} tokens, {w.host_slots} slots")
     slot_len, kv_off = S.host_slot_layout(w)
     kr = S.keys_direct(w, dev).to(w.torch_dtype).permute(1, 0, 2).contiguous()
@@ -284,7 +284,7 @@ def interleave_bench(steps, warmup):
     from long_context_memory_amd import msa, synth as S
 
     dev = "cuda"
-    w = S.workload("c5")
+    w = S.workload("interleave_32m")
     log(f"interleave: building {w.n_docs} docs, {w.T} tokens")
     bank = msa.Bank(w.doc_len, w.h_r, w.h_kv, w.dtype, dev, rope_base=w.rope_base)
     off = S.doc_token_offsets(w)
@@ -345,11 +345,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=20, help="0 skips the prefill leg")
     ap.add_argument("--prefill-splits", type=int, default=0, help="token splits (0: automatic)")
-    ap.add_argument("--c4-steps", type=int, default=0,
+    ap.add_argument("--host-bank-steps", type=int, default=0,
                     help="also run the 100M-token host-bank leg (0 skips it)")
-    ap.add_argument("--c4-cache-gb", type=float, default=0.0,
+    ap.add_argument("--host-cache-gb", type=float, default=0.0,
                     help="device document cache for the host-bank leg, GB (0: none)")
-    ap.add_argument("--c5-steps", type=int, default=0,
+    ap.add_argument("--interleave-steps", type=int, default=0,
                     help="also run the 3-hop interleave leg over 32 Mi tokens (0 skips it)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
@@ -366,7 +366,7 @@ def main():
     from long_context_memory_amd import msa, synth as S
 
     dev = "cuda"
-    w = S.workload("c2")
+    w = S.workload("decode_1m")
     log(f"building {w.name}: {w.n_docs} docs, {w.T} tokens")
     r = S.route_vectors(w, dev)
     k_raw, v_raw = S.kv_raw(w, dev)
@@ -447,14 +447,14 @@ def main():
         del bank, batches, ws, outs, r, k_raw, v_raw, raw0
         torch.cuda.empty_cache()
         res["prefill"] = prefill_bench(args.prefill_steps, 3, args.prefill_splits)
-    if args.c4_steps > 0:
+    if args.host_bank_steps > 0:
         torch.cuda.empty_cache()
-        res["host_bank"] = host_bank_bench(args.c4_steps, 2)
-        if args.c4_cache_gb > 0:
-            res["host_bank_cached"] = host_bank_bench(args.c4_steps, 2, args.c4_cache_gb)
-    if args.c5_steps > 0:
+        res["host_bank"] = host_bank_bench(args.host_bank_steps, 2)
+        if args.host_cache_gb > 0:
+            res["host_bank_cached"] = host_bank_bench(args.host_bank_steps, 2, args.host_cache_gb)
+    if args.interleave_steps > 0:
         torch.cuda.empty_cache()
-        res["interleave"] = interleave_bench(args.c5_steps, 2)
+        res["interleave"] = interleave_bench(args.interleave_steps, 2)
     print(json.dumps(res))
 
 

@@ -103,40 +103,41 @@ def lognormal_doc_lengths(total_tokens: int, median: int, sigma: float, lo: int,
 
 
 def workload(name: str) -> Workload:
-    """The named workload.  Full-size: c1..c5; small siblings: *_small."""
-    if name == "c1":
-        return Workload("c1", "f32", [1024] * 64, h_r=1, h_kv=2, h_q=8, k=4, B=1, L_loc=512,
+    """The named workload: tiny_f32_64k, decode_1m, prefill_8m, host_100m,
+    interleave_32m (full size) and their small siblings (*_small)."""
+    if name == "tiny_f32_64k":
+        return Workload("tiny_f32_64k", "f32", [1024] * 64, h_r=1, h_kv=2, h_q=8, k=4, B=1, L_loc=512,
                         pos0=1024, plant="pooled_key", seed=1001)
-    if name == "c2":
-        return Workload("c2", "bf16", [512] * 2048, h_r=8, h_kv=8, h_q=32, k=16, B=16,
+    if name == "decode_1m":
+        return Workload("decode_1m", "bf16", [512] * 2048, h_r=8, h_kv=8, h_q=32, k=16, B=16,
                         L_loc=4096, plant="direction", seed=1002)
-    if name == "c3":
-        return Workload("c3", "bf16", [2048] * 4096, h_r=8, h_kv=8, h_q=32, k=16, B=2048,
+    if name == "prefill_8m":
+        return Workload("prefill_8m", "bf16", [2048] * 4096, h_r=8, h_kv=8, h_q=32, k=16, B=2048,
                         L_loc=2048, mode="prefill", block=64, seed=1003)
-    if name == "c4":
-        return Workload("c4", "bf16", [8192] * 12207 + [256], h_r=8, h_kv=8, h_q=32, k=16, B=8,
+    if name == "host_100m":
+        return Workload("host_100m", "bf16", [8192] * 12207 + [256], h_r=8, h_kv=8, h_q=32, k=16, B=8,
                         L_loc=4096, keys_given=True, kv_host=True, host_slots=384, seed=1004)
-    if name == "c5":
+    if name == "interleave_32m":
         lens = lognormal_doc_lengths(32 * 2 ** 20, 4096, 1.0, 1024, 65536, seed=1005)
-        return Workload("c5", "bf16", lens, h_r=1, h_kv=8, h_q=32, k=8, B=64, L_loc=4096,
+        return Workload("interleave_32m", "bf16", lens, h_r=1, h_kv=8, h_q=32, k=8, B=64, L_loc=4096,
                         mode="interleave", hops=3, seed=1005)
     # small siblings: same structure, sizes the oracle finishes in seconds,
     # ragged local contexts
-    if name == "c1_small":
-        return Workload("c1_small", "f32", [1024] * 8, h_r=1, h_kv=2, h_q=8, k=4, B=2,
+    if name == "tiny_f32_small":
+        return Workload("tiny_f32_small", "f32", [1024] * 8, h_r=1, h_kv=2, h_q=8, k=4, B=2,
                         L_loc=77, pos0=1024, plant="pooled_key", seed=2001)
-    if name == "c2_small":
-        return Workload("c2_small", "bf16", [512] * 48, h_r=8, h_kv=8, h_q=32, k=4, B=3,
+    if name == "decode_small":
+        return Workload("decode_small", "bf16", [512] * 48, h_r=8, h_kv=8, h_q=32, k=4, B=3,
                         L_loc=300, plant="direction", seed=2002)
-    if name == "c3_small":
-        return Workload("c3_small", "bf16", [2048] * 12, h_r=8, h_kv=8, h_q=32, k=3, B=192,
+    if name == "prefill_small":
+        return Workload("prefill_small", "bf16", [2048] * 12, h_r=8, h_kv=8, h_q=32, k=3, B=192,
                         L_loc=250, mode="prefill", block=64, seed=2003)
-    if name == "c4_small":
-        return Workload("c4_small", "bf16", [1024] * 23 + [256], h_r=8, h_kv=8, h_q=32, k=4,
+    if name == "host_small":
+        return Workload("host_small", "bf16", [1024] * 23 + [256], h_r=8, h_kv=8, h_q=32, k=4,
                         B=2, L_loc=200, keys_given=True, kv_host=True, host_slots=5, seed=2004)
-    if name == "c5_small":
+    if name == "interleave_small":
         lens = lognormal_doc_lengths(40 * 1024, 1024, 1.0, 256, 8192, seed=2005)
-        return Workload("c5_small", "bf16", lens, h_r=1, h_kv=8, h_q=32, k=3, B=4, L_loc=129,
+        return Workload("interleave_small", "bf16", lens, h_r=1, h_kv=8, h_q=32, k=3, B=4, L_loc=129,
                         mode="interleave", hops=3, seed=2005)
     raise KeyError(name)
 

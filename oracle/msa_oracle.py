@@ -27,7 +27,7 @@ plainest reading of the prose):
 * the MLA/CSA attention article (mlqm.cn), section 6.2: the attention scale
   1/sqrt(head_dim).
 
-Readings where the pages are silent (each is also listed in the design doc):
+Readings where the pages are silent:
 rotate-half RoPE pairing (i, i + d/2) with theta_i = base^(-2i/d); no RoPE on
 routing keys; a document's score is the mean over router heads of the max
 cosine over its chunks; ties in top-k go to the lower document id; query

@@ -45,7 +45,7 @@ def step_case(w, bank):
 
 
 def test_append_matches_full_build(msa):
-    w = S.workload("c2_small")
+    w = S.workload("decode_small")
     full, grown = full_and_grown(msa, w, 17)
     C = w.C
     assert torch.equal(grown.kr[:, :C], full.kr) and torch.equal(grown.inv_norm[:, :C], full.inv_norm)
@@ -74,7 +74,7 @@ def test_append_matches_full_build(msa):
 
 
 def test_append_capacity_errors(msa):
-    w = S.workload("c2_small")
+    w = S.workload("decode_small")
     b = msa.Bank(w.doc_len[:10], w.h_r, w.h_kv, w.dtype, DEV, rope_base=w.rope_base,
                  chunk_cap=w.C, kv_tokens=sum(w.doc_len[:12]))
     with pytest.raises(msa.MSAError, match="kv_tokens"):
@@ -91,7 +91,7 @@ def test_append_capacity_errors(msa):
 
 
 def test_save_load_roundtrip(msa, tmp_path):
-    w = S.workload("c2_small")
+    w = S.workload("decode_small")
     full, _ = full_and_grown(msa, w, 30)
     ref = step_case(w, full)
     path = str(tmp_path / "bank.safetensors")

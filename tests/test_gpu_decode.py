@@ -47,10 +47,10 @@ def decode_case(msa, name):
     return c
 
 
-SMALL = ["c1_small", "c2_small", "c1"]
+SMALL = ["tiny_f32_small", "decode_small", "tiny_f32_64k"]
 
 
-@pytest.mark.parametrize("name", SMALL + ["c2"])
+@pytest.mark.parametrize("name", SMALL + ["decode_1m"])
 def test_bank_build_matches_oracle(msa, name):
     c = decode_case(msa, name)
     w, bank = c["w"], c["bank"]
@@ -71,7 +71,7 @@ def test_bank_build_matches_oracle(msa, name):
             np.testing.assert_allclose(M.np64(kg), k_o, rtol=2.5e-7, atol=1e-30)
 
 
-@pytest.mark.parametrize("name", ["c1_small", "c2_small"])
+@pytest.mark.parametrize("name", ["tiny_f32_small", "decode_small"])
 def test_prepare_local_matches_oracle(msa, name):
     c = decode_case(msa, name)
     w = c["w"]
@@ -91,7 +91,7 @@ def oracle_scores(c, exclude=None):
     return O.cosine_doc_scores(M.np64(c["q_route"]), c["kr_o"], c["inv_o"], w.doc_len, exclude)
 
 
-@pytest.mark.parametrize("name", SMALL + ["c2"])
+@pytest.mark.parametrize("name", SMALL + ["decode_1m"])
 def test_route_matches_oracle(msa, name):
     c = decode_case(msa, name)
     w = c["w"]
@@ -107,7 +107,7 @@ def test_route_matches_oracle(msa, name):
         assert all(int(ids[b, 0]) == c["target_doc"] for b in range(w.B))
 
 
-@pytest.mark.parametrize("name", ["c2_small"])
+@pytest.mark.parametrize("name", ["decode_small"])
 def test_route_exclusion_and_k_equals_n(msa, name):
     c = decode_case(msa, name)
     w = c["w"]
@@ -153,7 +153,7 @@ def oracle_decode(c, ids_gpu, so):
     return np.stack(outs)
 
 
-@pytest.mark.parametrize("name", SMALL + ["c2"])
+@pytest.mark.parametrize("name", SMALL + ["decode_1m"])
 def test_decode_step_matches_oracle(msa, name):
     c = decode_case(msa, name)
     w = c["w"]
@@ -170,7 +170,7 @@ def test_decode_step_matches_oracle(msa, name):
 
 def test_decode_power_wrong_document_is_caught(msa):
     # the tolerance is tight enough to see one swapped document
-    c = decode_case(msa, "c2_small")
+    c = decode_case(msa, "decode_small")
     w = c["w"]
     ids, scores, out, _ = c["bank"].step(c["q"], w.q_pos, w.k, c["k_loc"], c["v_loc"], c["L"],
                                          q_route=c["q_route"])
@@ -183,7 +183,7 @@ def test_decode_power_wrong_document_is_caught(msa):
         M.check_out(out[0].cpu().numpy(), ref_bad, w.dtype, "power")
 
 
-@pytest.mark.parametrize("name", ["c1_small", "c2_small"])
+@pytest.mark.parametrize("name", ["tiny_f32_small", "decode_small"])
 def test_decode_splits_and_determinism(msa, name):
     c = decode_case(msa, name)
     w = c["w"]
@@ -203,7 +203,7 @@ def test_decode_splits_and_determinism(msa, name):
 
 @pytest.mark.parametrize("L_loc", [0, 1, 63, 64, 65, 130])
 def test_decode_ragged_and_empty_local(msa, L_loc):
-    c = decode_case(msa, "c2_small")
+    c = decode_case(msa, "decode_small")
     w, bank = c["w"], c["bank"]
     lk, lv = c["lk"][:, :L_loc].contiguous(), c["lv"][:, :L_loc].contiguous()
     k_loc, v_loc, L = bank.prepare_local(lk, lv, w.P0)
@@ -224,7 +224,7 @@ def test_decode_ragged_and_empty_local(msa, L_loc):
 
 
 def test_decode_local_only_and_docs_only(msa):
-    c = decode_case(msa, "c2_small")
+    c = decode_case(msa, "decode_small")
     w, bank = c["w"], c["bank"]
     q = M.np64(c["q"])
     # k = 0: attention over the local context alone

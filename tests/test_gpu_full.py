@@ -51,7 +51,7 @@ def pick(ids_gpu_row, oracle_scores_row, k):
 
 
 def test_prefill_full_sampled(msa):
-    w = S.workload("c3")
+    w = S.workload("prefill_8m")
     bank = build_sliced(msa, w, 512)
     q = S.queries(w, DEV)
     rt = S.prefill_route_tokens(w, DEV)
@@ -80,7 +80,7 @@ def test_prefill_full_sampled(msa):
 
 
 def test_host_bank_full_sampled(msa):
-    w = S.workload("c4")
+    w = S.workload("host_100m")
     slot_len, kv_off = S.host_slot_layout(w)
     kr = S.keys_direct(w, DEV).to(w.torch_dtype)
     bank = msa.Bank(w.doc_len, w.h_r, w.h_kv, w.dtype, DEV, kv_loc="host", kv_off=kv_off,
@@ -119,7 +119,7 @@ def test_host_bank_full_sampled(msa):
 
 
 def test_interleave_full_sampled(msa):
-    w = S.workload("c5")
+    w = S.workload("interleave_32m")
     bank = build_sliced(msa, w, 256)
     q = S.queries(w, DEV)
     q_route = S.route_queries(w, DEV)

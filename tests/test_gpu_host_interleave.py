@@ -57,13 +57,13 @@ def host_doc_kv(c, n):
 
 
 def test_host_bank_norms(msa):
-    c = host_case(msa, "c4_small")
+    c = host_case(msa, "host_small")
     inv = M.np64(c["bank"].inv_norm.t())
     np.testing.assert_allclose(inv, c["inv_o"], rtol=2e-7, atol=0)
 
 
 def test_host_bank_step_matches_oracle(msa):
-    c = host_case(msa, "c4_small")
+    c = host_case(msa, "host_small")
     w, bank = c["w"], c["bank"]
     ids, scores, out, st = bank.step(c["q"], w.q_pos, w.k, c["k_loc"], c["v_loc"], c["L"],
                                      q_route=c["q_route"])
@@ -92,7 +92,7 @@ def test_host_bank_step_matches_oracle(msa):
 def test_host_bank_equals_device_bank(msa):
     """The same stores resident on the device give bit-identical results:
     staging changes where the kernels read, not what they compute."""
-    c = host_case(msa, "c4_small")
+    c = host_case(msa, "host_small")
     w, hb = c["w"], c["bank"]
     db = msa.Bank(w.doc_len, w.h_r, w.h_kv, w.dtype, DEV, kv_loc="device", kv_off=c["kv_off"],
                   kv_tokens=hb.kv_tokens, rope_base=w.rope_base, kr=hb.kr,
@@ -109,7 +109,7 @@ def test_host_bank_equals_device_bank(msa):
 
 def test_host_bank_copy_stream(msa):
     """Copies on a separate stream, ordered before the attention by an event."""
-    c = host_case(msa, "c4_small")
+    c = host_case(msa, "host_small")
     w, bank = c["w"], c["bank"]
     args = (c["q"], w.q_pos, w.k, c["k_loc"], c["v_loc"], c["L"])
     _, _, ref, _ = bank.step(*args, q_route=c["q_route"])
@@ -123,7 +123,7 @@ def test_host_bank_concurrent_steps(msa):
     """Two threads stepping one host-resident bank on their own streams,
     workspaces and staging buffers: every result equals the serial one."""
     import threading
-    c = host_case(msa, "c4_small")
+    c = host_case(msa, "host_small")
     w, bank = c["w"], c["bank"]
     args = (c["q"], w.q_pos, w.k, c["k_loc"], c["v_loc"], c["L"])
     _, _, ref, _ = bank.step(*args, q_route=c["q_route"])
@@ -170,7 +170,7 @@ def test_host_cache_identical_results_and_counts(msa):
     gives bit-identical results to the uncached copy path; every step's
     distinct documents are either hits or copies, and a repeated batch is
     served from the cache alone."""
-    c = host_case(msa, "c4_small")
+    c = host_case(msa, "host_small")
     w, bank = c["w"], c["bank"]
     batches = host_batches(c, 3)
     ref = []
@@ -203,7 +203,7 @@ def test_host_cache_identical_results_and_counts(msa):
 
 
 def test_host_cache_too_small_for_a_step(msa):
-    c = host_case(msa, "c4_small")
+    c = host_case(msa, "host_small")
     w, bank = c["w"], c["bank"]
     cache = torch.empty(2 * bank.cache_slot_bytes(), dtype=torch.uint8, device=DEV)
     bank.set_cache(cache)
@@ -214,7 +214,7 @@ def test_host_cache_too_small_for_a_step(msa):
         bank.set_cache(None)
     with pytest.raises(msa.MSAError):
         bank.set_cache(torch.empty(16, dtype=torch.uint8, device=DEV))  # smaller than a slot
-    dev_bank = interleave_case(msa, "c5_small")["bank"]
+    dev_bank = interleave_case(msa, "interleave_small")["bank"]
     with pytest.raises(msa.MSAError):  # device-resident banks take no cache
         dev_bank.set_cache(torch.empty(dev_bank.cache_slot_bytes(), dtype=torch.uint8, device=DEV))
 
@@ -223,7 +223,7 @@ def test_host_cache_concurrent_streams(msa):
     """Two threads stepping one cached host bank on their own streams and
     workspaces (evictions fenced against the other's attention)."""
     import threading
-    c = host_case(msa, "c4_small")
+    c = host_case(msa, "host_small")
     w, bank = c["w"], c["bank"]
     batches = host_batches(c, 3)
     refs = []
@@ -307,7 +307,7 @@ def oracle_hop(c, qr, excl, ids_gpu):
 def test_interleave_teacher_forced(msa, exclude_selected):
     """Each hop against the oracle, the oracle's hop h + 1 taking the GPU's
     hop-h output (and, with exclusion, the GPU's earlier selections)."""
-    c = interleave_case(msa, "c5_small")
+    c = interleave_case(msa, "interleave_small")
     w = c["w"]
     ids, scores, out, _ = c["bank"].step(c["q"], w.q_pos, w.k, c["k_loc"], c["v_loc"], c["L"],
                                          q_route=c["q_route"], hops=w.hops, w_proj=c["wp"],
@@ -330,7 +330,7 @@ def test_interleave_teacher_forced(msa, exclude_selected):
 def test_interleave_free_running(msa):
     """The oracle running its own hops selects the same documents (barring a
     near-tie at some hop, which is reported)."""
-    c = interleave_case(msa, "c5_small")
+    c = interleave_case(msa, "interleave_small")
     w = c["w"]
     ids, _, out, _ = c["bank"].step(c["q"], w.q_pos, w.k, c["k_loc"], c["v_loc"], c["L"],
                                     q_route=c["q_route"], hops=w.hops, w_proj=c["wp"])
@@ -352,7 +352,7 @@ def test_interleave_free_running(msa):
 
 def test_interleave_hop1_equals_single_step(msa):
     """Hop 1 of a multi-hop step is exactly the single-hop step."""
-    c = interleave_case(msa, "c5_small")
+    c = interleave_case(msa, "interleave_small")
     w = c["w"]
     args = (c["q"], w.q_pos, w.k, c["k_loc"], c["v_loc"], c["L"])
     ids3, sc3, out3, _ = c["bank"].step(*args, q_route=c["q_route"], hops=w.hops, w_proj=c["wp"])

@@ -66,7 +66,7 @@ def oracle_block(c, kr_o, inv_o, blk, ids_gpu, queries=None):
 
 
 def test_prefill_small_matches_oracle(msa):
-    w = S.workload("c3_small")
+    w = S.workload("prefill_small")
     c = run_prefill(msa, w)
     kr_o, inv_o = M.pool_oracle(w, c["r"])
     nb = w.B // w.block
@@ -81,7 +81,7 @@ def test_prefill_small_matches_oracle(msa):
 
 
 def test_prefill_splits_agree(msa):
-    w = S.workload("c3_small")
+    w = S.workload("prefill_small")
     a = run_prefill(msa, w, splits=1)["out"]
     b = run_prefill(msa, w, splits=5)["out"]
     scale = float(a.abs().max())
@@ -90,7 +90,7 @@ def test_prefill_splits_agree(msa):
 
 def test_prefill_vector_path_g2(msa):
     # h_q / h_kv = 2 takes the per-query vector kernel
-    w = dataclasses.replace(S.workload("c3_small"), h_q=16, name="c3_small_g2")
+    w = dataclasses.replace(S.workload("prefill_small"), h_q=16, name="prefill_small_g2")
     c = run_prefill(msa, w)
     kr_o, inv_o = M.pool_oracle(w, c["r"])
     out = c["out"].cpu().numpy()
