@@ -62,8 +62,11 @@ def round_to_bf16(x):
 
 
 def round_to_storage(x, dtype: str):
-    """Round to the bank's storage dtype ("f32" or "bf16"); float64 out."""
+    """Round to the bank's storage dtype ("f32" or "bf16"; "f64" keeps the
+    value, for exact identities in the pins); float64 out."""
     x = np.asarray(x, dtype=np.float64)
+    if dtype == "f64":
+        return x
     if dtype == "f32":
         return x.astype(np.float32).astype(np.float64)
     if dtype == "bf16":
@@ -196,13 +199,17 @@ def select_topk(scores, k: int):
 # --------------------------------------------------------------------------
 # a7 / a8: softmax attention over the union
 # --------------------------------------------------------------------------
-def softmax_attention(q, keys, values, scale, mask=None):
-    """out[i] = sum_j softmax_j(q[i] . keys[j] * scale) values[j].
+def softmax_attention(q, keys, values, scale, mask=None, bias=None):
+    """out[i] = sum_j softmax_j(q[i] . keys[j] * scale + bias[j]) values[j].
 
     q: [M, d]; keys: [L, d]; values: [L, dv]; mask: optional bool [M, L]
-    (True = attend).  Max-subtracted float64 softmax."""
+    (True = attend); bias: optional [L] log-weights of the keys (a key that
+    stands for n identical tokens has bias ln n).  Max-subtracted float64
+    softmax."""
     q = np.asarray(q, dtype=np.float64)
     s = (q @ np.asarray(keys, dtype=np.float64).T) * scale
+    if bias is not None:
+        s = s + np.asarray(bias, dtype=np.float64)[None, :]
     if mask is not None:
         s = np.where(mask, s, -np.inf)
     s = s - s.max(axis=1, keepdims=True)
@@ -211,11 +218,12 @@ def softmax_attention(q, keys, values, scale, mask=None):
     return p @ np.asarray(values, dtype=np.float64)
 
 
-def gqa_attention(q, keys, values, mask=None):
+def gqa_attention(q, keys, values, mask=None, bias=None):
     """Grouped-query attention with the 1/sqrt(d) scale.
 
     q: [M, H_q, d]; keys/values: [L, H_kv, d]; query head hq reads KV head
-    hq // (H_q / H_kv).  mask: optional bool [M, L].  Returns [M, H_q, d]."""
+    hq // (H_q / H_kv).  mask: optional bool [M, L]; bias: optional [L]
+    key log-weights (see softmax_attention).  Returns [M, H_q, d]."""
     q = np.asarray(q, dtype=np.float64)
     M, Hq, d = q.shape
     Hkv = keys.shape[1]
@@ -224,7 +232,7 @@ def gqa_attention(q, keys, values, mask=None):
     for hq in range(Hq):
         h = hq // G
         out[:, hq, :] = softmax_attention(q[:, hq, :], keys[:, h, :], values[:, h, :],
-                                          1.0 / np.sqrt(d), mask)
+                                          1.0 / np.sqrt(d), mask, bias)
     return out
 
 
@@ -309,3 +317,49 @@ def interleave_project(out, w):
     Returns [B, 1, d_r]."""
     o = np.asarray(out, dtype=np.float64).reshape(out.shape[0], -1)
     return (o @ np.asarray(w, dtype=np.float64).T)[:, None, :]
+
+
+# --------------------------------------------------------------------------
+# compressed (pooled) memory: attention over chunk means of the selected
+# documents' K/V
+# --------------------------------------------------------------------------
+def pooled_kv(k_rot, v, doc_len, dtype: str):
+    """The compressed memory of a bank: each 256-token chunk of every document
+    becomes one entry, the mean of its stored (document-RoPE'd) keys and the
+    mean of its values, rounded to the storage dtype -- the chunk-mean
+    pooling of the intelliparadigm.com article (section 3.1, "KV cache
+    compression") applied to K and V.
+
+    k_rot, v: [T, H_kv, d] stored K (rotated, rounded) and V; returns
+    ([C, H_kv, d], [C, H_kv, d])."""
+    return (round_to_storage(chunk_mean_pool(k_rot, doc_len), dtype),
+            round_to_storage(chunk_mean_pool(v, doc_len), dtype))
+
+
+def pooled_decode_step(q, q_pos, q_route, keys, inv_norm, pool_k, pool_v, doc_len,
+                       local_k_raw, local_v, local_pos0, k, base, dtype, exclude=None):
+    """Decode with a compressed memory: route and select as decode_step, then
+    attend over the selected documents' pooled entries (rank order, each
+    with the log-weight ln 256 of the 256 tokens it stands for) followed by
+    the local context's tokens.
+
+    pool_k, pool_v: [C, H_kv, d] from pooled_kv.  Other arguments as in
+    decode_step.  Returns (out [B, H_q, d], ids [B, k], scores [B, k])."""
+    scores = cosine_doc_scores(q_route, keys, inv_norm, doc_len, exclude)
+    ids, vals = select_topk(scores, k)
+    off = chunk_offsets(doc_len)
+    B = q.shape[0]
+    out = np.empty(q.shape, dtype=np.float64)
+    for b in range(B):
+        L = local_k_raw.shape[1]
+        lk = round_to_storage(
+            rope_rotate(local_k_raw[b], (local_pos0 + np.arange(L))[:, None], base), dtype)
+        pk = [pool_k[off[n]:off[n + 1]] for n in ids[b] if n >= 0]
+        pv = [pool_v[off[n]:off[n + 1]] for n in ids[b] if n >= 0]
+        n_pool = sum(x.shape[0] for x in pk)
+        K = np.concatenate(pk + [lk])
+        V = np.concatenate(pv + [local_v[b]])
+        bias = np.concatenate([np.full(n_pool, np.log(CHUNK)), np.zeros(L)])
+        qr = rope_rotate(q[b][None], np.full((1, q.shape[1]), q_pos), base)
+        out[b] = gqa_attention(qr, K, V, None, bias)[0]
+    return out, ids, vals

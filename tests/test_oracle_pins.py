@@ -347,3 +347,86 @@ def test_block_mean_and_projection_brute_force():
         flat = [out[b, h, a] for h in range(4) for a in range(5)]
         for j in range(3):
             assert abs(p[b, 0, j] - math.fsum(w[j, i] * flat[i] for i in range(20))) < 1e-13
+
+
+# ---------------------------------------------------------------- compressed memory
+def test_pooled_kv_brute_force():
+    rng = np.random.default_rng(71)
+    doc_len = [512, 256]
+    k = rng.standard_normal((768, 2, 4))
+    v = rng.standard_normal((768, 2, 4))
+    pk, pv = O.pooled_kv(k, v, doc_len, "f64")
+    assert pk.shape == (3, 2, 4)
+    for c in range(3):
+        for h in range(2):
+            for i in range(4):
+                assert math.isclose(pk[c, h, i], math.fsum(k[256 * c:256 * (c + 1), h, i]) / 256,
+                                    rel_tol=0, abs_tol=1e-15)
+                assert math.isclose(pv[c, h, i], math.fsum(v[256 * c:256 * (c + 1), h, i]) / 256,
+                                    rel_tol=0, abs_tol=1e-15)
+
+
+def test_pooled_attention_equals_full_when_chunks_are_constant():
+    """If every token of a chunk has the same key and value, one pooled
+    entry with log-weight ln 256 is exactly the chunk's 256 tokens."""
+    rng = np.random.default_rng(72)
+    C, H, d = 3, 2, 8
+    kc = rng.standard_normal((C, H, d))
+    vc = rng.standard_normal((C, H, d))
+    K = np.repeat(kc, 256, axis=0)
+    V = np.repeat(vc, 256, axis=0)
+    q = rng.standard_normal((5, 4, d))
+    full = O.gqa_attention(q, K, V)
+    pk, pv = O.pooled_kv(K, V, [256 * C], "f64")
+    np.testing.assert_allclose(pk, kc, rtol=1e-14, atol=0)  # a few ulps of summation
+    pooled = O.gqa_attention(q, pk, pv, None, np.full(C, np.log(256)))
+    np.testing.assert_allclose(pooled, full, rtol=0, atol=1e-12)
+    # without the log-weight the local tokens would be over-weighted
+    loc_k = rng.standard_normal((7, H, d))
+    loc_v = rng.standard_normal((7, H, d))
+    full2 = O.gqa_attention(q, np.concatenate([K, loc_k]), np.concatenate([V, loc_v]))
+    pooled2 = O.gqa_attention(q, np.concatenate([pk, loc_k]), np.concatenate([pv, loc_v]), None,
+                              np.concatenate([np.full(C, np.log(256)), np.zeros(7)]))
+    np.testing.assert_allclose(pooled2, full2, rtol=0, atol=1e-12)
+    unweighted = O.gqa_attention(q, np.concatenate([pk, loc_k]), np.concatenate([pv, loc_v]))
+    assert np.abs(unweighted - full2).max() > 1e-3
+
+
+def test_attention_bias_is_a_log_weight():
+    """A bias of ln n on a key equals n copies of it."""
+    rng = np.random.default_rng(73)
+    q = rng.standard_normal((3, 6))
+    K = rng.standard_normal((4, 6))
+    V = rng.standard_normal((4, 5))
+    rep = O.softmax_attention(q, np.concatenate([K, np.repeat(K[1:2], 4, axis=0)]),
+                              np.concatenate([V, np.repeat(V[1:2], 4, axis=0)]), 0.3)
+    b = np.zeros(4)
+    b[1] = np.log(5)
+    np.testing.assert_allclose(O.softmax_attention(q, K, V, 0.3, None, b), rep, rtol=0, atol=1e-12)
+
+
+def test_pooled_decode_step_reduces_to_decode_step_on_constant_chunks():
+    """End to end: with chunk-constant bank K/V, the compressed decode step
+    equals the per-token decode step (routing identical, attention equal)."""
+    rng = np.random.default_rng(74)
+    doc_len = [512, 256, 768]
+    T, C = sum(doc_len), sum(doc_len) // 256
+    H_kv, H_q, d, L = 2, 4, 8, 5
+    kc = rng.standard_normal((C, H_kv, d))
+    vc = rng.standard_normal((C, H_kv, d))
+    bank_k = np.repeat(kc, 256, axis=0)
+    bank_v = np.repeat(vc, 256, axis=0)
+    keys = rng.standard_normal((C, 1, d))
+    inv = O.inverse_norms(keys)
+    q = rng.standard_normal((2, H_q, d))
+    qr = rng.standard_normal((2, 1, d))
+    lk = rng.standard_normal((2, L, H_kv, d))
+    lv = rng.standard_normal((2, L, H_kv, d))
+    a, ia, _ = O.decode_step(q, 900, qr, keys, inv, bank_k, bank_v, doc_len, lk, lv, 890, 2,
+                             10000.0, "f64")
+    pk, pv = O.pooled_kv(bank_k, bank_v, doc_len, "f64")
+    b, ib, _ = O.pooled_decode_step(q, 900, qr, keys, inv, pk, pv, doc_len, lk, lv, 890, 2,
+                                    10000.0, "f64")
+    np.testing.assert_array_equal(ia, ib)
+    np.testing.assert_allclose(b, a, rtol=0, atol=1e-12)
+
