@@ -345,6 +345,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=20, help="0 skips the prefill leg")
     ap.add_argument("--prefill-splits", type=int, default=0, help="token splits (0: automatic)")
+    ap.add_argument("--pooled-steps", type=int, default=0,
+                    help="also time compressed-memory decode on the same bank (0 skips it)")
     ap.add_argument("--host-bank-steps", type=int, default=0,
                     help="also run the 100M-token host-bank leg (0 skips it)")
     ap.add_argument("--host-cache-gb", type=float, default=0.0,
@@ -443,6 +445,50 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(w, r, k_raw, v_raw, raw0)
+    if args.pooled_steps > 0:
+        # compressed memory on the same bank: per-chunk means of the selected
+        # documents' K/V (one log-weighted entry per 256 tokens) + local tokens
+        log("pooled-memory decode")
+        bank.attach_pooled()
+        torch.cuda.synchronize()
+        tb = time.perf_counter()
+        bank.build_pooled(0, w.n_docs)
+        torch.cuda.synchronize()
+        pool_build_s = time.perf_counter() - tb
+
+        def pstep(i):
+            si = i % len(streams)
+            q, q_route, k_loc, v_loc, L = batches[i % args.batches]
+            bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=q_route, ws=ws[si],
+                      outputs=outs[i % args.batches], stream=streams[si],
+                      memory=msa.MSA_MEMORY_POOLED)
+
+        for i in range(args.warmup):
+            pstep(i)
+        torch.cuda.synchronize()
+        msa.timer_enable(True)
+        msa.timer_read(msa.MSA_TIMER_ATTENTION)
+        t0 = time.perf_counter()
+        for i in range(args.pooled_steps):
+            pstep(i)
+        torch.cuda.synchronize()
+        pdt = time.perf_counter() - t0
+        pms, pn = msa.timer_read(msa.MSA_TIMER_ATTENTION)
+        msa.timer_enable(False)
+        entries = w.k * (512 // 256)
+        # bytes: the pooled K rows and V entries of 16 documents + the local K/V
+        pbytes = w.B * (entries + w.L_loc) * w.h_kv * 128 * 2 * 2
+        patt = pms * 1e-3 / max(pn, 1)
+        res["pooled"] = {"workload": "compressed-memory decode on the 1M-token bank: the 16 "
+                                     "selected documents as 2 chunk-mean entries each "
+                                     "(log-weighted) + 4096 local tokens, B=16",
+                         "queries_per_s": w.B * args.pooled_steps / pdt,
+                         "ms_per_step": pdt * 1e3 / args.pooled_steps,
+                         "pooled_build_s": pool_build_s,
+                         "attention": {"bound": "hbm", "bytes_per_launch": pbytes,
+                                       "avg_launch_us": patt * 1e6,
+                                       "achieved": pbytes / patt / 1e9, "peak": HBM_PEAK_GBS,
+                                       "unit": "GB/s", "frac": pbytes / patt / 1e9 / HBM_PEAK_GBS}}
     if args.prefill_steps > 0:
         del bank, batches, ws, outs, r, k_raw, v_raw, raw0
         torch.cuda.empty_cache()

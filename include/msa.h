@@ -81,6 +81,10 @@ typedef enum {
 typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype;
 typedef enum { MSA_KV_DEVICE = 0, MSA_KV_HOST = 1 } msa_kv_loc;
 typedef enum { MSA_DECODE = 0, MSA_PREFILL = 1 } msa_mode;
+/* What the attention reads of each selected document: its per-token K/V,
+ * or its compressed memory (one log-weighted entry per 256-token chunk, see
+ * msa_bank_set_pooled). */
+typedef enum { MSA_MEMORY_TOKENS = 0, MSA_MEMORY_POOLED = 1 } msa_memory;
 
 typedef struct msa_bank msa_bank;
 
@@ -146,6 +150,7 @@ typedef struct {
   const int64_t* src_off;    /* device [n_src] token offsets */
   const int32_t* src_len;    /* device [n_src] token lengths */
   int32_t n_src;             /* entries in src_off / src_len */
+  int32_t memory;            /* msa_memory: MSA_MEMORY_TOKENS, or MSA_MEMORY_POOLED (decode) */
 } msa_attend_args;
 
 /* One step of the path: route -> top-k -> gather -> attend, repeated for
@@ -178,6 +183,8 @@ typedef struct {
   void* staging;             /* host banks: device staging for copied documents */
   size_t staging_bytes;
   int32_t splits;
+  int32_t memory;            /* msa_memory, as in msa_attend_args; pooled memory needs no
+                                host->device copies, so staging is unused */
 } msa_step_args;
 
 typedef struct {
@@ -269,6 +276,25 @@ int msa_route(const msa_bank* bank, const float* q_route, int32_t B, int32_t k,
  * query i of group g = i / block sees group g's documents and local tokens
  * j <= L_loc - n_q + i (the queries are the last n_q local tokens). */
 int msa_attend(const msa_bank* bank, const msa_attend_args* args, void* stream);
+
+/* Compressed memory (intelliparadigm.com, section 3.1: chunk-mean pooling
+ * as KV-cache compression; "MSA" card, "Komponenty": a compressed memory
+ * bank).  Each 256-token chunk of a document becomes one entry: the mean of
+ * its stored (document-RoPE'd) K and the mean of its V, rounded to dtype.
+ * With memory = MSA_MEMORY_POOLED a decode attends over its selected
+ * documents' entries -- each scored with an extra ln 256, the log of the 256
+ * tokens it stands for -- followed by the local context's tokens.
+ *   msa_pooled_sizes: elements (of dtype) the two pooled stores hold.
+ *   msa_bank_set_pooled: attach caller-owned device stores (NULL detaches):
+ *     pool_k per document n at entry chunk_first(n): [h_kv][P_n][d]
+ *     (P_n = doc_len[n] / 256); pool_v per document [h_kv][ceil(P_n/64)][d][64]
+ *     (tile-blocked, zero-padded) at the running sum of 64-padded P.
+ *     msa_bank_append detaches them (sizes grow).
+ *   msa_build_pooled: fill the pooled stores of documents [doc0, doc1) from
+ *     the bank's device K/V stores (device-resident banks).  Asynchronous. */
+int msa_pooled_sizes(const msa_bank* bank, int64_t* k_elems, int64_t* v_elems);
+int msa_bank_set_pooled(msa_bank* bank, void* pool_k, void* pool_v);
+int msa_build_pooled(const msa_bank* bank, int32_t doc_begin, int32_t doc_end, void* stream);
 
 /* Device (HBM) document cache of a host-resident bank (intelliparadigm.com,
  * section 5.2: keep frequently used memory in HBM; "MSA" card, "Pułapki

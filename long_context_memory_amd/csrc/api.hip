@@ -104,11 +104,22 @@ constexpr int kMaxSplits = 256;
 // Splits of the attention kernels: the MFMA prefill takes any count, the
 // split-K decode kernel (and the vector prefill) multiples of 4.
 int resolve_splits(const Bank& bk, int mode, int splits, int n_q, int h_q, int block, int k,
-                   int L_loc) {
+                   int L_loc, bool pooled = false) {
   if (mode == MSA_PREFILL && prefill_mfma_supported(bk, n_q, h_q, block))
     return splits > 0 ? splits : prefill_auto_splits(bk, n_q, k, L_loc);
   if (splits > 0) return ((splits + 3) / 4) * 4;
-  return decode_auto_splits(bk, n_q, k, L_loc);
+  const double avg_doc = (double)bk.n_tokens / bk.desc.n_docs;
+  // expected 64-entry tiles per selected document
+  const double doc_tiles = pooled ? std::ceil(avg_doc / kChunk / kAttnTile) : avg_doc / kAttnTile;
+  return decode_auto_splits(bk, n_q, k, L_loc, doc_tiles);
+}
+
+// The compressed-memory sources: pooled entries, 64-padded V, ln 256 each
+AttnSources pooled_sources(const Bank& bk) {
+  AttnSources src{bk.pool_k, bk.pool_v, bk.d_pool_off, bk.d_pool_len, bk.desc.n_docs};
+  src.voff = bk.d_pool_voff;
+  src.bias = 8.0f;  // log2(256): scores are in log2 units
+  return src;
 }
 
 const Bank* as_bank(const msa_bank* b) { return reinterpret_cast<const Bank*>(b); }
@@ -172,7 +183,7 @@ const char* msa_status_string(int status) {
 
 const char* msa_last_error(void) { return g_last_error.c_str(); }
 
-int msa_version(void) { return 10100; }
+int msa_version(void) { return 10200; }
 
 int msa_timer_enable(int on) {
   g_timer.on = on != 0;
@@ -269,8 +280,15 @@ int bank_upload_tables(Bank* bk) {
   }
   tile_piece0[n_tiles] = piece;
   for (int m = last_doc + 1; m <= N; ++m) doc_piece0[m] = piece;
-  std::vector<int32_t> dl32(N);
-  for (int n = 0; n < N; ++n) dl32[n] = (int32_t)bk->doc_len[n];
+  std::vector<int32_t> dl32(N), plen(N);
+  std::vector<int64_t> poff(N), pvoff(N + 1);
+  pvoff[0] = 0;
+  for (int n = 0; n < N; ++n) {
+    dl32[n] = (int32_t)bk->doc_len[n];
+    plen[n] = (int32_t)(bk->doc_len[n] / kChunk);
+    poff[n] = bk->chunk_off[n];
+    pvoff[n + 1] = pvoff[n] + (plen[n] + kAttnTile - 1) / kAttnTile * kAttnTile;
+  }
   double inv_freq[kD / 2];
   for (int i = 0; i < kD / 2; ++i) inv_freq[i] = std::pow(bk->desc.rope_base, -2.0 * i / kD);
 
@@ -282,7 +300,8 @@ int bank_upload_tables(Bank* bk) {
   };
   const size_t o_dl = take(N * 4), o_kv = take(N * 8), o_tok = take((N + 1) * 8),
                o_cd = take(C * 4), o_tp = take((n_tiles + 1) * 4),
-               o_dp = take((N + 1) * 4), o_if = take(sizeof(inv_freq));
+               o_dp = take((N + 1) * 4), o_if = take(sizeof(inv_freq)),
+               o_po = take(N * 8), o_pl = take(N * 4), o_pv = take(N * 8);
   void* mem = nullptr;
   if (hipMalloc(&mem, off) != hipSuccess) return fail(MSA_ENOMEM, "hipMalloc of bank tables failed");
   char* base = (char*)mem;
@@ -294,6 +313,9 @@ int bank_upload_tables(Bank* bk) {
     e = hipMemcpy(base + o_tp, tile_piece0.data(), (n_tiles + 1) * 4, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(base + o_dp, doc_piece0.data(), (N + 1) * 4, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(base + o_if, inv_freq, sizeof(inv_freq), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(base + o_po, poff.data(), N * 8, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(base + o_pl, plen.data(), N * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(base + o_pv, pvoff.data(), N * 8, hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     (void)hipFree(mem);
     return fail(MSA_EHIP, std::string("uploading bank tables: ") + hipGetErrorString(e));
@@ -309,6 +331,10 @@ int bank_upload_tables(Bank* bk) {
   bk->d_tile_piece0 = (int32_t*)(base + o_tp);
   bk->d_doc_piece0 = (int32_t*)(base + o_dp);
   bk->d_inv_freq = (double*)(base + o_if);
+  bk->d_pool_off = (int64_t*)(base + o_po);
+  bk->d_pool_len = (int32_t*)(base + o_pl);
+  bk->d_pool_voff = (int64_t*)(base + o_pv);
+  bk->pool_voff.swap(pvoff);
   return MSA_OK;
 }
 
@@ -374,8 +400,13 @@ int msa_bank_append(msa_bank* b, int32_t n_new, const int64_t* doc_len, const in
   const int32_t n0 = bk->desc.n_docs;
   int st = bank_add_docs(bk, n_new, doc_len, kv_off);
   if (st != MSA_OK) return st;
+  const std::vector<int64_t> pool_voff0 = bk->pool_voff;
   st = bank_upload_tables(bk);
-  if (st != MSA_OK) {
+  if (st == MSA_OK) {
+    bk->pool_k = nullptr;  // the pooled stores' sizes grow: attach them again
+    bk->pool_v = nullptr;
+  } else {
+    bk->pool_voff = pool_voff0;
     bk->doc_len.swap(saved_tables.doc_len);
     bk->kv_off.swap(saved_tables.kv_off);
     bk->tok_off.swap(saved_tables.tok_off);
@@ -494,6 +525,34 @@ int msa_bank_set_cache(msa_bank* b, void* cache, size_t cache_bytes) {
   return MSA_OK;
 }
 
+int msa_pooled_sizes(const msa_bank* b, int64_t* k_elems, int64_t* v_elems) {
+  if (!b || !k_elems || !v_elems) return fail(MSA_EINVAL, "NULL argument");
+  const Bank& bk = *as_bank(b);
+  *k_elems = bk.n_chunks * bk.desc.h_kv * kD;
+  *v_elems = bk.pool_voff.back() * bk.desc.h_kv * kD;
+  return MSA_OK;
+}
+
+int msa_bank_set_pooled(msa_bank* b, void* pool_k, void* pool_v) {
+  if (!b) return fail(MSA_EINVAL, "NULL bank");
+  if ((pool_k == nullptr) != (pool_v == nullptr)) return fail(MSA_EINVAL, "pool_k and pool_v");
+  Bank& bk = *reinterpret_cast<Bank*>(b);
+  bk.pool_k = pool_k;
+  bk.pool_v = pool_v;
+  return MSA_OK;
+}
+
+int msa_build_pooled(const msa_bank* b, int32_t doc0, int32_t doc1, void* stream) {
+  if (!b) return fail(MSA_EINVAL, "NULL bank");
+  const Bank& bk = *as_bank(b);
+  if (doc0 < 0 || doc1 > bk.desc.n_docs || doc0 > doc1) return fail(MSA_EINVAL, "document range");
+  if (!bk.pool_k || !bk.pool_v) return fail(MSA_EINVAL, "no pooled stores attached");
+  if (bk.desc.kv_loc != MSA_KV_DEVICE)
+    return fail(MSA_EUNSUPPORTED, "pooled stores are built from a device-resident store");
+  MSA_CHECK_HIP(launch_pool_kv(bk, doc0, doc1, (hipStream_t)stream));
+  return MSA_OK;
+}
+
 int msa_route(const msa_bank* b, const float* q_route, int32_t B, int32_t k,
               const uint32_t* exclude, int32_t* ids, float* scores, void* ws, size_t ws_bytes,
               void* stream) {
@@ -525,7 +584,15 @@ int msa_attend(const msa_bank* b, const msa_attend_args* a, void* stream) {
   if (!a->q || !a->out || !a->ws || (a->k > 0 && !a->ids)) return fail(MSA_EINVAL, "NULL pointer");
   if (a->q_pos < 0) return fail(MSA_EINVAL, "q_pos < 0");
   AttnSources src{bk.desc.k_store, bk.desc.v_store, bk.d_kv_off, bk.d_doc_len, bk.desc.n_docs};
-  if (a->src_len || a->src_off || a->src_k || a->src_v) {
+  const bool pooled = a->memory == MSA_MEMORY_POOLED;
+  if (a->memory != MSA_MEMORY_TOKENS && !pooled) return fail(MSA_EINVAL, "memory");
+  if (pooled) {
+    if (a->mode != MSA_DECODE) return fail(MSA_EUNSUPPORTED, "pooled memory is a decode mode");
+    if (!bk.pool_k || !bk.pool_v) return fail(MSA_EINVAL, "no pooled stores attached");
+    if (a->src_len || a->src_off || a->src_k || a->src_v)
+      return fail(MSA_EINVAL, "pooled memory takes no source override");
+    src = pooled_sources(bk);
+  } else if (a->src_len || a->src_off || a->src_k || a->src_v) {
     if (!a->src_len || !a->src_off || !a->src_k || !a->src_v || a->n_src < 0)
       return fail(MSA_EINVAL, "source override needs src_k, src_v, src_off, src_len and n_src");
     src = AttnSources{a->src_k, a->src_v, a->src_off, a->src_len, a->n_src};
@@ -534,7 +601,7 @@ int msa_attend(const msa_bank* b, const msa_attend_args* a, void* stream) {
   }
   if (a->splits < 0 || a->splits > kMaxSplits) return fail(MSA_EINVAL, "splits must be in [0, 256]");
   const int splits =
-      resolve_splits(bk, a->mode, a->splits, a->n_q, a->h_q, a->block, a->k, a->L_loc);
+      resolve_splits(bk, a->mode, a->splits, a->n_q, a->h_q, a->block, a->k, a->L_loc, pooled);
   const WsLayout L = ws_layout(bk, a->mode, a->n_q, a->h_q, a->k, a->block, 1, splits);
   if (a->ws_bytes < L.total) return fail(MSA_ENOMEM, "workspace too small for msa_attend");
   char* w = (char*)a->ws;
@@ -574,11 +641,17 @@ int msa_step(const msa_bank* b, const msa_step_args* a, void* stream, void* copy
   if (!a->q || !a->ids || !a->scores || !a->out || !a->ws) return fail(MSA_EINVAL, "NULL pointer");
   if (prefill ? !a->route_tokens : !a->q_route) return fail(MSA_EINVAL, "router input is NULL");
   if (a->q_pos < 0) return fail(MSA_EINVAL, "q_pos < 0");
-  const bool host = bk.desc.kv_loc == MSA_KV_HOST;
+  const bool pooled = a->memory == MSA_MEMORY_POOLED;
+  if (a->memory != MSA_MEMORY_TOKENS && !pooled) return fail(MSA_EINVAL, "memory");
+  if (pooled && a->mode != MSA_DECODE) return fail(MSA_EUNSUPPORTED, "pooled memory is a decode mode");
+  if (pooled && (!bk.pool_k || !bk.pool_v)) return fail(MSA_EINVAL, "no pooled stores attached");
+  // pooled memory lives on the device: no host copies even for a host-resident bank
+  const bool host = bk.desc.kv_loc == MSA_KV_HOST && !pooled;
   const int n_groups = prefill ? a->n_q / a->block : a->n_q;
   const int k = a->k;
   if (a->splits < 0 || a->splits > kMaxSplits) return fail(MSA_EINVAL, "splits must be in [0, 256]");
-  const int splits = resolve_splits(bk, a->mode, a->splits, a->n_q, a->h_q, a->block, k, a->L_loc);
+  const int splits =
+      resolve_splits(bk, a->mode, a->splits, a->n_q, a->h_q, a->block, k, a->L_loc, pooled);
   const WsLayout L = ws_layout(bk, a->mode, a->n_q, a->h_q, k, a->block, a->hops, splits);
   if (a->ws_bytes < L.total) return fail(MSA_ENOMEM, "workspace too small for msa_step");
   const size_t esz = dtype_size(bk.desc.dtype);
@@ -626,7 +699,9 @@ int msa_step(const msa_bank* b, const msa_step_args* a, void* stream, void* copy
     MSA_CHECK_HIP(launch_topk(bk, (const float*)(w + L.piecemax), n_groups, k, excl,
                               a->exclude_selected ? excl : nullptr, ids, scores,
                               (uint64_t*)(w + L.keys), s));
-    AttnSources src{bk.desc.k_store, bk.desc.v_store, bk.d_kv_off, bk.d_doc_len, N};
+    AttnSources src = pooled ? pooled_sources(bk)
+                             : AttnSources{bk.desc.k_store, bk.desc.v_store, bk.d_kv_off,
+                                           bk.d_doc_len, N};
     const int32_t* att_ids = ids;
     if (host) {
       // top-k -> K/V fetch is sequential: read the ids back, then make each

@@ -268,6 +268,75 @@ hipError_t launch_key_norms(const Bank& bk, int doc0, int doc1, hipStream_t s) {
   return hipGetLastError();
 }
 
+namespace {
+
+// Compressed memory: entry j of document n is the mean of the document's
+// chunk j of stored K (already rotated at document positions) and of V
+// (intelliparadigm.com, section 3.1: chunk-mean pooling of the KV cache),
+// accumulated in float64 and rounded once.  One workgroup per (chunk, KV
+// head): 128 channels x 2 halves of the chunk's 256 tokens.
+template <typename T>
+__global__ __launch_bounds__(256) void pool_kv_kernel(
+    const T* __restrict__ ks, const T* __restrict__ vs, const int32_t* __restrict__ chunk_doc,
+    const int32_t* __restrict__ doc_len, const int64_t* __restrict__ kv_off,
+    const int64_t* __restrict__ tok_off, const int64_t* __restrict__ pool_voff, int h_kv,
+    int64_t c0, T* __restrict__ pk, T* __restrict__ pv) {
+  const int64_t c = c0 + blockIdx.x;
+  const int h = blockIdx.y;
+  const int n = chunk_doc[c];
+  const int64_t L = doc_len[n];
+  const int64_t P = L / kChunk;
+  const int64_t cfirst = tok_off[n] / kChunk;
+  const int64_t j = c - cfirst;  // entry (chunk) within the document
+  const int d = threadIdx.x & (kD - 1), half = threadIdx.x >> 7;
+  const int64_t base = (kv_off[n] * h_kv + (int64_t)h * L) * kD;  // this head's block
+  double sk = 0.0, sv = 0.0;
+  for (int t = 128 * half; t < 128 * half + 128; ++t) {
+    const int64_t tt = j * kChunk + t;  // token within the document
+    sk += St<T>::load(ks[base + tt * kD + d]);
+    sv += St<T>::load(vs[base + (tt / kAttnTile) * kD * kAttnTile + d * kAttnTile + tt % kAttnTile]);
+  }
+  __shared__ double red[2][kD];
+  if (half == 1) {
+    red[0][d] = sk;
+    red[1][d] = sv;
+  }
+  __syncthreads();
+  if (half == 0) {
+    sk += red[0][d];
+    sv += red[1][d];
+    pk[(cfirst * h_kv + (int64_t)h * P + j) * kD + d] = St<T>::store(sk / (double)kChunk);
+    const int64_t Pp = (P + kAttnTile - 1) / kAttnTile * kAttnTile;
+    pv[(pool_voff[n] * h_kv + (int64_t)h * Pp) * kD + (j / kAttnTile) * kD * kAttnTile +
+       d * kAttnTile + j % kAttnTile] = St<T>::store(sv / (double)kChunk);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pool_kv(const Bank& bk, int doc0, int doc1, hipStream_t s) {
+  const int64_t c0 = bk.chunk_off[doc0], nc = bk.chunk_off[doc1] - c0;
+  if (nc == 0) return hipSuccess;
+  const size_t esz = dtype_size(bk.desc.dtype);
+  const size_t row = (size_t)bk.desc.h_kv * kD * esz;
+  // V rows past a document's last entry (tile padding) are zero
+  hipError_t e = hipMemsetAsync((char*)bk.pool_v + (size_t)bk.pool_voff[doc0] * row, 0,
+                                (size_t)(bk.pool_voff[doc1] - bk.pool_voff[doc0]) * row, s);
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)nc, (unsigned)bk.desc.h_kv);
+  if (bk.desc.dtype == MSA_BF16)
+    hipLaunchKernelGGL(pool_kv_kernel<uint16_t>, grid, dim3(256), 0, s,
+                       (const uint16_t*)bk.desc.k_store, (const uint16_t*)bk.desc.v_store,
+                       bk.d_chunk_doc, bk.d_doc_len, bk.d_kv_off, bk.d_tok_off, bk.d_pool_voff,
+                       bk.desc.h_kv, c0, (uint16_t*)bk.pool_k, (uint16_t*)bk.pool_v);
+  else
+    hipLaunchKernelGGL(pool_kv_kernel<float>, grid, dim3(256), 0, s,
+                       (const float*)bk.desc.k_store, (const float*)bk.desc.v_store,
+                       bk.d_chunk_doc, bk.d_doc_len, bk.d_kv_off, bk.d_tok_off, bk.d_pool_voff,
+                       bk.desc.h_kv, c0, (float*)bk.pool_k, (float*)bk.pool_v);
+  return hipGetLastError();
+}
+
 hipError_t launch_store_kv(const Bank& bk, int doc0, int doc1, const void* k_raw,
                            const void* v_raw, hipStream_t s) {
   const int64_t ntok = bk.tok_off[doc1] - bk.tok_off[doc0];

@@ -43,6 +43,8 @@ struct DecodeP {
   int id_div;      // queries per id row (decode 1; prefill: the routing block)
   int loc_shared;  // 1: every query reads local sequence 0 (prefill)
   int causal_off;  // < 0: none; else query b sees local tokens j < causal_off + b + 1
+  const int64_t* svoff;  // NULL, or V offsets of padded (64-entry tile) V blocks
+  float doc_bias;        // added to the scores of document entries (log2 units)
   float* part;     // [B][h_kv][S][G][130]: m (log2 units), l, o[128]
 };
 
@@ -94,15 +96,16 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeP p) {
   if ((int)threadIdx.x < k) {
     const int id = p.ids[(size_t)(b / p.id_div) * k + threadIdx.x];
     int L = 0;
-    int64_t off = 0;
+    int64_t off = 0, voff = 0;
     if (id >= 0 && id < p.n_src) {
       L = p.slen[id];
       off = p.soff[id];
+      voff = p.svoff ? p.svoff[id] : off;
     }
-    const int64_t o = (off * p.h_kv + (int64_t)h * L) * kD;
+    const int64_t Lp = p.svoff ? (L + kAttnTile - 1) / kAttnTile * kAttnTile : L;
     s_len[threadIdx.x] = L;
-    s_koff[threadIdx.x] = o;
-    s_voff[threadIdx.x] = o;
+    s_koff[threadIdx.x] = (off * p.h_kv + (int64_t)h * L) * kD;
+    s_voff[threadIdx.x] = (voff * p.h_kv + (int64_t)h * Lp) * kD;
   } else if ((int)threadIdx.x == k) {
     const int64_t seq = p.loc_shared ? 0 : b;
     const int64_t tp = (p.L_loc + kAttnTile - 1) / kAttnTile;  // padded local tiles
@@ -232,9 +235,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeP p) {
 
     // ---- online softmax (base 2; scores are pre-scaled by log2 e)
     const bool tv = tau < nvalid;
+    const float bias = loc ? 0.f : p.doc_bias;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const float sc = tv ? acc[g] : -INFINITY;
+      const float sc = tv ? acc[g] + bias : -INFINITY;
       const float m_new = fmaxf(m_run[g], wave_max(sc));
       const float alpha = exp2f(m_run[g] - m_new);
       const float pe = exp2f(sc - m_new);
@@ -394,7 +398,7 @@ size_t decode_partial_floats(int B, int h_kv, int G, int splits) {
   return (size_t)B * h_kv * splits * G * (kD + 2);
 }
 
-int decode_auto_splits(const Bank& bk, int B, int k, int L_loc) {
+int decode_auto_splits(const Bank& bk, int B, int k, int L_loc, double doc_tiles) {
   // At least one long-running wave per SIMD (1024 waves on 256 CUs): each
   // wave walks a long contiguous run of tiles, which streams best when the
   // unions are of equal length.  With documents of mixed lengths the unions
@@ -402,8 +406,7 @@ int decode_auto_splits(const Bank& bk, int B, int k, int L_loc) {
   // expected union lets short unions' waves finish and make room for the
   // rest of the long ones.  Splits come in multiples of 4 (one workgroup =
   // 4 waves) and never exceed the tiles.
-  const double avg_doc = (double)bk.n_tokens / bk.desc.n_docs;
-  const double tiles = k * avg_doc / kAttnTile + (L_loc + kAttnTile - 1) / kAttnTile;
+  const double tiles = k * doc_tiles + (L_loc + kAttnTile - 1) / kAttnTile;
   const int64_t pairs = std::max<int64_t>(1, (int64_t)B * bk.desc.h_kv);
   int s = (int)((1024 + pairs - 1) / pairs);
   s = std::max(s, (int)std::ceil(tiles / 32.0));
@@ -423,6 +426,8 @@ hipError_t launch_decode(const Bank& bk, const void* q_rot, int B, int h_q, cons
   p.soff = src.off;
   p.slen = src.len;
   p.n_src = src.n;
+  p.svoff = src.voff;
+  p.doc_bias = src.bias;
   p.kl = k_loc;
   p.vl = v_loc;
   p.k = k;
@@ -470,6 +475,8 @@ hipError_t launch_prefill_vector(const Bank& bk, const void* q_rot, int n_q, int
   p.soff = src.off;
   p.slen = src.len;
   p.n_src = src.n;
+  p.svoff = src.voff;
+  p.doc_bias = src.bias;
   p.kl = k_loc;
   p.vl = v_loc;
   p.k = k;

@@ -39,6 +39,14 @@ struct Bank {
   int32_t* d_tile_piece0 = nullptr;  // [n_tiles + 1]
   int32_t* d_doc_piece0 = nullptr;   // [N + 1]
   double* d_inv_freq = nullptr;      // [64]
+  // compressed memory (msa_bank_set_pooled): per document its pooled K
+  // offset (= its first chunk), entry count (chunks) and padded V offset
+  int64_t* d_pool_off = nullptr;     // [N]
+  int32_t* d_pool_len = nullptr;     // [N]
+  int64_t* d_pool_voff = nullptr;    // [N]
+  std::vector<int64_t> pool_voff;    // N+1, host copy (entries, 64-padded per document)
+  void* pool_k = nullptr;            // [C][h_kv][d] in per-document [h_kv][P][d] blocks
+  void* pool_v = nullptr;            // per document [h_kv][ceil(P/64)][d][64], zero-padded
   // host-resident banks: pinned buffers for reading back selected ids and
   // staging the remap tables, and the events that order the copies.  The
   // host part of msa_step holds host_mu while it uses them.
@@ -196,6 +204,7 @@ __device__ __forceinline__ float float_from_order_key(uint32_t k) {
 hipError_t launch_pool_keys(const Bank& bk, int doc0, int doc1, const void* route_vec,
                             hipStream_t s);
 hipError_t launch_key_norms(const Bank& bk, int doc0, int doc1, hipStream_t s);
+hipError_t launch_pool_kv(const Bank& bk, int doc0, int doc1, hipStream_t s);
 hipError_t launch_store_kv(const Bank& bk, int doc0, int doc1, const void* k_raw,
                            const void* v_raw, hipStream_t s);
 hipError_t launch_prepare_local(const Bank& bk, const void* k_raw, const void* v_raw, int n_seq,
@@ -222,7 +231,10 @@ struct AttnSources {
   const void* v;
   const int64_t* off;
   const int32_t* len;
-  int n;  // entries in off / len
+  int n;                          // entries in off / len
+  const int64_t* voff = nullptr;  // V offsets (entries) when V rows are padded to
+                                  // whole 64-entry tiles; NULL: V shares off
+  float bias = 0.f;               // score bias of these entries, log2 units
 };
 hipError_t launch_decode(const Bank& bk, const void* q_rot, int B, int h_q, const int32_t* ids,
                          int k, const AttnSources& src, const void* k_loc, const void* v_loc,
@@ -234,7 +246,7 @@ hipError_t launch_prefill(const Bank& bk, const void* q_rot, int n_q, int h_q, c
 
 // sizes of the attention partial buffers
 size_t decode_partial_floats(int B, int h_kv, int G, int splits);
-int decode_auto_splits(const Bank& bk, int B, int k, int L_loc);
+int decode_auto_splits(const Bank& bk, int B, int k, int L_loc, double doc_tiles);
 size_t prefill_partial_floats(int n_q, int h_kv, int splits);
 int prefill_auto_splits(const Bank& bk, int n_q, int k, int L_loc);
 bool prefill_mfma_supported(const Bank& bk, int n_q, int h_q, int block);

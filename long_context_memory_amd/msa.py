@@ -26,9 +26,10 @@ EXPORTS = [
     "msa_bank_destroy", "msa_bank_get_info", "msa_build_bank", "msa_prepare_local",
     "msa_workspace_bytes", "msa_staging_bytes", "msa_route", "msa_attend", "msa_step",
     "msa_timer_enable", "msa_timer_read", "msa_bank_set_cache", "msa_cache_slot_bytes",
-    "msa_bank_append",
+    "msa_bank_append", "msa_pooled_sizes", "msa_bank_set_pooled", "msa_build_pooled",
 ]
 MSA_TIMER_ATTENTION, MSA_TIMER_ROUTE = 0, 1
+MSA_MEMORY_TOKENS, MSA_MEMORY_POOLED = 0, 1
 
 vp = C.c_void_p
 i32 = C.c_int32
@@ -53,7 +54,7 @@ class AttendArgs(C.Structure):
                 ("ids", vp), ("k", i32), ("block", i32), ("k_loc", vp), ("v_loc", vp),
                 ("L_loc", i32), ("out", vp), ("ws", vp),
                 ("ws_bytes", C.c_size_t), ("splits", i32), ("src_k", vp), ("src_v", vp),
-                ("src_off", vp), ("src_len", vp), ("n_src", i32)]
+                ("src_off", vp), ("src_len", vp), ("n_src", i32), ("memory", i32)]
 
 
 class StepArgs(C.Structure):
@@ -61,7 +62,8 @@ class StepArgs(C.Structure):
                 ("q_pos", i32), ("q_route", vp), ("route_tokens", vp), ("block", i32),
                 ("k_loc", vp), ("v_loc", vp), ("L_loc", i32), ("hops", i32), ("w_proj", vp), ("exclude_selected", i32), ("exclude", vp),
                 ("ids", vp), ("scores", vp), ("out", vp), ("ws", vp), ("ws_bytes", C.c_size_t),
-                ("staging", vp), ("staging_bytes", C.c_size_t), ("splits", i32)]
+                ("staging", vp), ("staging_bytes", C.c_size_t), ("splits", i32),
+                ("memory", i32)]
 
 
 class StepStats(C.Structure):
@@ -87,6 +89,12 @@ def _load():
     lib.msa_workspace_bytes.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32]
     lib.msa_staging_bytes.restype = C.c_size_t
     lib.msa_staging_bytes.argtypes = [vp, i32, i32]
+    lib.msa_pooled_sizes.restype = C.c_int
+    lib.msa_pooled_sizes.argtypes = [vp, C.POINTER(i64), C.POINTER(i64)]
+    lib.msa_bank_set_pooled.restype = C.c_int
+    lib.msa_bank_set_pooled.argtypes = [vp, vp, vp]
+    lib.msa_build_pooled.restype = C.c_int
+    lib.msa_build_pooled.argtypes = [vp, i32, i32, vp]
     lib.msa_bank_append.restype = C.c_int
     lib.msa_bank_append.argtypes = [vp, i32, C.POINTER(i64), C.POINTER(i64)]
     lib.msa_cache_slot_bytes.restype = C.c_size_t
@@ -249,6 +257,26 @@ class Bank:
         n = self.workspace_bytes(mode, n_q, h_q, k, block, hops, splits)
         return torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
 
+    def attach_pooled(self):
+        """Allocate and attach the compressed-memory stores (per-chunk means
+        of K and V); fill them with build_pooled."""
+        ke, ve = i64(), i64()
+        _check(lib.msa_pooled_sizes(self.handle, C.byref(ke), C.byref(ve)), "msa_pooled_sizes")
+        self.pool_k = torch.empty(max(1, ke.value), dtype=self.dtype, device=self.device)
+        self.pool_v = torch.empty(max(1, ve.value), dtype=self.dtype, device=self.device)
+        _check(lib.msa_bank_set_pooled(self.handle, _ptr(self.pool_k), _ptr(self.pool_v)),
+               "msa_bank_set_pooled")
+
+    def use_pooled(self, pool_k, pool_v):
+        """Attach existing pooled stores (e.g. built on a device-resident twin
+        of a host-resident bank); None detaches."""
+        self.pool_k, self.pool_v = pool_k, pool_v
+        _check(lib.msa_bank_set_pooled(self.handle, _ptr(pool_k), _ptr(pool_v)),
+               "msa_bank_set_pooled")
+
+    def build_pooled(self, doc0: int, doc1: int, stream=None):
+        _check(lib.msa_build_pooled(self.handle, doc0, doc1, _stream(stream)), "msa_build_pooled")
+
     def cache_slot_bytes(self) -> int:
         return int(lib.msa_cache_slot_bytes(self.handle))
 
@@ -275,7 +303,7 @@ class Bank:
         return ids, scores
 
     def attend(self, q, q_pos: int, ids, k_loc, v_loc, L_loc: int, mode=MSA_DECODE, block: int = 64, splits: int = 0, ws=None, src=None,
-               out=None, stream=None):
+               out=None, stream=None, memory=MSA_MEMORY_TOKENS):
         n_q, h_q = int(q.shape[0]), int(q.shape[1])
         k = 0 if ids is None else int(ids.shape[1])
         if ws is None:
@@ -286,19 +314,21 @@ class Bank:
         a = AttendArgs(mode, n_q, h_q, _ptr(q), int(q_pos), _ptr(ids), k, block, _ptr(k_loc),
                        _ptr(v_loc), int(L_loc), _ptr(out), _ptr(ws),
                        ws.numel(), splits, _ptr(sk), _ptr(sv), _ptr(so), _ptr(sl),
-                       0 if sl is None else int(sl.numel()))
+                       0 if sl is None else int(sl.numel()), int(memory))
         _check(lib.msa_attend(self.handle, C.byref(a), _stream(stream)), "msa_attend")
         return out
 
     def step(self, q, q_pos: int, k: int, k_loc, v_loc, L_loc: int, q_route=None, route_tokens=None, mode=MSA_DECODE, block: int = 64, hops: int = 1,
              w_proj=None, exclude_selected: bool = False, exclude=None, splits: int = 0,
-             ws=None, staging=None, outputs=None, stream=None, copy_stream=None):
+             ws=None, staging=None, outputs=None, stream=None, copy_stream=None,
+             memory=MSA_MEMORY_TOKENS):
         """Returns (ids [hops, n_groups, k], scores, out [hops, n_q, h_q, 128], stats)."""
         n_q, h_q = int(q.shape[0]), int(q.shape[1])
         n_groups = n_q // block if mode == MSA_PREFILL else n_q
         if ws is None:
             ws = self.workspace(mode, n_q, h_q, k, block, hops, splits)
-        if self.kv_host and staging is None and getattr(self, "cache", None) is None:
+        if (self.kv_host and staging is None and getattr(self, "cache", None) is None
+                and memory == MSA_MEMORY_TOKENS):
             staging = self.staging(n_groups, k)
         if outputs is None:
             ids = torch.empty((hops, n_groups, k), dtype=torch.int32, device=self.device)
@@ -310,7 +340,7 @@ class Bank:
                      block, _ptr(k_loc), _ptr(v_loc), int(L_loc), hops,
                      _ptr(w_proj), int(bool(exclude_selected)), _ptr(exclude), _ptr(ids),
                      _ptr(scores), _ptr(out), _ptr(ws), ws.numel(), _ptr(staging),
-                     0 if staging is None else staging.numel(), splits)
+                     0 if staging is None else staging.numel(), splits, int(memory))
         st = StepStats()
         cs = None if copy_stream is None else _stream(copy_stream)
         _check(lib.msa_step(self.handle, C.byref(a), _stream(stream), cs, C.byref(st)),
