@@ -184,20 +184,58 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillP p) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
+  // -ref_of(m_run) in every element: the accumulator a score tile starts
+  // from, so scores come out relative to the row's reference
+  f32x16_t negm;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) negm[e] = 0.f;
 
-  int r_issue = 0;
-  auto tile_at = [&](int& r, int u) {
-    while (u >= __builtin_amdgcn_readfirstlane(s_tile0[r + 1])) ++r;
+  // Tile cursors.  Tile u of the split walks the segments (the selected
+  // documents in rank order, then the local context) 64 tokens at a time; a
+  // cursor keeps its segment's values in scalar registers and reads the
+  // segment table only when it crosses into the next segment.
+  auto rfl = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
+  auto rfl64 = [&](int64_t v) {
+    return (int64_t)(((uint64_t)(uint32_t)rfl((int)(v >> 32)) << 32) | (uint32_t)rfl((int)v));
+  };
+  struct Cursor {
+    int u, r, end, t0, len;
+    const uint16_t* kb;  // segment's K rows for this KV head
+    const uint16_t* vb;  // segment's V^T tiles for this KV head
+  };
+  auto load_seg = [&](Cursor& c) __attribute__((always_inline)) {
+    c.end = rfl(s_tile0[c.r + 1]);
+    c.len = rfl(s_len[c.r]);
+    c.kb = (c.r == k ? p.kl : p.ks) + rfl64(s_koff[c.r]);
+    c.vb = (c.r == k ? p.vl : p.vs) + rfl64(s_voff[c.r]);
+  };
+  auto seek = [&](Cursor& c, int u) __attribute__((always_inline)) {
+    c.u = u;
+    c.r = 0;
+    while (u >= rfl(s_tile0[c.r + 1])) ++c.r;
+    load_seg(c);
+    c.t0 = (u - rfl(s_tile0[c.r])) * 64;
+  };
+  // next tile, or stay on the split's last tile
+  auto advance = [&](Cursor& c, int u_stop) __attribute__((always_inline)) {
+    if (c.u >= u_stop) return;
+    ++c.u;
+    if (c.u < c.end) {
+      c.t0 += 64;
+      return;
+    }
+    do ++c.r;
+    while (c.u >= rfl(s_tile0[c.r + 1]));
+    load_seg(c);
+    c.t0 = 0;
+  };
+  auto tile_of = [&](const Cursor& c) __attribute__((always_inline)) {
     Tile t;
-    t.t0 = (u - __builtin_amdgcn_readfirstlane(s_tile0[r])) * 64;
-    t.nvalid = min(64, __builtin_amdgcn_readfirstlane(s_len[r]) - t.t0);
-    t.local = r == k;
-    const int64_t koff = ((int64_t)__builtin_amdgcn_readfirstlane((int)(s_koff[r] >> 32)) << 32) |
-                         (uint32_t)__builtin_amdgcn_readfirstlane((int)s_koff[r]);
-    const int64_t voff = ((int64_t)__builtin_amdgcn_readfirstlane((int)(s_voff[r] >> 32)) << 32) |
-                         (uint32_t)__builtin_amdgcn_readfirstlane((int)s_voff[r]);
-    t.kb = (t.local ? p.kl : p.ks) + koff + (size_t)t.t0 * kD;
-    t.vb = (t.local ? p.vl : p.vs) + voff + (size_t)t.t0 * kD;
+    t.t0 = c.t0;
+    t.nvalid = min(64, c.len - c.t0);
+    t.local = c.r == k;
+    t.kb = c.kb + (size_t)c.t0 * kD;
+    t.vb = c.vb + (size_t)c.t0 * kD;
     return t;
   };
   // Stage a tile: wave w's load i fills 1 KB j = w + 8*i of the K tile (LDS
@@ -210,22 +248,23 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillP p) {
   // slot must differ across rows of equal parity.  K rows past the tile's
   // valid tokens repeat its last valid row (their scores are masked); V^T
   // tiles are zero-padded in memory.
-  auto issue = [&](const Tile& t, uint8_t* base) {
+  int krow[2], kcol[2], vofs[2];  // this lane's load in each half of a tile
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int j = wave + kWaves * i;
-      const int r = 4 * j + (lane >> 4);
-      const int tok = min(perm16(r), t.nvalid - 1);
-      const int c = (lane & 15) ^ (r & 15);
-      dma16(t.kb + (size_t)tok * kD + 8 * c, base + 1024 * j);
-    }
+  for (int i = 0; i < 2; ++i) {
+    const int j = wave + kWaves * i;
+    const int r = 4 * j + (lane >> 4);
+    krow[i] = perm16(r);
+    kcol[i] = 8 * ((lane & 15) ^ (r & 15));
+    const int d = 8 * j + (lane >> 3);
+    vofs[i] = d * 64 + 8 * ((lane & 7) ^ ((d >> 1) & 7));
+  }
+  auto issue = [&](const Tile& t, uint8_t* base) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int j = wave + kWaves * i;
-      const int d = 8 * j + (lane >> 3);
-      const int cv = (lane & 7) ^ ((d >> 1) & 7);
-      dma16(t.vb + d * 64 + 8 * cv, base + kTileB + 1024 * j);
-    }
+    for (int i = 0; i < 2; ++i)
+      dma16(t.kb + (min(krow[i], t.nvalid - 1) * kD + kcol[i]), base + 1024 * (wave + kWaves * i));
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      dma16(t.vb + vofs[i], base + kTileB + 1024 * (wave + kWaves * i));
   };
 
   using I0 = std::integral_constant<int, 0>;
@@ -290,6 +329,8 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillP p) {
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int e = 0; e < 16; ++e) sc[mt][e] -= mx;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) negm[e] = -m_new;
       }
     }
   };
@@ -297,47 +338,46 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillP p) {
   // Software pipeline: the scores of tile u + 1 go onto the matrix cores in
   // the same straight-line block as tile u's exponentials and P.V, so the
   // matrix and vector units overlap.  Every ring step issues exactly one
-  // tile (indices past the split's end repeat its last tile, and a score pass
-  // past the end is discarded), so the ring's wait counts are the same on
-  // every path.
+  // tile (past the split's end the cursors stay on its last tile, and a
+  // score pass past the end is discarded), so the ring's wait counts are the
+  // same on every path.  Score tiles alternate between two register sets.
   const int u_last = u1 - 1;
-  f32x16_t sc[2];
+  f32x16_t sA[2], sB[2];
   Tile cur{};
-  int r_next = 0;
+  Cursor ci{}, cc{};  // issue cursor (three tiles ahead) and compute cursor
   if (u0 < u1) {
-    issue(tile_at(r_issue, u0), stage_buf(I0{}));
-    issue(tile_at(r_issue, min(u0 + 1, u_last)), stage_buf(I1{}));
-    issue(tile_at(r_issue, min(u0 + 2, u_last)), stage_buf(I2{}));
+    seek(ci, u0);
+    cc = ci;
+    issue(tile_of(ci), stage_buf(I0{}));
+    advance(ci, u_last);
+    issue(tile_of(ci), stage_buf(I1{}));
+    advance(ci, u_last);
+    issue(tile_of(ci), stage_buf(I2{}));
+    advance(ci, u_last);
     wait_ring_barrier<kWaitVm8>();  // tile u0 landed
-    cur = tile_at(r_next, u0);
+    cur = tile_of(cc);
     const uint8_t* sk = stage_buf(I0{});
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
+      sA[mt] = mfma32(kfrag(sk, mt, 0), qf[0], negm);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sc[mt][e] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) sc[mt] = mfma32(kfrag(sk, mt, kk), qf[kk], sc[mt]);
+      for (int kk = 1; kk < 8; ++kk) sA[mt] = mfma32(kfrag(sk, mt, kk), qf[kk], sA[mt]);
     }
   }
 
   // ring step for tile u in stage st: tile u + 1 (stage st + 1) must have
   // landed; tile u + 3 goes to stage st + 3, which held tile u - 1
-  auto step = [&](auto st, int u) __attribute__((always_inline)) {
+  auto step = [&](auto st, int u, f32x16_t(&sc)[2], f32x16_t(&sn)[2]) __attribute__((always_inline)) {
     constexpr int S = decltype(st)::value;
     wait_ring_barrier<kWaitVm4>();
-    issue(tile_at(r_issue, min(u + kStages - 1, u_last)),
-          stage_buf(std::integral_constant<int, (S + kStages - 1) % kStages>{}));
+    issue(tile_of(ci), stage_buf(std::integral_constant<int, (S + kStages - 1) % kStages>{}));
+    advance(ci, u_last);
     if (u >= u1) return;
     softmax_pre(cur, sc);
-    const Tile nxt = tile_at(r_next, min(u + 1, u_last));
+    advance(cc, u_last);
+    const Tile nxt = tile_of(cc);
     const uint8_t* sk = stage_buf(std::integral_constant<int, (S + 1) % kStages>{});
     const uint8_t* sv = stage_buf(st) + kTileB;
-    const float m_ref = ref_of(m_run);
-    f32x16_t sn[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sn[mt][e] = -m_ref;
     // k-step ks: 4 score MFMAs of tile u + 1 (half ks/2, k-steps
     // 4*(ks%2) .. +3), then tile u's probabilities for tokens 16*ks + 8*hl
     // .. +7 (elements 8*(ks%2) .. +7 of sc[ks/2]) as bf16 and their 4 P.V
@@ -348,7 +388,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillP p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int mt = ks >> 1, kk = 4 * (ks & 1) + j;
-        sn[mt] = mfma32(kfrag(sk, mt, kk), qf[kk], sn[mt]);
+        sn[mt] = mfma32(kfrag(sk, mt, kk), qf[kk], kk == 0 ? negm : sn[mt]);
       }
       uint32_t w[4];
 #pragma unroll
@@ -362,17 +402,15 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillP p) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) o[dt] = mfma32(vfrag(sv, ks, dt), pb, o[dt]);
     }
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) sc[mt] = sn[mt];
     cur = nxt;
   };
   for (int u = u0; u < u1; u += kStages) {
     // all four steps run on every pass, so every wave meets the same
     // barriers and the wait counts hold on every path
-    step(I0{}, u);
-    step(I1{}, u + 1);
-    step(I2{}, u + 2);
-    step(I3{}, u + 3);
+    step(I0{}, u, sA, sB);
+    step(I1{}, u + 1, sB, sA);
+    step(I2{}, u + 2, sA, sB);
+    step(I3{}, u + 3, sB, sA);
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no load may still write LDS after the workgroup ends
 
