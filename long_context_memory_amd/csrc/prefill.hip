@@ -70,11 +70,19 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-// One 16-byte global->LDS copy per lane: lane l's bytes land at
-// lds_wave_base + 16*l (the base is wave-uniform).
-__device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+// One 16-byte global->LDS copy per lane through a buffer descriptor: lane l
+// reads bytes [voff, voff + 16) of the buffer (zeros past its range) and they
+// land at lds_wave_base + 16*l (the base is wave-uniform).  The buffer form,
+// unlike the flat-encoded global one, leaves the compiler's count of
+// outstanding LDS reads exact, so fragment reads can be pipelined while ring
+// loads are in flight.
+constexpr int kBufWord3 = 0x00020000;  // raw buffer, 32-bit data format
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufWord3);
+}
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, int voff, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base,
+                                           16, voff, 0, 0, 0);
 }
 
 // LDS row r of a staged K tile holds token perm16(r): bits 2 and 3 swapped.
@@ -245,26 +253,26 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillP p) {
   // 16-byte-per-lane read 16 lanes at a time: K rows are 256 bytes, so 16
   // consecutive rows must use 16 different slots; V^T rows are 128 bytes, so
   // rows d and d + 1 already sit in different halves of the banks and the
-  // slot must differ across rows of equal parity.  K rows past the tile's
-  // valid tokens repeat its last valid row (their scores are masked); V^T
-  // tiles are zero-padded in memory.
-  int krow[2], kcol[2], vofs[2];  // this lane's load in each half of a tile
+  // slot must differ across rows of equal parity.  V^T tiles are
+  // zero-padded in memory.
+  int kofs[2], vofs[2];  // byte offsets of this lane's loads in each half of a tile
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int j = wave + kWaves * i;
     const int r = 4 * j + (lane >> 4);
-    krow[i] = perm16(r);
-    kcol[i] = 8 * ((lane & 15) ^ (r & 15));
+    kofs[i] = perm16(r) * 256 + 16 * ((lane & 15) ^ (r & 15));
     const int d = 8 * j + (lane >> 3);
-    vofs[i] = d * 64 + 8 * ((lane & 7) ^ ((d >> 1) & 7));
+    vofs[i] = d * 128 + 16 * ((lane & 7) ^ ((d >> 1) & 7));
   }
+  // The K buffer ends at the tile's last valid token, so rows past it load
+  // as zeros (their scores are masked).
   auto issue = [&](const Tile& t, uint8_t* base) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rk = buf_rsrc(t.kb, t.nvalid * 256);
+    const __amdgpu_buffer_rsrc_t rv = buf_rsrc(t.vb, kTileB);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      dma16(t.kb + (min(krow[i], t.nvalid - 1) * kD + kcol[i]), base + 1024 * (wave + kWaves * i));
+    for (int i = 0; i < 2; ++i) dma16(rk, kofs[i], base + 1024 * (wave + kWaves * i));
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      dma16(t.vb + vofs[i], base + kTileB + 1024 * (wave + kWaves * i));
+    for (int i = 0; i < 2; ++i) dma16(rv, vofs[i], base + kTileB + 1024 * (wave + kWaves * i));
   };
 
   using I0 = std::integral_constant<int, 0>;
