@@ -438,7 +438,12 @@ def main():
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic("decode_c2_counters"),
                      "bytes_per_launch": kv_bytes, "avg_launch_us": att_avg_us,
-                     "launches": att_n},
+                     "launches": att_n,
+                     # the two streams' launches overlap, so a launch's duration
+                     # includes time shared with the other stream's launch; the
+                     # whole-run rate counts every byte once over the wall clock
+                     "aggregate_GBs": kv_bytes * args.steps / dt / 1e9,
+                     "aggregate_frac": kv_bytes * args.steps / dt / 1e9 / HBM_PEAK_GBS},
         "tokens_attended_per_s": qps * (w.k * 512 + w.L_loc),
         "bank_build_s": build_s,
     }

@@ -292,12 +292,15 @@ class Bank:
         return torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
 
     # -- hot path -----------------------------------------------------------
-    def route(self, q_route, k: int, exclude=None, ws=None, stream=None):
+    def route(self, q_route, k: int, exclude=None, ws=None, stream=None, outputs=None):
         B = int(q_route.shape[0])
         if ws is None:
             ws = self.workspace(MSA_DECODE, B, self.h_kv, k)
-        ids = torch.empty((B, k), dtype=torch.int32, device=self.device)
-        scores = torch.empty((B, k), dtype=torch.float32, device=self.device)
+        if outputs is None:
+            ids = torch.empty((B, k), dtype=torch.int32, device=self.device)
+            scores = torch.empty((B, k), dtype=torch.float32, device=self.device)
+        else:
+            ids, scores = outputs
         _check(lib.msa_route(self.handle, _ptr(q_route), B, k, _ptr(exclude), _ptr(ids),
                              _ptr(scores), _ptr(ws), ws.numel(), _stream(stream)), "msa_route")
         return ids, scores

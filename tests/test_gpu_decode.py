@@ -201,6 +201,22 @@ def test_decode_splits_and_determinism(msa, name):
         assert float((o - outs[0]).abs().max()) <= tol * scale
 
 
+def test_decode_workspace_reuse(msa):
+    # the split merge counters live in the workspace: a poisoned workspace and
+    # one reused call after call give the same bits as a fresh one
+    c = decode_case(msa, "decode_small")
+    w, bank = c["w"], c["bank"]
+    ids, _ = bank.route(c["q_route"], w.k)
+    ref = bank.attend(c["q"], w.q_pos, ids, c["k_loc"], c["v_loc"], c["L"])
+    ws = bank.workspace(msa.MSA_DECODE, w.B, w.h_q, w.k)
+    ws.fill_(255)
+    outs = [bank.attend(c["q"], w.q_pos, ids, c["k_loc"], c["v_loc"], c["L"], ws=ws)
+            for _ in range(3)]
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o, ref)
+
+
 @pytest.mark.parametrize("L_loc", [0, 1, 63, 64, 65, 130])
 def test_decode_ragged_and_empty_local(msa, L_loc):
     c = decode_case(msa, "decode_small")
