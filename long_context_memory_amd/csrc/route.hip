@@ -16,16 +16,17 @@
 namespace msa {
 namespace {
 
-constexpr int kCosStride = 65;   // floats per query row of staged cosines
 constexpr int kQPerWave = 16;    // queries a wave scores per pass (64 per workgroup pass)
 
 // Routing scan.  Workgroup = one (tile of 64 chunks, router head); the tile's
-// key rows are staged once through LDS (coalesced 16-byte loads, all issued
-// before the first store) and every wave takes all 64 rows, one per lane.
-// The batch's router queries for this head are staged in LDS and read back as
-// broadcasts.  Wave w scores queries w, w+4, ... of a pass of 64, stages the
-// cosines in its own LDS rows, then lane j folds query j's cosines into
-// per-document maxima, one per run of equal documents ("piece") in the tile.
+// key rows are staged once through LDS and every wave takes all 64 rows, one
+// per lane.  The batch's router queries for this head are staged in LDS and
+// read back as broadcasts.  Every global load of the workgroup (key rows,
+// queries, chunk table) is issued before the first LDS store, so a launch
+// costs one memory round trip.  Wave w scores queries w, w+4, ...; for each,
+// lane c holds the cosine of chunk c and a segmented max across lanes folds
+// the tile's runs of equal documents ("pieces") into per-document maxima,
+// written by the lane that starts each run.
 //
 // bf16 keys: the dot products use v_dot2_f32_bf16 with the float32 query
 // split into two bfloat16 terms (q = hi + lo + r, |r| <= 2^-17 |q|), fp32
@@ -39,45 +40,91 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
   // queries bg .. bg + min(64, B - bg) - 1 (one launch per group of 64)
   constexpr bool kBF = sizeof(T) == 2;
   constexpr int RowF = kD * (int)sizeof(T) / 4 + 4;  // 32-bit words per staged row (+16 B pad)
-  constexpr int QW = kBF ? kD : kD;                  // words per staged query (bf16: hi|lo pairs)
+  constexpr int QW = kD;                             // words per staged query (bf16: hi|lo pairs)
   __shared__ __attribute__((aligned(16))) uint32_t s_rows[64 * RowF];
   __shared__ __attribute__((aligned(16))) uint32_t s_q[64 * QW];
-  __shared__ float s_cos[4][kQPerWave * kCosStride];
   __shared__ float s_iq[64];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int tile = blockIdx.x, h = blockIdx.y;
   const int64_t c0 = (int64_t)tile * kRouteTile;
   const int nc = (int)min((int64_t)kRouteTile, C - c0);
+  const int npass = min(64, B - bg);
   const T* rows = kr + ((size_t)h * Cs + c0) * kD;  // Cs: rows per head (capacity)
 
-  // stage the tile: 64 rows x VPR 16-byte vectors; rows past the end of the
-  // bank read the last row and are stored as zero
+  // ---- every global load first: the tile (64 rows x VPR 16-byte vectors;
+  // rows past the end of the bank read the last row and are stored as zero),
+  // this pass's queries (64 x 32 float4, rows past the pass skipped) and the
+  // tile's chunk table
   constexpr int VPR = kD * (int)sizeof(T) / 16;
   constexpr int NLD = 64 * VPR / 256;
-  {
-    uint4 v[NLD];
+  uint4 v[NLD];
 #pragma unroll
-    for (int u = 0; u < NLD; ++u) {
-      const int f = u * 256 + threadIdx.x;
-      const int row = f / VPR, col = f % VPR;
-      v[u] = *reinterpret_cast<const uint4*>(rows + ((size_t)min(row, nc - 1) * VPR + col) *
-                                                        (16 / sizeof(T)));
-    }
-#pragma unroll
-    for (int u = 0; u < NLD; ++u) {
-      const int f = u * 256 + threadIdx.x;
-      const int row = f / VPR, col = f % VPR;
-      *reinterpret_cast<uint4*>(s_rows + row * RowF + col * 4) =
-          row < nc ? v[u] : make_uint4(0, 0, 0, 0);
-    }
+  for (int u = 0; u < NLD; ++u) {
+    const int f = u * 256 + threadIdx.x;
+    const int row = f / VPR, col = f % VPR;
+    v[u] = *reinterpret_cast<const uint4*>(rows + ((size_t)min(row, nc - 1) * VPR + col) *
+                                                      (16 / sizeof(T)));
   }
-  // document runs inside the tile (same for every wave)
+  float4 qv[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int f = u * 256 + threadIdx.x;
+    const int qi = f / (kD / 4), col = f % (kD / 4);
+    qv[u] = qi < npass ? *reinterpret_cast<const float4*>(q + ((size_t)(bg + qi) * h_r + h) * kD +
+                                                          col * 4)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   const int my_doc = lane < nc ? chunk_doc[c0 + lane] : -1;
-  const int prev_doc = __shfl_up(my_doc, 1, 64);
-  const uint64_t starts = __ballot(lane < nc && (lane == 0 || my_doc != prev_doc));
   const float inv_k = lane < nc ? inv_norm[(size_t)h * Cs + c0 + lane] : 0.0f;
   const int piece0 = tile_piece0[tile];
+
+#pragma unroll
+  for (int u = 0; u < NLD; ++u) {
+    const int f = u * 256 + threadIdx.x;
+    const int row = f / VPR, col = f % VPR;
+    *reinterpret_cast<uint4*>(s_rows + row * RowF + col * 4) =
+        row < nc ? v[u] : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int f = u * 256 + threadIdx.x;
+    const int qi = f / (kD / 4), col = f % (kD / 4);
+    if constexpr (kBF) {
+      // words [qi][0..63]: hi pairs; [qi][64..127]: lo pairs
+      const float x[4] = {qv[u].x, qv[u].y, qv[u].z, qv[u].w};
+      uint32_t hi[2], lo[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const uint32_t h0 = f32_to_bf16(x[2 * e]), h1 = f32_to_bf16(x[2 * e + 1]);
+        hi[e] = h0 | (h1 << 16);
+        lo[e] = f32_to_bf16(x[2 * e] - __uint_as_float(h0 << 16)) |
+                (f32_to_bf16(x[2 * e + 1] - __uint_as_float(h1 << 16)) << 16);
+      }
+      *reinterpret_cast<uint2*>(s_q + qi * QW + col * 2) = make_uint2(hi[0], hi[1]);
+      *reinterpret_cast<uint2*>(s_q + qi * QW + 64 + col * 2) = make_uint2(lo[0], lo[1]);
+    } else {
+      *reinterpret_cast<float4*>(s_q + qi * QW + col * 4) = qv[u];
+    }
+    // partial squared norm of the float32 query
+    float ss = qv[u].x * qv[u].x + qv[u].y * qv[u].y + qv[u].z * qv[u].z + qv[u].w * qv[u].w;
+    // 32 consecutive threads hold one query row: reduce within the 32
+    ss += __shfl_xor(ss, 1, 64);
+    ss += __shfl_xor(ss, 2, 64);
+    ss += __shfl_xor(ss, 4, 64);
+    ss += __shfl_xor(ss, 8, 64);
+    ss += __shfl_xor(ss, 16, 64);
+    if (col == 0) s_iq[qi] = ss > 0.f ? 1.0f / sqrtf(ss) : 0.0f;
+  }
+
+  // document runs inside the tile (same for every wave): this lane's run
+  // ends before lane `end`; a run's first lane writes piece piece0 + seg
+  const int prev_doc = __shfl_up(my_doc, 1, 64);
+  const bool start = lane < nc && (lane == 0 || my_doc != prev_doc);
+  const uint64_t starts = __ballot(start);
+  const uint64_t later = lane == 63 ? 0 : starts & (~0ull << (lane + 1));
+  const int end = later ? __builtin_ctzll(later) : nc;
+  const int seg = __builtin_popcountll(starts & ((1ull << lane) - 1));
   __syncthreads();
 
   // this lane's key row: bf16 stays packed (16 x uint4), f32 as 32 x uint4
@@ -85,104 +132,50 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
 #pragma unroll
   for (int c = 0; c < VPR; ++c) kw[c] = *reinterpret_cast<const uint4*>(s_rows + lane * RowF + c * 4);
 
-  float* cw = s_cos[wave];
-  {
-    const int npass = min(64, B - bg);
-    // stage this pass's queries (head h): 64 x 32 float4, loads first
-    {
-      float4 v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int f = u * 256 + threadIdx.x;
-        const int qi = f / (kD / 4), col = f % (kD / 4);
-        v[u] = *reinterpret_cast<const float4*>(
-            q + ((size_t)(bg + min(qi, npass - 1)) * h_r + h) * kD + col * 4);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int f = u * 256 + threadIdx.x;
-        const int qi = f / (kD / 4), col = f % (kD / 4);
-        if constexpr (kBF) {
-          // words [qi][0..63]: hi pairs; [qi][64..127]: lo pairs
-          const float x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-          uint32_t hi[2], lo[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const uint32_t h0 = f32_to_bf16(x[2 * e]), h1 = f32_to_bf16(x[2 * e + 1]);
-            hi[e] = h0 | (h1 << 16);
-            lo[e] = f32_to_bf16(x[2 * e] - __uint_as_float(h0 << 16)) |
-                    (f32_to_bf16(x[2 * e + 1] - __uint_as_float(h1 << 16)) << 16);
-          }
-          *reinterpret_cast<uint2*>(s_q + qi * QW + col * 2) = make_uint2(hi[0], hi[1]);
-          *reinterpret_cast<uint2*>(s_q + qi * QW + 64 + col * 2) = make_uint2(lo[0], lo[1]);
-        } else {
-          *reinterpret_cast<float4*>(s_q + qi * QW + col * 4) = v[u];
-        }
-        // partial squared norm of the float32 query
-        float ss = v[u].x * v[u].x + v[u].y * v[u].y + v[u].z * v[u].z + v[u].w * v[u].w;
-        // 32 consecutive threads hold one query row: reduce within the 32
-        ss += __shfl_xor(ss, 1, 64);
-        ss += __shfl_xor(ss, 2, 64);
-        ss += __shfl_xor(ss, 4, 64);
-        ss += __shfl_xor(ss, 8, 64);
-        ss += __shfl_xor(ss, 16, 64);
-        if (col == 0) s_iq[qi] = ss > 0.f ? 1.0f / sqrtf(ss) : 0.0f;
-      }
-    }
-    __syncthreads();
-    // this wave's queries: bg + wave + 4*j, j < nq
-    const int nq = max(0, min(kQPerWave, (npass - wave + 3) / 4));
+  // this wave's queries: bg + wave + 4*j, j < nq
+  const int nq = max(0, min(kQPerWave, (npass - wave + 3) / 4));
 #pragma unroll 1
-    for (int j = 0; j < nq; ++j) {
-      const uint32_t* qj = s_q + (wave + 4 * j) * QW;
-      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-      if constexpr (kBF) {
+  for (int j = 0; j < nq; ++j) {
+    const int qi = wave + 4 * j;
+    const uint32_t* qj = s_q + qi * QW;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    if constexpr (kBF) {
 #pragma unroll
-        for (int c = 0; c < 16; c += 2) {
-          const uint4 h0 = *reinterpret_cast<const uint4*>(qj + c * 4);
-          const uint4 l0 = *reinterpret_cast<const uint4*>(qj + 64 + c * 4);
-          const uint4 h1 = *reinterpret_cast<const uint4*>(qj + c * 4 + 4);
-          const uint4 l1 = *reinterpret_cast<const uint4*>(qj + 64 + c * 4 + 4);
-          a0 = dot2_bf16(kw[c].x, h0.x, a0); a0 = dot2_bf16(kw[c].y, h0.y, a0);
-          a0 = dot2_bf16(kw[c].z, h0.z, a0); a0 = dot2_bf16(kw[c].w, h0.w, a0);
-          a1 = dot2_bf16(kw[c].x, l0.x, a1); a1 = dot2_bf16(kw[c].y, l0.y, a1);
-          a1 = dot2_bf16(kw[c].z, l0.z, a1); a1 = dot2_bf16(kw[c].w, l0.w, a1);
-          a2 = dot2_bf16(kw[c + 1].x, h1.x, a2); a2 = dot2_bf16(kw[c + 1].y, h1.y, a2);
-          a2 = dot2_bf16(kw[c + 1].z, h1.z, a2); a2 = dot2_bf16(kw[c + 1].w, h1.w, a2);
-          a3 = dot2_bf16(kw[c + 1].x, l1.x, a3); a3 = dot2_bf16(kw[c + 1].y, l1.y, a3);
-          a3 = dot2_bf16(kw[c + 1].z, l1.z, a3); a3 = dot2_bf16(kw[c + 1].w, l1.w, a3);
-        }
-      } else {
-#pragma unroll
-        for (int c = 0; c < 32; c += 2) {
-          const float4 x0 = *reinterpret_cast<const float4*>(qj + c * 4);
-          const float4 x1 = *reinterpret_cast<const float4*>(qj + c * 4 + 4);
-          a0 = fmaf(__uint_as_float(kw[c].x), x0.x, a0); a1 = fmaf(__uint_as_float(kw[c].y), x0.y, a1);
-          a0 = fmaf(__uint_as_float(kw[c].z), x0.z, a0); a1 = fmaf(__uint_as_float(kw[c].w), x0.w, a1);
-          a2 = fmaf(__uint_as_float(kw[c + 1].x), x1.x, a2); a3 = fmaf(__uint_as_float(kw[c + 1].y), x1.y, a3);
-          a2 = fmaf(__uint_as_float(kw[c + 1].z), x1.z, a2); a3 = fmaf(__uint_as_float(kw[c + 1].w), x1.w, a3);
-        }
+      for (int c = 0; c < 16; c += 2) {
+        const uint4 h0 = *reinterpret_cast<const uint4*>(qj + c * 4);
+        const uint4 l0 = *reinterpret_cast<const uint4*>(qj + 64 + c * 4);
+        const uint4 h1 = *reinterpret_cast<const uint4*>(qj + c * 4 + 4);
+        const uint4 l1 = *reinterpret_cast<const uint4*>(qj + 64 + c * 4 + 4);
+        a0 = dot2_bf16(kw[c].x, h0.x, a0); a0 = dot2_bf16(kw[c].y, h0.y, a0);
+        a0 = dot2_bf16(kw[c].z, h0.z, a0); a0 = dot2_bf16(kw[c].w, h0.w, a0);
+        a1 = dot2_bf16(kw[c].x, l0.x, a1); a1 = dot2_bf16(kw[c].y, l0.y, a1);
+        a1 = dot2_bf16(kw[c].z, l0.z, a1); a1 = dot2_bf16(kw[c].w, l0.w, a1);
+        a2 = dot2_bf16(kw[c + 1].x, h1.x, a2); a2 = dot2_bf16(kw[c + 1].y, h1.y, a2);
+        a2 = dot2_bf16(kw[c + 1].z, h1.z, a2); a2 = dot2_bf16(kw[c + 1].w, h1.w, a2);
+        a3 = dot2_bf16(kw[c + 1].x, l1.x, a3); a3 = dot2_bf16(kw[c + 1].y, l1.y, a3);
+        a3 = dot2_bf16(kw[c + 1].z, l1.z, a3); a3 = dot2_bf16(kw[c + 1].w, l1.w, a3);
       }
-      cw[j * kCosStride + lane] = ((a0 + a1) + (a2 + a3)) * inv_k;
+    } else {
+#pragma unroll
+      for (int c = 0; c < 32; c += 2) {
+        const float4 x0 = *reinterpret_cast<const float4*>(qj + c * 4);
+        const float4 x1 = *reinterpret_cast<const float4*>(qj + c * 4 + 4);
+        a0 = fmaf(__uint_as_float(kw[c].x), x0.x, a0); a1 = fmaf(__uint_as_float(kw[c].y), x0.y, a1);
+        a0 = fmaf(__uint_as_float(kw[c].z), x0.z, a0); a1 = fmaf(__uint_as_float(kw[c].w), x0.w, a1);
+        a2 = fmaf(__uint_as_float(kw[c + 1].x), x1.x, a2); a3 = fmaf(__uint_as_float(kw[c + 1].y), x1.y, a3);
+        a2 = fmaf(__uint_as_float(kw[c + 1].z), x1.z, a2); a3 = fmaf(__uint_as_float(kw[c + 1].w), x1.w, a3);
+      }
     }
-    __syncthreads();
-    // lane j: maxima over each run of equal documents, then the query norm
+    // segmented max over [lane, end): after the step with offset o a lane
+    // holds the max of [lane, min(lane + 2o, end)); then the query norm
     // (x -> x * s with s > 0 is monotone, so it commutes with the max)
-    const float my_iq = lane < nq ? s_iq[wave + 4 * lane] : 0.f;
-    uint64_t rest = starts;
-    int seg = 0;
-    while (rest) {
-      const int a0 = __builtin_ctzll(rest);
-      rest &= rest - 1;
-      const int e = rest ? __builtin_ctzll(rest) : nc;
-      if (lane < nq) {
-        float m = -INFINITY;
-        for (int c = a0; c < e; ++c) m = fmaxf(m, cw[lane * kCosStride + c]);
-        const int b = bg + wave + 4 * lane;
-        piecemax[((size_t)b * h_r + h) * P + piece0 + seg] = m * my_iq;
-      }
-      ++seg;
+    float m = ((a0 + a1) + (a2 + a3)) * inv_k;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float u = __shfl_down(m, o, 64);
+      if (lane + o < end) m = fmaxf(m, u);
     }
+    if (start) piecemax[((size_t)(bg + qi) * h_r + h) * P + piece0 + seg] = m * s_iq[qi];
   }
 }
 
