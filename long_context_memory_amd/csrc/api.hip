@@ -607,15 +607,17 @@ int msa_attend(const msa_bank* b, const msa_attend_args* a, void* stream) {
   char* w = (char*)a->ws;
   hipStream_t s = (hipStream_t)stream;
   const bool prefill = a->mode == MSA_PREFILL;
-  MSA_CHECK_HIP(launch_rope_queries(bk, a->q, a->n_q, a->h_q, a->q_pos, prefill ? 1 : 0,
-                                    w + L.qrot, s));
-  if (prefill)
+  // decode rotates the queries inside the attention kernel
+  if (prefill) {
+    MSA_CHECK_HIP(launch_rope_queries(bk, a->q, a->n_q, a->h_q, a->q_pos, 1, w + L.qrot, s));
     MSA_CHECK_HIP(launch_prefill(bk, w + L.qrot, a->n_q, a->h_q, a->ids, a->k, a->block, src,
                                  a->k_loc, a->v_loc, a->L_loc, splits, (float*)(w + L.part),
                                  a->out, s));
-  else
-    MSA_CHECK_HIP(launch_decode(bk, w + L.qrot, a->n_q, a->h_q, a->ids, a->k, src, a->k_loc,
-                                a->v_loc, a->L_loc, splits, (float*)(w + L.part), a->out, s));
+  } else {
+    MSA_CHECK_HIP(launch_decode(bk, a->q, a->q_pos, a->n_q, a->h_q, a->ids, a->k, src,
+                                a->k_loc, a->v_loc, a->L_loc, splits, (float*)(w + L.part),
+                                a->out, s));
+  }
   return MSA_OK;
 }
 
@@ -689,8 +691,9 @@ int msa_step(const msa_bank* b, const msa_step_args* a, void* stream, void* copy
   }
   const float* qr = prefill ? q_route : a->q_route;
   const size_t out_stride = (size_t)a->n_q * a->h_q * kD;
-  MSA_CHECK_HIP(launch_rope_queries(bk, a->q, a->n_q, a->h_q, a->q_pos, prefill ? 1 : 0,
-                                    w + L.qrot, s));
+  // decode rotates the queries inside the attention kernel
+  if (prefill)
+    MSA_CHECK_HIP(launch_rope_queries(bk, a->q, a->n_q, a->h_q, a->q_pos, 1, w + L.qrot, s));
   for (int hop = 0; hop < a->hops; ++hop) {
     int32_t* ids = a->ids + (size_t)hop * n_groups * k;
     float* scores = a->scores + (size_t)hop * n_groups * k;
@@ -829,8 +832,9 @@ int msa_step(const msa_bank* b, const msa_step_args* a, void* stream, void* copy
                                    a->k_loc, a->v_loc, a->L_loc, splits, (float*)(w + L.part), out,
                                    s));
     else
-      MSA_CHECK_HIP(launch_decode(bk, w + L.qrot, a->n_q, a->h_q, att_ids, k, src, a->k_loc,
-                                  a->v_loc, a->L_loc, splits, (float*)(w + L.part), out, s));
+      MSA_CHECK_HIP(launch_decode(bk, a->q, a->q_pos, a->n_q, a->h_q, att_ids, k, src,
+                                  a->k_loc, a->v_loc, a->L_loc, splits, (float*)(w + L.part),
+                                  out, s));
     if (host && bk.cache) {
       MSA_CHECK_HIP(hipEventRecord(bk.attn_done, s));
       bk.attn_pending = true;

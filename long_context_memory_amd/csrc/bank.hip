@@ -17,16 +17,6 @@
 namespace msa {
 namespace {
 
-template <typename T> struct St;
-template <> struct St<float> {
-  static __device__ __forceinline__ float store(double x) { return (float)x; }
-  static __device__ __forceinline__ double load(float x) { return (double)x; }
-};
-template <> struct St<uint16_t> {
-  static __device__ __forceinline__ uint16_t store(double x) { return f64_to_bf16(x); }
-  static __device__ __forceinline__ double load(uint16_t x) { return (double)bf16_to_f32(x); }
-};
-
 // ---------------------------------------------------------------- pooling
 // One workgroup per chunk.  Thread t owns 16-byte vector (t % NV) of every
 // token row (NV vectors per row of h_r*128 elements) and tokens t/NV,

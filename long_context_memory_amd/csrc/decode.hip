@@ -30,7 +30,10 @@ namespace msa {
 namespace {
 
 struct DecodeP {
-  const void* q;       // [B][h_q][128] rotated, pre-scaled by log2(e)/sqrt(d)
+  const void* q;       // [B][h_q][128]: rotated and pre-scaled by log2(e)/sqrt(d), or raw
+                       // when inv_freq is set
+  const double* inv_freq;  // NULL, or [64]: rotate the raw queries at q_pos in the prologue
+  int q_pos;
   const int32_t* ids;  // [B][k]
   const void* ks;
   const void* vs;
@@ -91,8 +94,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeP p) {
   __shared__ int64_t s_koff[kMaxK + 1], s_voff[kMaxK + 1];
   __shared__ int s_len[kMaxK + 1], s_tile0[kMaxK + 2];
   __shared__ __attribute__((aligned(16))) T s_p[4][G][kAttnTile];
+  __shared__ double s_cs[64], s_sn[64];  // RoPE of the queries: pair i at q_pos
+  __shared__ __attribute__((aligned(16))) T s_q[G * kD];  // the rotated queries of (b, h)
 
   const int k = p.k;
+  if (p.inv_freq && threadIdx.x >= 192)
+    sincos((double)p.q_pos * p.inv_freq[threadIdx.x - 192], &s_sn[threadIdx.x - 192],
+           &s_cs[threadIdx.x - 192]);
   if ((int)threadIdx.x < k) {
     const int id = p.ids[(size_t)(b / p.id_div) * k + threadIdx.x];
     int L = 0;
@@ -122,6 +130,20 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeP p) {
     }
     s_tile0[k + 1] = acc;
   }
+  if (p.inv_freq) {
+    // rotate-half RoPE at q_pos and the log2(e)/sqrt(d) scale, in float64
+    // and rounded once, as the query RoPE kernel does; one (head, pair) per
+    // thread, into LDS
+    const double scale = 1.4426950408889634 / sqrt((double)kD);
+    const T* qraw = (const T*)p.q + ((size_t)b * p.h_q + (size_t)h * G) * kD;
+    for (int t = threadIdx.x; t < G * 64; t += 256) {
+      const int g = t >> 6, pair = t & 63;
+      const double x1 = St<T>::load(qraw[g * kD + pair]), x2 = St<T>::load(qraw[g * kD + 64 + pair]);
+      const double cs = s_cs[pair], sn = s_sn[pair];
+      s_q[g * kD + pair] = St<T>::store((x1 * cs - x2 * sn) * scale);
+      s_q[g * kD + 64 + pair] = St<T>::store((x2 * cs + x1 * sn) * scale);
+    }
+  }
   __syncthreads();
 
   const int NT = __builtin_amdgcn_readfirstlane(s_tile0[k + 1]);
@@ -135,11 +157,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeP p) {
   // fp32: chunks j, j+8, j+16, j+24 of 4)
   constexpr int QV = kBF ? 2 : 4;  // 16-byte vectors per lane per head
   uint4 qf[G][QV];
+  const T* qsrc = p.inv_freq ? s_q : qrow;
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int c = 0; c < QV; ++c)
-      qf[g][c] = *reinterpret_cast<const uint4*>(qrow + (size_t)g * kD +
+      qf[g][c] = *reinterpret_cast<const uint4*>(qsrc + (size_t)g * kD +
                                                  (kBF ? (c * 64 + 8 * j) : (c * 32 + 4 * j)));
 
   float m_run[G], l_run[G], o[8 * G];
@@ -415,11 +438,14 @@ int decode_auto_splits(const Bank& bk, int B, int k, int L_loc, double doc_tiles
   return std::min(s, 256);
 }
 
-hipError_t launch_decode(const Bank& bk, const void* q_rot, int B, int h_q, const int32_t* ids,
-                         int k, const AttnSources& src, const void* k_loc, const void* v_loc,
-                         int L_loc, int splits, float* part, float* out, hipStream_t s) {
+hipError_t launch_decode(const Bank& bk, const void* q, int q_pos, int B, int h_q,
+                         const int32_t* ids, int k, const AttnSources& src, const void* k_loc,
+                         const void* v_loc, int L_loc, int splits, float* part, float* out,
+                         hipStream_t s) {
   DecodeP p;
-  p.q = q_rot;
+  p.q = q;
+  p.inv_freq = bk.d_inv_freq;
+  p.q_pos = q_pos;
   p.ids = ids;
   p.ks = src.k;
   p.vs = src.v;
@@ -469,6 +495,8 @@ hipError_t launch_prefill_vector(const Bank& bk, const void* q_rot, int n_q, int
                                  float* part, float* out, hipStream_t s) {
   DecodeP p;
   p.q = q_rot;
+  p.inv_freq = nullptr;
+  p.q_pos = 0;
   p.ids = ids;
   p.ks = src.k;
   p.vs = src.v;

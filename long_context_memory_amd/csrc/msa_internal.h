@@ -117,6 +117,17 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double x) {
   return (uint16_t)((sign << 15) | ((uint64_t)e << 7) | mant);
 }
 
+// storage element <-> float64 (bf16 stores round to nearest even)
+template <typename T> struct St;
+template <> struct St<float> {
+  static __device__ __forceinline__ float store(double x) { return (float)x; }
+  static __device__ __forceinline__ double load(float x) { return (double)x; }
+};
+template <> struct St<uint16_t> {
+  static __device__ __forceinline__ uint16_t store(double x) { return f64_to_bf16(x); }
+  static __device__ __forceinline__ double load(uint16_t x) { return (double)bf16_to_f32(x); }
+};
+
 // fp32 accumulate of a bf16 pair dot product: c + a.lo*b.lo + a.hi*b.hi
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
@@ -236,9 +247,12 @@ struct AttnSources {
                                   // whole 64-entry tiles; NULL: V shares off
   float bias = 0.f;               // score bias of these entries, log2 units
 };
-hipError_t launch_decode(const Bank& bk, const void* q_rot, int B, int h_q, const int32_t* ids,
-                         int k, const AttnSources& src, const void* k_loc, const void* v_loc,
-                         int L_loc, int splits, float* part, float* out, hipStream_t s);
+// q: the raw queries [B][h_q][128] (dtype), rotated at q_pos inside the
+// kernel, exactly as launch_rope_queries would
+hipError_t launch_decode(const Bank& bk, const void* q, int q_pos, int B, int h_q,
+                         const int32_t* ids, int k, const AttnSources& src, const void* k_loc,
+                         const void* v_loc, int L_loc, int splits, float* part, float* out,
+                         hipStream_t s);
 hipError_t launch_prefill(const Bank& bk, const void* q_rot, int n_q, int h_q, const int32_t* ids,
                           int k, int block, const AttnSources& src, const void* k_loc,
                           const void* v_loc, int L_loc, int splits, float* part, float* out,
