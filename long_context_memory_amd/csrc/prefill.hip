@@ -57,6 +57,7 @@ struct PrefillP {
   const uint16_t* vl;  // [h_kv][Tp][128][64]
   int k, L_loc, n_q, h_kv, h_q, S;
   float* part;  // [n_blocks][h_kv][S][256][130]
+  float* out;   // [n_q][h_q][128]: written directly when S == 1
 };
 
 __device__ __forceinline__ f32x16_t mfma32(const bf16x8_t& a, const bf16x8_t& b,
@@ -422,8 +423,20 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillP p) {
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no load may still write LDS after the workgroup ends
 
-  // ---- partials of this lane's row (both lane halves hold half the tokens' l)
+  // ---- this lane's row (both lane halves hold half the tokens' l)
   l_run += __shfl_xor(l_run, 32, 64);
+  if (p.S == 1) {
+    // one split: the merge reduces to o / l, so write the output directly
+    // (row R -> query R/4, head R%4 of this KV head)
+    const int R = 32 * wave + l32;
+    float* orow = p.out + ((size_t)(blk * kQBlock + (R >> 2)) * p.h_q + (size_t)h * kPG + (R & 3)) * kD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        orow[32 * dt + 8 * (e >> 2) + 4 * hl + (e & 3)] = l_run > 0.f ? o[dt][e] / l_run : 0.f;
+    return;
+  }
   float* pr = p.part + ((((size_t)blk * p.h_kv + h) * p.S + split) * kRows + 32 * wave + l32) * (kD + 2);
   if (hl == 0) {
     pr[0] = m_run;
@@ -504,13 +517,15 @@ hipError_t launch_prefill(const Bank& bk, const void* q_rot, int n_q, int h_q, c
   p.h_q = h_q;
   p.S = splits;
   p.part = part;
+  p.out = out;
   const int n_blocks = n_q / kQBlock;
   timer_mark(0, true, s);
   hipLaunchKernelGGL(prefill_mfma_kernel, dim3((unsigned)splits, (unsigned)p.h_kv, (unsigned)n_blocks),
                      dim3(kThreads), 0, s, p);
   timer_mark(0, false, s);
-  hipLaunchKernelGGL(prefill_combine_kernel, dim3(kRows / 2, (unsigned)p.h_kv, (unsigned)n_blocks),
-                     dim3(256), 0, s, part, splits, p.h_kv, h_q, out);
+  if (splits > 1)
+    hipLaunchKernelGGL(prefill_combine_kernel, dim3(kRows / 2, (unsigned)p.h_kv, (unsigned)n_blocks),
+                       dim3(256), 0, s, part, splits, p.h_kv, h_q, out);
   return hipGetLastError();
 }
 
