@@ -151,6 +151,35 @@ def _stream(stream=None):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
 
 
+def _expect(t, shape, dtype, name, device=None):
+    """Refuse a tensor whose shape, dtype, layout or device is not what the C
+    call will read or write: the library sees only a pointer, so a tensor
+    smaller than the sizes passed beside it would be read out of bounds."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(int(x) for x in shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and (t.device.type != device.type or
+                               (device.index is not None and t.device.index != device.index)):
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+
+
+def _expect_bytes(t, nbytes, name, device=None):
+    """A flat buffer (workspace, staging, pooled store) of at least nbytes."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name}: {t.numel() * t.element_size()} bytes, need {nbytes}")
+    if device is not None and t.device.type != device.type:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+
+
 def _dt(dtype) -> int:
     return MSA_BF16 if dtype in ("bf16", torch.bfloat16) else MSA_F32
 
@@ -234,13 +263,27 @@ class Bank:
 
     # -- build --------------------------------------------------------------
     def build(self, doc0: int, doc1: int, route_vec=None, k_raw=None, v_raw=None, stream=None):
+        if not 0 <= doc0 <= doc1 <= self.n_docs:
+            raise ValueError(f"document range [{doc0}, {doc1}) outside [0, {self.n_docs}]")
+        T = sum(self.doc_len[doc0:doc1])
+        if route_vec is not None:
+            _expect(route_vec, (T, self.h_r, 128), self.dtype, "route_vec", self.device)
+        if (k_raw is None) != (v_raw is None):
+            raise ValueError("k_raw and v_raw go together")
+        if k_raw is not None:
+            _expect(k_raw, (T, self.h_kv, 128), self.dtype, "k_raw", self.device)
+            _expect(v_raw, (T, self.h_kv, 128), self.dtype, "v_raw", self.device)
         _check(lib.msa_build_bank(self.handle, doc0, doc1, _ptr(route_vec), _ptr(k_raw),
                                   _ptr(v_raw), _stream(stream)), "msa_build_bank")
 
     def prepare_local(self, k_raw, v_raw, pos0: int, stream=None):
         """k_raw, v_raw: [n_seq, L, h_kv, 128] -> (k_loc [n_seq, h_kv, L, 128],
         v_loc [n_seq, h_kv, ceil(L/64), 128, 64], L)."""
+        if k_raw.dim() != 4:
+            raise ValueError(f"k_raw: {k_raw.dim()}-d, expected [n_seq, L, h_kv, 128]")
         n_seq, L = int(k_raw.shape[0]), int(k_raw.shape[1])
+        _expect(k_raw, (n_seq, L, self.h_kv, 128), self.dtype, "k_raw", self.device)
+        _expect(v_raw, (n_seq, L, self.h_kv, 128), self.dtype, "v_raw", self.device)
         tp = (L + 63) // 64
         k_loc = torch.empty((n_seq, self.h_kv, L, 128), dtype=self.dtype, device=self.device)
         v_loc = torch.empty((n_seq, self.h_kv, tp, 128, 64), dtype=self.dtype, device=self.device)
@@ -270,6 +313,16 @@ class Bank:
     def use_pooled(self, pool_k, pool_v):
         """Attach existing pooled stores (e.g. built on a device-resident twin
         of a host-resident bank); None detaches."""
+        if (pool_k is None) != (pool_v is None):
+            raise ValueError("pool_k and pool_v go together")
+        if pool_k is not None:
+            ke, ve = i64(), i64()
+            _check(lib.msa_pooled_sizes(self.handle, C.byref(ke), C.byref(ve)), "msa_pooled_sizes")
+            esz = 2 if self.dtype == torch.bfloat16 else 4
+            for t, n, name in ((pool_k, ke.value, "pool_k"), (pool_v, ve.value, "pool_v")):
+                if t.dtype != self.dtype:
+                    raise ValueError(f"{name}: dtype {t.dtype}, expected {self.dtype}")
+                _expect_bytes(t, n * esz, name, self.device)
         self.pool_k, self.pool_v = pool_k, pool_v
         _check(lib.msa_bank_set_pooled(self.handle, _ptr(pool_k), _ptr(pool_v)),
                "msa_bank_set_pooled")
@@ -291,9 +344,25 @@ class Bank:
         n = int(lib.msa_staging_bytes(self.handle, n_groups, k))
         return torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
 
+    def _check_queries(self, q):
+        if q is None or q.dim() != 3:
+            raise ValueError("q must be [n_q, h_q, 128]")
+        n_q, h_q = int(q.shape[0]), int(q.shape[1])
+        _expect(q, (n_q, h_q, 128), self.dtype, "q", self.device)
+        return n_q, h_q
+
+    def _check_local(self, k_loc, v_loc, L_loc, n_seq):
+        L_loc = int(L_loc)
+        _expect(k_loc, (n_seq, self.h_kv, L_loc, 128), self.dtype, "k_loc", self.device)
+        _expect(v_loc, (n_seq, self.h_kv, (L_loc + 63) // 64, 128, 64), self.dtype, "v_loc",
+                self.device)
+
     # -- hot path -----------------------------------------------------------
     def route(self, q_route, k: int, exclude=None, ws=None, stream=None, outputs=None):
         B = int(q_route.shape[0])
+        _expect(q_route, (B, self.h_r, 128), torch.float32, "q_route", self.device)
+        if exclude is not None:
+            _expect(exclude, (B, (self.n_docs + 31) // 32), torch.int32, "exclude", self.device)
         if ws is None:
             ws = self.workspace(MSA_DECODE, B, self.h_kv, k)
         if outputs is None:
@@ -301,22 +370,38 @@ class Bank:
             scores = torch.empty((B, k), dtype=torch.float32, device=self.device)
         else:
             ids, scores = outputs
+        _expect(ids, (B, k), torch.int32, "ids", self.device)
+        _expect(scores, (B, k), torch.float32, "scores", self.device)
         _check(lib.msa_route(self.handle, _ptr(q_route), B, k, _ptr(exclude), _ptr(ids),
-                             _ptr(scores), _ptr(ws), ws.numel(), _stream(stream)), "msa_route")
+                             _ptr(scores), _ptr(ws), ws.numel() * ws.element_size(),
+                             _stream(stream)), "msa_route")
         return ids, scores
 
     def attend(self, q, q_pos: int, ids, k_loc, v_loc, L_loc: int, mode=MSA_DECODE, block: int = 64, splits: int = 0, ws=None, src=None,
                out=None, stream=None, memory=MSA_MEMORY_TOKENS):
-        n_q, h_q = int(q.shape[0]), int(q.shape[1])
+        n_q, h_q = self._check_queries(q)
+        prefill = mode == MSA_PREFILL
+        n_groups = n_q // block if prefill and block > 0 else n_q
         k = 0 if ids is None else int(ids.shape[1])
+        if ids is not None:
+            _expect(ids, (n_groups, k), torch.int32, "ids", self.device)
+        self._check_local(k_loc, v_loc, L_loc, 1 if prefill else n_q)
         if ws is None:
             ws = self.workspace(mode, n_q, h_q, k, block, 1, splits)
         if out is None:
             out = torch.empty((n_q, h_q, 128), dtype=torch.float32, device=self.device)
+        _expect(out, (n_q, h_q, 128), torch.float32, "out", self.device)
         sk, sv, so, sl = (None, None, None, None) if src is None else src
+        if src is not None:
+            for t, dt, name in ((sk, self.dtype, "src_k"), (sv, self.dtype, "src_v"),
+                                (so, torch.int64, "src_off"), (sl, torch.int32, "src_len")):
+                if t is None or t.dtype != dt or not t.is_contiguous():
+                    raise ValueError(f"{name}: a contiguous {dt} tensor is required")
+            if so.numel() != sl.numel():
+                raise ValueError("src_off and src_len differ in length")
         a = AttendArgs(mode, n_q, h_q, _ptr(q), int(q_pos), _ptr(ids), k, block, _ptr(k_loc),
                        _ptr(v_loc), int(L_loc), _ptr(out), _ptr(ws),
-                       ws.numel(), splits, _ptr(sk), _ptr(sv), _ptr(so), _ptr(sl),
+                       ws.numel() * ws.element_size(), splits, _ptr(sk), _ptr(sv), _ptr(so), _ptr(sl),
                        0 if sl is None else int(sl.numel()), int(memory))
         _check(lib.msa_attend(self.handle, C.byref(a), _stream(stream)), "msa_attend")
         return out
@@ -326,8 +411,21 @@ class Bank:
              ws=None, staging=None, outputs=None, stream=None, copy_stream=None,
              memory=MSA_MEMORY_TOKENS):
         """Returns (ids [hops, n_groups, k], scores, out [hops, n_q, h_q, 128], stats)."""
-        n_q, h_q = int(q.shape[0]), int(q.shape[1])
-        n_groups = n_q // block if mode == MSA_PREFILL else n_q
+        n_q, h_q = self._check_queries(q)
+        prefill = mode == MSA_PREFILL
+        n_groups = n_q // block if prefill and block > 0 else n_q
+        if prefill:
+            if route_tokens is None:
+                raise ValueError("prefill routes with route_tokens")
+            _expect(route_tokens, (n_q, self.h_r, 128), self.dtype, "route_tokens", self.device)
+        else:
+            _expect(q_route, (n_q, self.h_r, 128), torch.float32, "q_route", self.device)
+        self._check_local(k_loc, v_loc, L_loc, 1 if prefill else n_q)
+        if hops > 1:
+            _expect(w_proj, (128, h_q * 128), torch.float32, "w_proj", self.device)
+        if exclude is not None:
+            _expect(exclude, (n_groups, (self.n_docs + 31) // 32), torch.int32, "exclude",
+                    self.device)
         if ws is None:
             ws = self.workspace(mode, n_q, h_q, k, block, hops, splits)
         if (self.kv_host and staging is None and getattr(self, "cache", None) is None
@@ -339,11 +437,16 @@ class Bank:
             out = torch.empty((hops, n_q, h_q, 128), dtype=torch.float32, device=self.device)
         else:
             ids, scores, out = outputs
+        _expect(ids, (hops, n_groups, k), torch.int32, "ids", self.device)
+        _expect(scores, (hops, n_groups, k), torch.float32, "scores", self.device)
+        _expect(out, (hops, n_q, h_q, 128), torch.float32, "out", self.device)
         a = StepArgs(mode, n_q, h_q, k, _ptr(q), int(q_pos), _ptr(q_route), _ptr(route_tokens),
                      block, _ptr(k_loc), _ptr(v_loc), int(L_loc), hops,
                      _ptr(w_proj), int(bool(exclude_selected)), _ptr(exclude), _ptr(ids),
-                     _ptr(scores), _ptr(out), _ptr(ws), ws.numel(), _ptr(staging),
-                     0 if staging is None else staging.numel(), splits, int(memory))
+                     _ptr(scores), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                     _ptr(staging),
+                     0 if staging is None else staging.numel() * staging.element_size(), splits,
+                     int(memory))
         st = StepStats()
         cs = None if copy_stream is None else _stream(copy_stream)
         _check(lib.msa_step(self.handle, C.byref(a), _stream(stream), cs, C.byref(st)),
