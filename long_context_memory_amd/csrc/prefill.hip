@@ -86,6 +86,15 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, int voff, void* 
                                            16, voff, 0, 0, 0);
 }
 
+// max over lanes l and l ^ 32: a swap of the wave's halves (one VALU op, no
+// LDS round trip); with the same register as both operands, the two results
+// hold this lane's value and its partner's in some order
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // LDS row r of a staged K tile holds token perm16(r): bits 2 and 3 swapped.
 __device__ __forceinline__ int perm16(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
@@ -322,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillP p) {
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[mt][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));  // relative to m_use
+    mx = max_xor32(mx);  // relative to m_use
     const bool grow = mx + m_use > m_run + 8.f;
     if (__builtin_amdgcn_readfirstlane((int)(__ballot(grow) != 0))) {
       if (grow) {
