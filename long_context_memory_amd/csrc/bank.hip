@@ -199,18 +199,20 @@ __global__ __launch_bounds__(256) void rope_queries_kernel(const T* __restrict__
                                                            int h_q, int pos0, int pos_step,
                                                            const double* __restrict__ inv_freq,
                                                            double scale, T* __restrict__ out) {
-  // one thread per (query row, head, channel pair)
+  // one thread per (query row, channel pair); the angle depends only on the
+  // row's position, so its sine and cosine serve every head of the row
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)n_q * h_q * 64) return;
+  if (idx >= (int64_t)n_q * 64) return;
   const int pair = (int)(idx & 63);
-  const int64_t row = idx >> 6;  // i * h_q + h
-  const int i = (int)(row / h_q);
+  const int i = (int)(idx >> 6);
   double sn, cs;
   sincos((double)(pos0 + (int64_t)i * pos_step) * inv_freq[pair], &sn, &cs);
-  const size_t o = (size_t)row * kD;
-  const double x1 = St<T>::load(q[o + pair]), x2 = St<T>::load(q[o + 64 + pair]);
-  out[o + pair] = St<T>::store((x1 * cs - x2 * sn) * scale);
-  out[o + 64 + pair] = St<T>::store((x2 * cs + x1 * sn) * scale);
+  for (int h = 0; h < h_q; ++h) {
+    const size_t o = ((size_t)i * h_q + h) * kD;
+    const double x1 = St<T>::load(q[o + pair]), x2 = St<T>::load(q[o + 64 + pair]);
+    out[o + pair] = St<T>::store((x1 * cs - x2 * sn) * scale);
+    out[o + 64 + pair] = St<T>::store((x2 * cs + x1 * sn) * scale);
+  }
 }
 
 KLayout bank_layout(const Bank& bk, int doc0, int doc1) {
@@ -375,7 +377,7 @@ hipError_t launch_rope_queries(const Bank& bk, const void* q, int n_q, int h_q, 
                                int pos_step, void* q_rot, hipStream_t s) {
   if (n_q == 0) return hipSuccess;
   const double scale = 1.4426950408889634 / sqrt((double)kD);  // log2(e) / sqrt(d)
-  const unsigned grid = (unsigned)(((int64_t)n_q * h_q * 64 + 255) / 256);
+  const unsigned grid = (unsigned)(((int64_t)n_q * 64 + 255) / 256);
   if (bk.desc.dtype == MSA_BF16)
     hipLaunchKernelGGL(rope_queries_kernel<uint16_t>, dim3(grid), dim3(256), 0, s,
                        (const uint16_t*)q, n_q, h_q, pos0, pos_step, bk.d_inv_freq, scale,

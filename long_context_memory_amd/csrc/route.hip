@@ -279,11 +279,16 @@ __global__ __launch_bounds__(128) void block_mean_kernel(const T* __restrict__ r
                                                          int block, float* __restrict__ qo) {
   const int g = blockIdx.x, h = blockIdx.y, i = threadIdx.x;
   double s = 0.0;
-  for (int t = 0; t < block; ++t) {
-    const T x = rt[((size_t)(g * block + t) * h_r + h) * kD + i];
-    if constexpr (sizeof(T) == 2) s += (double)bf16_to_f32(x);
-    else s += (double)x;
+  int t = 0;
+  // eight loads in flight ahead of the (sequential) float64 sum
+  for (; t + 8 <= block; t += 8) {
+    T x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = rt[((size_t)(g * block + t + u) * h_r + h) * kD + i];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += St<T>::load(x[u]);
   }
+  for (; t < block; ++t) s += St<T>::load(rt[((size_t)(g * block + t) * h_r + h) * kD + i]);
   qo[((size_t)g * h_r + h) * kD + i] = (float)(s / (double)block);
 }
 
