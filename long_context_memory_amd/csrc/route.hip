@@ -66,9 +66,12 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
     v[u] = *reinterpret_cast<const uint4*>(rows + ((size_t)min(row, nc - 1) * VPR + col) *
                                                       (16 / sizeof(T)));
   }
+  // query slice u covers queries 8u .. 8u + 7 (workgroup-uniform bound)
+  const int nslice = (npass + 7) / 8;
   float4 qv[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
+    if (u >= nslice) break;
     const int f = u * 256 + threadIdx.x;
     const int qi = f / (kD / 4), col = f % (kD / 4);
     qv[u] = qi < npass ? *reinterpret_cast<const float4*>(q + ((size_t)(bg + qi) * h_r + h) * kD +
@@ -88,6 +91,7 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
   }
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
+    if (u >= nslice) break;
     const int f = u * 256 + threadIdx.x;
     const int qi = f / (kD / 4), col = f % (kD / 4);
     if constexpr (kBF) {
@@ -170,6 +174,152 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
     // holds the max of [lane, min(lane + 2o, end)); then the query norm
     // (x -> x * s with s > 0 is monotone, so it commutes with the max)
     float m = ((a0 + a1) + (a2 + a3)) * inv_k;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float u = __shfl_down(m, o, 64);
+      if (lane + o < end) m = fmaxf(m, u);
+    }
+    if (start) piecemax[((size_t)(bg + qi) * h_r + h) * P + piece0 + seg] = m * s_iq[qi];
+  }
+}
+
+// Router queries split once per launch for the matrix-core scan: row
+// (query, head) of 128 floats -> 64 words of bfloat16 "hi" pairs, then 64
+// words of "lo" pairs (q = hi + lo + r, |r| <= 2^-17 |q|), and 1/||q||.
+// The arithmetic (and the order of the norm's sum) is that of the vector
+// scan's staging.  32 threads per row, one float4 each.
+__global__ __launch_bounds__(256) void route_prep_kernel(const float* __restrict__ q, int rows,
+                                                         uint32_t* __restrict__ words,
+                                                         float* __restrict__ inv_q) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = t / (kD / 4);
+  const int col = (int)(t % (kD / 4));
+  const bool ok = row < rows;
+  const float4 v = ok ? *reinterpret_cast<const float4*>(q + row * kD + col * 4)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+  const float x[4] = {v.x, v.y, v.z, v.w};
+  uint32_t hi[2], lo[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const uint32_t h0 = f32_to_bf16(x[2 * e]), h1 = f32_to_bf16(x[2 * e + 1]);
+    hi[e] = h0 | (h1 << 16);
+    lo[e] = f32_to_bf16(x[2 * e] - __uint_as_float(h0 << 16)) |
+            (f32_to_bf16(x[2 * e + 1] - __uint_as_float(h1 << 16)) << 16);
+  }
+  float ss = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  ss += __shfl_xor(ss, 1, 64);
+  ss += __shfl_xor(ss, 2, 64);
+  ss += __shfl_xor(ss, 4, 64);
+  ss += __shfl_xor(ss, 8, 64);
+  ss += __shfl_xor(ss, 16, 64);
+  if (!ok) return;
+  *reinterpret_cast<uint2*>(words + row * kD + col * 2) = make_uint2(hi[0], hi[1]);
+  *reinterpret_cast<uint2*>(words + row * kD + 64 + col * 2) = make_uint2(lo[0], lo[1]);
+  if (col == 0) inv_q[row] = ss > 0.f ? 1.0f / sqrtf(ss) : 0.0f;
+}
+
+// Routing scan on the matrix cores, for bf16 keys and passes of 32 or more
+// queries, where the scan is a dense contraction ([queries x 128] times
+// [128 x chunks]) that would otherwise be VALU-bound.  Workgroup = one (tile
+// of 64 chunks, router head); its key tile and every operand it needs are
+// loaded in one memory round trip.  Wave w computes one 32x32 block of
+// cosines, chunks 32*(w&1).. by queries 32*(w>>1).., with
+// v_mfma_f32_32x32x16_bf16: the float32 query enters as its two bfloat16
+// terms, read straight from the prepared rows, two MFMAs per 16-channel step,
+// fp32 accumulation, so the accuracy is that of the vector scan.  The blocks
+// go through LDS as [query][chunk] rows, then each wave folds its queries'
+// rows into per-document maxima with the segmented max.
+typedef __bf16 rbf16x8_t __attribute__((ext_vector_type(8)));
+typedef float rf32x16_t __attribute__((ext_vector_type(16)));
+
+__global__ __launch_bounds__(256) void route_scan_mfma_kernel(
+    const uint16_t* __restrict__ kr, const float* __restrict__ inv_norm,
+    const uint32_t* __restrict__ qwords, const float* __restrict__ inv_q, int B, int bg, int h_r,
+    int64_t C, int64_t Cs, const int32_t* __restrict__ chunk_doc,
+    const int32_t* __restrict__ tile_piece0, int P, float* __restrict__ piecemax) {
+  constexpr int RowF = kD / 2 + 4;  // 32-bit words per staged key row (+16 B pad)
+  __shared__ __attribute__((aligned(16))) uint32_t s_rows[64 * RowF];
+  __shared__ float s_cos[64 * 65];  // [query][chunk], rows padded to 65
+  __shared__ float s_iq[64], s_ik[64];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, l32 = lane & 31, hl = lane >> 5;
+  const int tile = blockIdx.x, h = blockIdx.y;
+  const int64_t c0 = (int64_t)tile * kRouteTile;
+  const int nc = (int)min((int64_t)kRouteTile, C - c0);
+  const int npass = min(64, B - bg);
+  const uint16_t* rows = kr + ((size_t)h * Cs + c0) * kD;
+  const int cb = wave & 1, qb = wave >> 1;
+  const bool busy = 32 * qb < npass;  // wave-uniform
+
+  // ---- every global load first: key tile, this wave's query fragments
+  // (query 32*qb + l32, channels 16*kk + 8*hl .. +7, hi then lo), the tile's
+  // chunk table and norms
+  constexpr int NLD = 64 * 16 / 256;  // 16-byte vectors of the tile per thread
+  uint4 v[NLD];
+#pragma unroll
+  for (int u = 0; u < NLD; ++u) {
+    const int f = u * 256 + threadIdx.x;
+    const int row = f / 16, col = f % 16;
+    v[u] = *reinterpret_cast<const uint4*>(rows + ((size_t)min(row, nc - 1) * 16 + col) * 8);
+  }
+  uint4 qh[8], ql[8];
+  {
+    const int qi = 32 * qb + l32;
+    const bool qok = busy && qi < npass;
+    const uint32_t* qw = qwords + ((size_t)(bg + (qok ? qi : 0)) * h_r + h) * kD + 4 * hl;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      qh[kk] = qok ? *reinterpret_cast<const uint4*>(qw + 8 * kk) : make_uint4(0, 0, 0, 0);
+      ql[kk] = qok ? *reinterpret_cast<const uint4*>(qw + 64 + 8 * kk) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  const int my_doc = lane < nc ? chunk_doc[c0 + lane] : -1;
+  if (threadIdx.x < 64) {
+    const int i = threadIdx.x;
+    s_ik[i] = i < nc ? inv_norm[(size_t)h * Cs + c0 + i] : 0.f;
+    s_iq[i] = i < npass ? inv_q[(size_t)(bg + i) * h_r + h] : 0.f;
+  }
+  const int piece0 = tile_piece0[tile];
+#pragma unroll
+  for (int u = 0; u < NLD; ++u) {
+    const int f = u * 256 + threadIdx.x;
+    const int row = f / 16, col = f % 16;
+    *reinterpret_cast<uint4*>(s_rows + row * RowF + col * 4) = row < nc ? v[u] : make_uint4(0, 0, 0, 0);
+  }
+  const int prev_doc = __shfl_up(my_doc, 1, 64);
+  const bool start = lane < nc && (lane == 0 || my_doc != prev_doc);
+  const uint64_t starts = __ballot(start);
+  const uint64_t later = lane == 63 ? 0 : starts & (~0ull << (lane + 1));
+  const int end = later ? __builtin_ctzll(later) : nc;
+  const int seg = __builtin_popcountll(starts & ((1ull << lane) - 1));
+  __syncthreads();
+
+  // ---- wave w: cosines of chunks 32*cb + row by queries 32*qb + column
+  if (busy) {
+    rf32x16_t acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    const uint32_t* krow = s_rows + (32 * cb + l32) * RowF + 4 * hl;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const rbf16x8_t a = __builtin_bit_cast(rbf16x8_t, *reinterpret_cast<const uint4*>(krow + 8 * kk));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(rbf16x8_t, qh[kk]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(rbf16x8_t, ql[kk]), acc, 0, 0, 0);
+    }
+    // element e: chunk row 8*(e/4) + 4*hl + e%4 of the block, query column l32
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int c = 32 * cb + 8 * (e >> 2) + 4 * hl + (e & 3);
+      s_cos[(32 * qb + l32) * 65 + c] = acc[e] * s_ik[c];
+    }
+  }
+  __syncthreads();
+
+  // ---- wave w folds queries w, w+4, ...: lane c holds chunk c's cosine
+  const int nq = max(0, min(16, (npass - wave + 3) / 4));
+  for (int j = 0; j < nq; ++j) {
+    const int qi = wave + 4 * j;
+    float m = s_cos[qi * 65 + lane];
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const float u = __shfl_down(m, o, 64);
@@ -316,20 +466,40 @@ __global__ __launch_bounds__(256) void project_kernel(const float* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_route_scan(const Bank& bk, const float* q_route, int B, float* piecemax,
-                             hipStream_t s) {
+size_t route_prep_bytes(const Bank& bk, int B) {
+  return (size_t)B * bk.desc.h_r * (kD * 4 + 4);
+}
+
+hipError_t launch_route_scan(const Bank& bk, const float* q_route, int B, void* prep,
+                             float* piecemax, hipStream_t s) {
   const dim3 grid((unsigned)bk.n_tiles, (unsigned)bk.desc.h_r);
+  const int rows = B * bk.desc.h_r;
+  uint32_t* qwords = (uint32_t*)prep;
+  float* inv_q = (float*)((char*)prep + (size_t)rows * kD * 4);
+  bool prepped = false;
   for (int bg = 0; bg < B; bg += 64) {
-    if (bk.desc.dtype == MSA_BF16)
+    if (bk.desc.dtype == MSA_BF16 && std::min(64, B - bg) >= 32) {
+      if (!prepped) {
+        const unsigned pg = (unsigned)(((int64_t)rows * (kD / 4) + 255) / 256);
+        hipLaunchKernelGGL(route_prep_kernel, dim3(pg), dim3(256), 0, s, q_route, rows, qwords,
+                           inv_q);
+        prepped = true;
+      }
+      hipLaunchKernelGGL(route_scan_mfma_kernel, grid, dim3(256), 0, s,
+                         (const uint16_t*)bk.desc.kr, bk.desc.inv_norm, qwords, inv_q, B, bg,
+                         bk.desc.h_r, bk.n_chunks, bk.chunk_stride, bk.d_chunk_doc, bk.d_tile_piece0,
+                         bk.n_pieces, piecemax);
+    } else if (bk.desc.dtype == MSA_BF16) {
       hipLaunchKernelGGL(route_scan_kernel<uint16_t>, grid, dim3(256), 0, s,
                          (const uint16_t*)bk.desc.kr, bk.desc.inv_norm, q_route, B, bg,
                          bk.desc.h_r, bk.n_chunks, bk.chunk_stride, bk.d_chunk_doc, bk.d_tile_piece0,
                          bk.n_pieces, piecemax);
-    else
+    } else {
       hipLaunchKernelGGL(route_scan_kernel<float>, grid, dim3(256), 0, s,
                          (const float*)bk.desc.kr, bk.desc.inv_norm, q_route, B, bg,
                          bk.desc.h_r, bk.n_chunks, bk.chunk_stride, bk.d_chunk_doc, bk.d_tile_piece0,
                          bk.n_pieces, piecemax);
+    }
   }
   return hipGetLastError();
 }

@@ -107,6 +107,21 @@ def test_route_matches_oracle(msa, name):
         assert all(int(ids[b, 0]) == c["target_doc"] for b in range(w.B))
 
 
+@pytest.mark.parametrize("B", [32, 40, 64, 70])
+def test_route_large_batches_match_oracle(msa, B):
+    # 32 or more queries per pass take the matrix-core scan (70: a pass of 64
+    # and a pass of 6 on the vector scan); the bank's last tile is ragged
+    c = decode_case(msa, "decode_small")
+    w = c["w"]
+    g = torch.Generator(device=DEV)
+    g.manual_seed(7000 + B)
+    qr = torch.randn((B, w.h_r, 128), generator=g, device=DEV)
+    ids, scores = c["bank"].route(qr, w.k)
+    torch.cuda.synchronize()
+    so = O.cosine_doc_scores(M.np64(qr), c["kr_o"], c["inv_o"], w.doc_len)
+    M.check_topk(ids.cpu().numpy(), scores.cpu().numpy(), so, w.k)
+
+
 @pytest.mark.parametrize("name", ["decode_small"])
 def test_route_exclusion_and_k_equals_n(msa, name):
     c = decode_case(msa, name)
