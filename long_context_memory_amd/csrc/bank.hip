@@ -207,6 +207,7 @@ __global__ __launch_bounds__(256) void rope_queries_kernel(const T* __restrict__
   const int i = (int)(idx >> 6);
   double sn, cs;
   sincos((double)(pos0 + (int64_t)i * pos_step) * inv_freq[pair], &sn, &cs);
+#pragma unroll 8
   for (int h = 0; h < h_q; ++h) {
     const size_t o = ((size_t)i * h_q + h) * kD;
     const double x1 = St<T>::load(q[o + pair]), x2 = St<T>::load(q[o + 64 + pair]);
