@@ -166,14 +166,17 @@ def prefill_bench(steps, warmup, splits=0):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    msa.timer_reserve(2 * steps)  # attention + routing intervals, events made up front
     msa.timer_enable(True)
     msa.timer_read(msa.MSA_TIMER_ATTENTION)
+    msa.timer_read(msa.MSA_TIMER_ROUTE)
     t0 = time.perf_counter()
     for _ in range(steps):
         step()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     att_ms, att_n = msa.timer_read(msa.MSA_TIMER_ATTENTION)
+    msa.timer_read(msa.MSA_TIMER_ROUTE)
     msa.timer_enable(False)
     # algorithmic flops: QK^T and PV over every unmasked (query, key) pair
     doc_pairs = w.B * w.k * 2048
@@ -310,14 +313,17 @@ def interleave_bench(steps, warmup):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    msa.timer_reserve(2 * steps * w.hops)  # attention + routing intervals, events made up front
     msa.timer_enable(True)
     msa.timer_read(msa.MSA_TIMER_ATTENTION)
+    msa.timer_read(msa.MSA_TIMER_ROUTE)
     t0 = time.perf_counter()
     for _ in range(steps):
         step()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     att_ms, att_n = msa.timer_read(msa.MSA_TIMER_ATTENTION)
+    msa.timer_read(msa.MSA_TIMER_ROUTE)
     msa.timer_enable(False)
     ids = outs[0].cpu().numpy()
     lens = np.asarray(w.doc_len, dtype=np.int64)
@@ -338,7 +344,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=1000,
+                    help="untimed steps first (about 0.15 s: the chip reaches its steady state)")
     ap.add_argument("--batches", type=int, default=4, help="rotating query batches")
     ap.add_argument("--streams", type=int, default=2, help="HIP streams batches alternate over")
     ap.add_argument("--splits", type=int, default=0, help="attention splits (0 = automatic)")
@@ -406,8 +413,10 @@ def main():
         step(i)
     torch.cuda.synchronize()
     log("timed")
+    msa.timer_reserve(2 * args.steps)  # attention + routing intervals, events made up front
     msa.timer_enable(True)
     msa.timer_read(msa.MSA_TIMER_ATTENTION)
+    msa.timer_read(msa.MSA_TIMER_ROUTE)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -415,7 +424,7 @@ def main():
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     att_ms, att_n = msa.timer_read(msa.MSA_TIMER_ATTENTION)
-    msa.timer_read(msa.MSA_TIMER_ROUTE)
+    rt_ms, rt_n = msa.timer_read(msa.MSA_TIMER_ROUTE)
     msa.timer_enable(False)
     log("done")
     ms = dt * 1e3 / args.steps
@@ -444,6 +453,14 @@ def main():
                      # whole-run rate counts every byte once over the wall clock
                      "aggregate_GBs": kv_bytes * args.steps / dt / 1e9,
                      "aggregate_frac": kv_bytes * args.steps / dt / 1e9 / HBM_PEAK_GBS},
+        # the routing scan streams every routing key and its norm once per step;
+        # timed inside the two-stream step, where it overlaps the other
+        # stream's attention
+        "routing": {"kernel": "cosine routing scan (overlapped with attention)", "bound": "hbm",
+                    "bytes_per_launch": w.C * w.h_r * (128 * 2 + 4),
+                    "avg_launch_us": rt_ms * 1e3 / max(rt_n, 1), "launches": rt_n,
+                    "achieved": w.C * w.h_r * (128 * 2 + 4) / (rt_ms * 1e-3 / max(rt_n, 1)) / 1e9,
+                    "unit": "GB/s", "peak": HBM_PEAK_GBS},
         "tokens_attended_per_s": qps * (w.k * 512 + w.L_loc),
         "bank_build_s": build_s,
     }
@@ -471,14 +488,17 @@ def main():
         for i in range(args.warmup):
             pstep(i)
         torch.cuda.synchronize()
+        msa.timer_reserve(2 * args.pooled_steps)
         msa.timer_enable(True)
         msa.timer_read(msa.MSA_TIMER_ATTENTION)
+        msa.timer_read(msa.MSA_TIMER_ROUTE)
         t0 = time.perf_counter()
         for i in range(args.pooled_steps):
             pstep(i)
         torch.cuda.synchronize()
         pdt = time.perf_counter() - t0
         pms, pn = msa.timer_read(msa.MSA_TIMER_ATTENTION)
+        msa.timer_read(msa.MSA_TIMER_ROUTE)
         msa.timer_enable(False)
         entries = w.k * (512 // 256)
         # bytes: the pooled K rows and V entries of 16 documents + the local K/V

@@ -334,10 +334,16 @@ int msa_step(const msa_bank* bank, const msa_step_args* args, void* stream,
  * those events, returns the accumulated milliseconds and the number of
  * launches since the last read, and clears them.
  *   which: MSA_TIMER_ATTENTION (decode or prefill attention kernel),
- *          MSA_TIMER_ROUTE (routing scan). */
+ *          MSA_TIMER_ROUTE (routing scan: the query split, if any, and the
+ *          scan launches of one call, as one interval). */
 enum { MSA_TIMER_ATTENTION = 0, MSA_TIMER_ROUTE = 1 };
 int msa_timer_enable(int on);
 int msa_timer_read(int which, double* total_ms, int64_t* launches);
+/* Create the events for `launches` timed launches ahead of a timed region
+ * (events are otherwise created on first use, on the host, inside it).
+ * Synchronous; MSA_EINVAL if launches < 0, MSA_EHIP if HIP cannot create
+ * an event. */
+int msa_timer_reserve(int64_t launches);
 
 #ifdef __cplusplus
 }

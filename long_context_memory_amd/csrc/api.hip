@@ -191,6 +191,16 @@ int msa_timer_enable(int on) {
   return MSA_OK;
 }
 
+int msa_timer_reserve(int64_t launches) {
+  if (launches < 0) return fail(MSA_EINVAL, "timer_reserve: launches < 0");
+  while ((int64_t)g_timer.pool.size() < 2 * launches) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return fail(MSA_EHIP, "hipEventCreate");
+    g_timer.pool.push_back(e);
+  }
+  return MSA_OK;
+}
+
 int msa_timer_read(int which, double* total_ms, int64_t* launches) {
   if (which < 0 || which > 1 || !total_ms || !launches) return fail(MSA_EINVAL, "timer_read");
   double tot = 0.0;

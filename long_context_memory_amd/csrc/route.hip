@@ -477,6 +477,7 @@ hipError_t launch_route_scan(const Bank& bk, const float* q_route, int B, void* 
   uint32_t* qwords = (uint32_t*)prep;
   float* inv_q = (float*)((char*)prep + (size_t)rows * kD * 4);
   bool prepped = false;
+  timer_mark(1, true, s);
   for (int bg = 0; bg < B; bg += 64) {
     if (bk.desc.dtype == MSA_BF16 && std::min(64, B - bg) >= 32) {
       if (!prepped) {
@@ -501,6 +502,7 @@ hipError_t launch_route_scan(const Bank& bk, const float* q_route, int B, void* 
                          bk.n_pieces, piecemax);
     }
   }
+  timer_mark(1, false, s);
   return hipGetLastError();
 }
 

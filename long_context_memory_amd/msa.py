@@ -25,7 +25,7 @@ EXPORTS = [
     "msa_status_string", "msa_last_error", "msa_version", "msa_bank_create",
     "msa_bank_destroy", "msa_bank_get_info", "msa_build_bank", "msa_prepare_local",
     "msa_workspace_bytes", "msa_staging_bytes", "msa_route", "msa_attend", "msa_step",
-    "msa_timer_enable", "msa_timer_read", "msa_bank_set_cache", "msa_cache_slot_bytes",
+    "msa_timer_enable", "msa_timer_read", "msa_timer_reserve", "msa_bank_set_cache", "msa_cache_slot_bytes",
     "msa_bank_append", "msa_pooled_sizes", "msa_bank_set_pooled", "msa_build_pooled",
 ]
 MSA_TIMER_ATTENTION, MSA_TIMER_ROUTE = 0, 1
@@ -106,7 +106,8 @@ def _load():
     lib.msa_step.argtypes = [vp, C.POINTER(StepArgs), vp, vp, C.POINTER(StepStats)]
     lib.msa_timer_enable.argtypes = [C.c_int]
     lib.msa_timer_read.argtypes = [C.c_int, C.POINTER(C.c_double), C.POINTER(i64)]
-    for f in (lib.msa_timer_enable, lib.msa_timer_read):
+    lib.msa_timer_reserve.argtypes = [i64]
+    for f in (lib.msa_timer_enable, lib.msa_timer_read, lib.msa_timer_reserve):
         f.restype = C.c_int
     for f in (lib.msa_bank_create, lib.msa_bank_destroy, lib.msa_bank_get_info,
               lib.msa_build_bank, lib.msa_prepare_local, lib.msa_route, lib.msa_attend,
@@ -120,6 +121,11 @@ lib = _load()
 
 def timer_enable(on: bool = True):
     _check(lib.msa_timer_enable(int(bool(on))), "msa_timer_enable")
+
+
+def timer_reserve(launches: int):
+    """Create the events of `launches` timed launches before a timed region."""
+    _check(lib.msa_timer_reserve(int(launches)), "msa_timer_reserve")
 
 
 def timer_read(which: int):
