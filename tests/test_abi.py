@@ -85,6 +85,11 @@ def test_null_arguments(msa):
     assert msa.lib.msa_step(None, None, None, None, None) == msa.MSA_EINVAL
     assert msa.lib.msa_workspace_bytes(None, 0, 1, 32, 16, 64, 1, 0) == 0
     assert msa.lib.msa_build_bank(None, 0, 1, None, None, None, None) == msa.MSA_EINVAL
+    ms, n = C.c_double(), C.c_int64()
+    assert msa.lib.msa_timer_read(2, C.byref(ms), C.byref(n)) == msa.MSA_EINVAL
+    assert msa.lib.msa_timer_read(0, None, None) == msa.MSA_EINVAL
+    assert msa.lib.msa_timer_reserve(-1) == msa.MSA_EINVAL
+    assert msa.lib.msa_timer_reserve(0) == msa.MSA_OK  # nothing to create: no device needed
 
 
 def test_build_script_flags():
