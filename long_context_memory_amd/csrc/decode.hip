@@ -21,6 +21,9 @@
 //     reduction of the accumulators happens once, at the end.
 //   - the "gather" is an indirection: per (query, head) the workgroup reads
 //     the k selected ids and the document table and walks the tiles in place.
+//   - decode queries arrive raw: the prologue rotates them at q_pos (float64,
+//     one (head, pair) per thread, into LDS), so no separate RoPE launch
+//     precedes the kernel.
 #include <algorithm>
 #include <cmath>
 

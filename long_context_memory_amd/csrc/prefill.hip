@@ -11,14 +11,16 @@
 // waves per SIMD so one wave's softmax overlaps the other's matrix work.
 // Each 64-token K/V tile is staged once in LDS and shared by all 256 rows:
 // 256 flop per byte of K/V.  Tiles stream through a 4-stage LDS ring filled
-// by direct global->LDS loads (no register staging), three tiles in flight
-// while one is consumed.  Both contractions use v_mfma_f32_32x32x16_bf16 with
+// by direct global->LDS loads through buffer descriptors (no register
+// staging), three tiles in flight while one is consumed.  Both contractions use v_mfma_f32_32x32x16_bf16 with
 // fp32 accumulation.  Scores are computed transposed, S^T = K . Q^T (tokens
 // x rows), so the accumulator of S^T is already laid out as the B operand
 // P^T of O^T = V^T . P^T; K rows are permuted inside each 16-row group when
 // staged so that every lane's 8 probabilities of a 16-token k-step are 8
 // consecutive tokens, i.e. one 16-byte V^T read.  Online softmax in base 2
-// (queries are pre-scaled by log2 e / sqrt(d)).
+// (queries are pre-scaled by log2 e / sqrt(d)).  With a single token split
+// the kernel writes the normalised output; otherwise per-split partials
+// that prefill_combine_kernel merges.
 #include <algorithm>
 #include <type_traits>
 
