@@ -30,12 +30,21 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def _code_tokens(text):
+    """Source text without comments, whitespace collapsed: what the compiler
+    sees, so that a comment edit does not count as a kernel change."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def _sources_sha256(paths):
     import hashlib
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(_code_tokens(f.read()).encode())
     return h.hexdigest()
 
 
