@@ -64,6 +64,28 @@ def measured_traffic(name):
     return rec["hbm_bytes_per_launch"]
 
 
+def measured_read_rate(n_bytes=1 << 30, reps=20):
+    """HBM rate of the library's read-only stream over a 1 GiB buffer (four
+    times the last-level cache): what a kernel that only reads reaches on
+    this device, next to the datasheet's 8 TB/s."""
+    import torch
+    from long_context_memory_amd import msa
+    buf = torch.ones(n_bytes // 4, dtype=torch.float32, device="cuda")
+    out = torch.empty(msa.MSA_STREAM_READ_BLOCKS, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        msa.stream_read(buf, out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        msa.stream_read(buf, out)
+    e1.record()
+    e1.synchronize()
+    rate = n_bytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf, out
+    torch.cuda.empty_cache()
+    return rate
+
+
 def calibrate_copy(n_bytes=1 << 30, reps=10):
     """A plain device copy of known size (reads and writes n_bytes each), run
     under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE to scale those counters."""
@@ -258,11 +280,19 @@ def host_bank_bench(steps, warmup, cache_gb=0.0):
     for i in range(warmup):
         step(i, False)
     torch.cuda.synchronize()
+    msa.timer_reserve(2 * steps)
+    msa.timer_enable(True)
+    msa.timer_read(msa.MSA_TIMER_ATTENTION)
+    msa.timer_read(msa.MSA_TIMER_ROUTE)
     t0 = time.perf_counter()
     for i in range(steps):
         step(warmup + i, True)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    msa.timer_read(msa.MSA_TIMER_ATTENTION)
+    rt_ms, rt_n = msa.timer_read(msa.MSA_TIMER_ROUTE)
+    msa.timer_enable(False)
+    rt_bytes = w.C * w.h_r * (128 * 2 + 4)  # every routing key (bf16) and its norm
     bank.set_cache(None)
     # a plain pinned host -> device copy of 1 GiB, for the link's own rate
     hsrc = torch.empty(1 << 28, dtype=torch.float32, pin_memory=True)
@@ -281,6 +311,10 @@ def host_bank_bench(steps, warmup, cache_gb=0.0):
             "h2d_GBs": copied[0] / dt / 1e9, "docs_copied_per_step": copied[1] / steps,
             "bytes_copied_per_step": copied[0] / steps, "pinned_copy_GBs": link,
             "h2d_frac_of_pinned_copy": copied[0] / dt / 1e9 / link,
+            "routing": {"bound": "hbm", "bytes_per_launch": rt_bytes,
+                        "avg_launch_us": rt_ms * 1e3 / max(rt_n, 1),
+                        "achieved": rt_bytes / (rt_ms * 1e-3 / max(rt_n, 1)) / 1e9,
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s"},
             "cache": {"slots": slots, "bytes": slots * bank.cache_slot_bytes(),
                       "share_of_documents": slots / w.n_docs,
                       "hit_rate": copied[2] / max(1, copied[1] + copied[2])} if slots else None}
@@ -332,8 +366,11 @@ def interleave_bench(steps, warmup):
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     att_ms, att_n = msa.timer_read(msa.MSA_TIMER_ATTENTION)
-    msa.timer_read(msa.MSA_TIMER_ROUTE)
+    rt_ms, rt_n = msa.timer_read(msa.MSA_TIMER_ROUTE)
     msa.timer_enable(False)
+    rt_bytes = w.C * w.h_r * (128 * 2 + 4)
+    # the scan's arithmetic: 64 queries x every key x 128 channels, multiply-add
+    rt_flops = 2 * w.B * w.C * w.h_r * 128
     ids = outs[0].cpu().numpy()
     lens = np.asarray(w.doc_len, dtype=np.int64)
     tok = int(lens[ids].sum()) + w.hops * w.B * w.L_loc  # union tokens over the 3 hops
@@ -346,7 +383,12 @@ def interleave_bench(steps, warmup):
             "attention": {"bound": "hbm", "bytes_per_step": att_bytes,
                           "avg_launch_us": att_s / w.hops * 1e6,
                           "achieved": att_bytes / att_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": att_bytes / att_s / 1e9 / HBM_PEAK_GBS}}
+                          "frac": att_bytes / att_s / 1e9 / HBM_PEAK_GBS},
+            "routing": {"kernel": "routing scan on the matrix cores (64 queries per pass)",
+                        "bytes_per_launch": rt_bytes, "flops_per_launch": rt_flops,
+                        "avg_launch_us": rt_ms * 1e3 / max(rt_n, 1),
+                        "achieved_GBs": rt_bytes / (rt_ms * 1e-3 / max(rt_n, 1)) / 1e9,
+                        "peak_GBs": HBM_PEAK_GBS}}
 
 
 def main():
@@ -470,6 +512,7 @@ def main():
                     "avg_launch_us": rt_ms * 1e3 / max(rt_n, 1), "launches": rt_n,
                     "achieved": w.C * w.h_r * (128 * 2 + 4) / (rt_ms * 1e-3 / max(rt_n, 1)) / 1e9,
                     "unit": "GB/s", "peak": HBM_PEAK_GBS},
+        "hbm_read_stream_GBs": measured_read_rate(),
         "tokens_attended_per_s": qps * (w.k * 512 + w.L_loc),
         "bank_build_s": build_s,
     }

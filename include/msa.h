@@ -334,8 +334,8 @@ int msa_step(const msa_bank* bank, const msa_step_args* args, void* stream,
  * those events, returns the accumulated milliseconds and the number of
  * launches since the last read, and clears them.
  *   which: MSA_TIMER_ATTENTION (decode or prefill attention kernel),
- *          MSA_TIMER_ROUTE (routing scan: the query split, if any, and the
- *          scan launches of one call, as one interval). */
+ *          MSA_TIMER_ROUTE (routing scan: the scan launches of one call,
+ *          as one interval). */
 enum { MSA_TIMER_ATTENTION = 0, MSA_TIMER_ROUTE = 1 };
 int msa_timer_enable(int on);
 int msa_timer_read(int which, double* total_ms, int64_t* launches);
@@ -344,6 +344,18 @@ int msa_timer_read(int which, double* total_ms, int64_t* launches);
  * Synchronous; MSA_EINVAL if launches < 0, MSA_EHIP if HIP cannot create
  * an event. */
 int msa_timer_reserve(int64_t launches);
+
+/* HBM read-rate probe, for measurement: streams `bytes` of the device buffer
+ * `buf` once (every byte read, nothing else touched) on `stream`, so that
+ * the rate a kernel which only reads can reach on this device can be timed
+ * by the caller and set beside the datasheet's peak.  `buf`: device, 16-byte
+ * aligned; `bytes`: a positive multiple of 16; `out`: device array of
+ * MSA_STREAM_READ_BLOCKS uint32 words that receives a checksum per
+ * workgroup (its only purpose is to keep every load).  Asynchronous;
+ * MSA_EINVAL on a null pointer, misalignment or a bad size, MSA_EHIP if the
+ * launch fails.  Buffers are the caller's. */
+enum { MSA_STREAM_READ_BLOCKS = 2048 };
+int msa_stream_read(const void* buf, int64_t bytes, uint32_t* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmsa.so")
-SOURCES = ["api.hip", "bank.hip", "route.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.hip", "bank.hip", "route.hip", "decode.hip", "prefill.hip", "stream.hip"]
 ARCH = os.environ.get("MSA_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

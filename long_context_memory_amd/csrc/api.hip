@@ -68,7 +68,7 @@ bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
 // Workspace layout shared by msa_workspace_bytes and the entry points.
 struct WsLayout {
-  size_t piecemax = 0, keys = 0, prep = 0, qroute = 0, qrot = 0, part = 0, srcids = 0, srcoff = 0,
+  size_t piecemax = 0, keys = 0, route_end = 0, qroute = 0, qrot = 0, part = 0, srcids = 0, srcoff = 0,
          srclen = 0, excl = 0, total = 0;
 };
 
@@ -86,7 +86,7 @@ WsLayout ws_layout(const Bank& bk, int mode, int n_q, int h_q, int k, int block,
   L.piecemax = take((size_t)bk.desc.h_r * bk.n_pieces * n_groups * sizeof(float));
   L.keys = take((size_t)n_groups * topk_scratch_keys(bk.desc.n_docs, std::max(k, 1)) *
                 sizeof(uint64_t));
-  L.prep = take(route_prep_bytes(bk, n_groups));
+  L.route_end = off;  // msa_route uses the workspace up to here
   L.qroute = take((size_t)n_groups * bk.desc.h_r * kD * sizeof(float));
   L.qrot = take((size_t)n_q * h_q * kD * esz);
   const int G = std::max(1, h_q / bk.desc.h_kv);
@@ -198,6 +198,15 @@ int msa_timer_reserve(int64_t launches) {
     if (hipEventCreate(&e) != hipSuccess) return fail(MSA_EHIP, "hipEventCreate");
     g_timer.pool.push_back(e);
   }
+  return MSA_OK;
+}
+
+int msa_stream_read(const void* buf, int64_t bytes, uint32_t* out, void* stream) {
+  static_assert(MSA_STREAM_READ_BLOCKS == kStreamReadBlocks, "probe grid");
+  if (!buf || !out || bytes <= 0 || bytes % 16 || reinterpret_cast<uintptr_t>(buf) % 16)
+    return fail(MSA_EINVAL, "stream_read: null pointer, misaligned buffer or bytes not a "
+                            "positive multiple of 16");
+  MSA_CHECK_HIP(launch_stream_read(buf, bytes, out, static_cast<hipStream_t>(stream)));
   return MSA_OK;
 }
 
@@ -575,11 +584,11 @@ int msa_route(const msa_bank* b, const float* q_route, int32_t B, int32_t k,
   if (B == 0) return MSA_OK;
   if (!q_route || !ids || !scores || !ws) return fail(MSA_EINVAL, "NULL pointer");
   const WsLayout L = ws_layout(bk, MSA_DECODE, B, bk.desc.h_kv, k, 1, 1, 4);
-  const size_t need = L.prep + align256(route_prep_bytes(bk, B));
+  const size_t need = L.route_end;
   if (ws_bytes < need) return fail(MSA_ENOMEM, "workspace too small for msa_route");
   char* w = (char*)ws;
   hipStream_t s = (hipStream_t)stream;
-  MSA_CHECK_HIP(launch_route_scan(bk, q_route, B, w + L.prep, (float*)(w + L.piecemax), s));
+  MSA_CHECK_HIP(launch_route_scan(bk, q_route, B, (float*)(w + L.piecemax), s));
   MSA_CHECK_HIP(launch_topk(bk, (const float*)(w + L.piecemax), B, k, exclude, nullptr, ids,
                             scores, (uint64_t*)(w + L.keys), s));
   return MSA_OK;
@@ -709,7 +718,7 @@ int msa_step(const msa_bank* b, const msa_step_args* a, void* stream, void* copy
     int32_t* ids = a->ids + (size_t)hop * n_groups * k;
     float* scores = a->scores + (size_t)hop * n_groups * k;
     float* out = a->out + (size_t)hop * out_stride;
-    MSA_CHECK_HIP(launch_route_scan(bk, qr, n_groups, w + L.prep, (float*)(w + L.piecemax), s));
+    MSA_CHECK_HIP(launch_route_scan(bk, qr, n_groups, (float*)(w + L.piecemax), s));
     MSA_CHECK_HIP(launch_topk(bk, (const float*)(w + L.piecemax), n_groups, k, excl,
                               a->exclude_selected ? excl : nullptr, ids, scores,
                               (uint64_t*)(w + L.keys), s));

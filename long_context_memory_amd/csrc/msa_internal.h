@@ -225,10 +225,11 @@ hipError_t launch_rope_queries(const Bank& bk, const void* q, int n_q, int h_q, 
                                int pos_step, void* q_rot, hipStream_t s);
 
 // routing
-// prep: route_prep_bytes(bk, B) of scratch for the router queries' split
-hipError_t launch_route_scan(const Bank& bk, const float* q_route, int B, void* prep,
-                             float* piecemax, hipStream_t s);
-size_t route_prep_bytes(const Bank& bk, int B);
+hipError_t launch_route_scan(const Bank& bk, const float* q_route, int B, float* piecemax,
+                             hipStream_t s);
+// HBM read-rate probe: kStreamReadBlocks workgroups; out holds one word each
+constexpr int kStreamReadBlocks = 2048;
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* out, hipStream_t s);
 hipError_t launch_topk(const Bank& bk, const float* piecemax, int B, int k,
                        const uint32_t* exclude, uint32_t* exclude_out, int32_t* ids,
                        float* scores, uint64_t* keys, hipStream_t s);

@@ -10,6 +10,7 @@
 // top-k later takes the max over a document's pieces and the mean over
 // heads, so no atomics and no initialisation are needed.
 #include <algorithm>
+#include <atomic>
 
 #include "msa_internal.h"
 
@@ -17,30 +18,34 @@ namespace msa {
 namespace {
 
 constexpr int kQPerWave = 16;    // queries a wave scores per pass (64 per workgroup pass)
+constexpr int kScanWgPerCu = 3;  // resident matrix-core scan workgroups per compute unit
 
-// Routing scan.  Workgroup = one (tile of 64 chunks, router head); the tile's
-// key rows are staged once through LDS and every wave takes all 64 rows, one
-// per lane.  The batch's router queries for this head are staged in LDS and
-// read back as broadcasts.  Every global load of the workgroup (key rows,
-// queries, chunk table) is issued before the first LDS store, so a launch
-// costs one memory round trip.  Wave w scores queries w, w+4, ...; for each,
-// lane c holds the cosine of chunk c and a segmented max across lanes folds
-// the tile's runs of equal documents ("pieces") into per-document maxima,
-// written by the lane that starts each run.
-//
-// bf16 keys: the dot products use v_dot2_f32_bf16 with the float32 query
-// split into two bfloat16 terms (q = hi + lo + r, |r| <= 2^-17 |q|), fp32
-// accumulation: one instruction per key element and query, and the packed
-// key row stays in 64 registers.  float32 keys: plain fp32 FMAs.
-template <typename T>
+// Workgroup barrier that waits for this wave's LDS operations only (a
+// __syncthreads() would also wait for every global load in flight).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their maxima
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Routing scan for float32 keys.  Workgroup = one (tile of 64 chunks, router
+// head); the tile's key rows are staged once through LDS and every wave takes
+// all 64 rows, one per lane.  The batch's router queries for this head are
+// staged in LDS and read back as broadcasts.  Every global load of the
+// workgroup (key rows, queries, chunk table) is issued before the first LDS
+// store, so a launch costs one memory round trip.  Wave w scores queries w,
+// w+4, ... with fp32 FMAs; for each, lane c holds the cosine of chunk c and a
+// segmented max across lanes folds the tile's runs of equal documents
+// ("pieces") into per-document maxima, written by the lane that starts each
+// run.
 __global__ __launch_bounds__(256) void route_scan_kernel(
-    const T* __restrict__ kr, const float* __restrict__ inv_norm, const float* __restrict__ q,
+    const float* __restrict__ kr, const float* __restrict__ inv_norm, const float* __restrict__ q,
     int B, int bg, int h_r, int64_t C, int64_t Cs, const int32_t* __restrict__ chunk_doc,
     const int32_t* __restrict__ tile_piece0, int P, float* __restrict__ piecemax) {
   // queries bg .. bg + min(64, B - bg) - 1 (one launch per group of 64)
-  constexpr bool kBF = sizeof(T) == 2;
-  constexpr int RowF = kD * (int)sizeof(T) / 4 + 4;  // 32-bit words per staged row (+16 B pad)
-  constexpr int QW = kD;                             // words per staged query (bf16: hi|lo pairs)
+  constexpr int RowF = kD + 4;  // 32-bit words per staged row (+16 B pad)
+  constexpr int QW = kD;        // words per staged query
   __shared__ __attribute__((aligned(16))) uint32_t s_rows[64 * RowF];
   __shared__ __attribute__((aligned(16))) uint32_t s_q[64 * QW];
   __shared__ float s_iq[64];
@@ -50,21 +55,20 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
   const int64_t c0 = (int64_t)tile * kRouteTile;
   const int nc = (int)min((int64_t)kRouteTile, C - c0);
   const int npass = min(64, B - bg);
-  const T* rows = kr + ((size_t)h * Cs + c0) * kD;  // Cs: rows per head (capacity)
+  const float* rows = kr + ((size_t)h * Cs + c0) * kD;  // Cs: rows per head (capacity)
 
   // ---- every global load first: the tile (64 rows x VPR 16-byte vectors;
   // rows past the end of the bank read the last row and are stored as zero),
   // this pass's queries (64 x 32 float4, rows past the pass skipped) and the
   // tile's chunk table
-  constexpr int VPR = kD * (int)sizeof(T) / 16;
+  constexpr int VPR = kD / 4;
   constexpr int NLD = 64 * VPR / 256;
   uint4 v[NLD];
 #pragma unroll
   for (int u = 0; u < NLD; ++u) {
     const int f = u * 256 + threadIdx.x;
     const int row = f / VPR, col = f % VPR;
-    v[u] = *reinterpret_cast<const uint4*>(rows + ((size_t)min(row, nc - 1) * VPR + col) *
-                                                      (16 / sizeof(T)));
+    v[u] = *reinterpret_cast<const uint4*>(rows + ((size_t)min(row, nc - 1) * VPR + col) * 4);
   }
   // query slice u covers queries 8u .. 8u + 7 (workgroup-uniform bound)
   const int nslice = (npass + 7) / 8;
@@ -94,22 +98,7 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
     if (u >= nslice) break;
     const int f = u * 256 + threadIdx.x;
     const int qi = f / (kD / 4), col = f % (kD / 4);
-    if constexpr (kBF) {
-      // words [qi][0..63]: hi pairs; [qi][64..127]: lo pairs
-      const float x[4] = {qv[u].x, qv[u].y, qv[u].z, qv[u].w};
-      uint32_t hi[2], lo[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const uint32_t h0 = f32_to_bf16(x[2 * e]), h1 = f32_to_bf16(x[2 * e + 1]);
-        hi[e] = h0 | (h1 << 16);
-        lo[e] = f32_to_bf16(x[2 * e] - __uint_as_float(h0 << 16)) |
-                (f32_to_bf16(x[2 * e + 1] - __uint_as_float(h1 << 16)) << 16);
-      }
-      *reinterpret_cast<uint2*>(s_q + qi * QW + col * 2) = make_uint2(hi[0], hi[1]);
-      *reinterpret_cast<uint2*>(s_q + qi * QW + 64 + col * 2) = make_uint2(lo[0], lo[1]);
-    } else {
-      *reinterpret_cast<float4*>(s_q + qi * QW + col * 4) = qv[u];
-    }
+    *reinterpret_cast<float4*>(s_q + qi * QW + col * 4) = qv[u];
     // partial squared norm of the float32 query
     float ss = qv[u].x * qv[u].x + qv[u].y * qv[u].y + qv[u].z * qv[u].z + qv[u].w * qv[u].w;
     // 32 consecutive threads hold one query row: reduce within the 32
@@ -131,7 +120,7 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
   const int seg = __builtin_popcountll(starts & ((1ull << lane) - 1));
   __syncthreads();
 
-  // this lane's key row: bf16 stays packed (16 x uint4), f32 as 32 x uint4
+  // this lane's key row (32 x uint4)
   uint4 kw[VPR];
 #pragma unroll
   for (int c = 0; c < VPR; ++c) kw[c] = *reinterpret_cast<const uint4*>(s_rows + lane * RowF + c * 4);
@@ -143,32 +132,14 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
     const int qi = wave + 4 * j;
     const uint32_t* qj = s_q + qi * QW;
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    if constexpr (kBF) {
 #pragma unroll
-      for (int c = 0; c < 16; c += 2) {
-        const uint4 h0 = *reinterpret_cast<const uint4*>(qj + c * 4);
-        const uint4 l0 = *reinterpret_cast<const uint4*>(qj + 64 + c * 4);
-        const uint4 h1 = *reinterpret_cast<const uint4*>(qj + c * 4 + 4);
-        const uint4 l1 = *reinterpret_cast<const uint4*>(qj + 64 + c * 4 + 4);
-        a0 = dot2_bf16(kw[c].x, h0.x, a0); a0 = dot2_bf16(kw[c].y, h0.y, a0);
-        a0 = dot2_bf16(kw[c].z, h0.z, a0); a0 = dot2_bf16(kw[c].w, h0.w, a0);
-        a1 = dot2_bf16(kw[c].x, l0.x, a1); a1 = dot2_bf16(kw[c].y, l0.y, a1);
-        a1 = dot2_bf16(kw[c].z, l0.z, a1); a1 = dot2_bf16(kw[c].w, l0.w, a1);
-        a2 = dot2_bf16(kw[c + 1].x, h1.x, a2); a2 = dot2_bf16(kw[c + 1].y, h1.y, a2);
-        a2 = dot2_bf16(kw[c + 1].z, h1.z, a2); a2 = dot2_bf16(kw[c + 1].w, h1.w, a2);
-        a3 = dot2_bf16(kw[c + 1].x, l1.x, a3); a3 = dot2_bf16(kw[c + 1].y, l1.y, a3);
-        a3 = dot2_bf16(kw[c + 1].z, l1.z, a3); a3 = dot2_bf16(kw[c + 1].w, l1.w, a3);
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < 32; c += 2) {
-        const float4 x0 = *reinterpret_cast<const float4*>(qj + c * 4);
-        const float4 x1 = *reinterpret_cast<const float4*>(qj + c * 4 + 4);
-        a0 = fmaf(__uint_as_float(kw[c].x), x0.x, a0); a1 = fmaf(__uint_as_float(kw[c].y), x0.y, a1);
-        a0 = fmaf(__uint_as_float(kw[c].z), x0.z, a0); a1 = fmaf(__uint_as_float(kw[c].w), x0.w, a1);
-        a2 = fmaf(__uint_as_float(kw[c + 1].x), x1.x, a2); a3 = fmaf(__uint_as_float(kw[c + 1].y), x1.y, a3);
-        a2 = fmaf(__uint_as_float(kw[c + 1].z), x1.z, a2); a3 = fmaf(__uint_as_float(kw[c + 1].w), x1.w, a3);
-      }
+    for (int c = 0; c < 32; c += 2) {
+      const float4 x0 = *reinterpret_cast<const float4*>(qj + c * 4);
+      const float4 x1 = *reinterpret_cast<const float4*>(qj + c * 4 + 4);
+      a0 = fmaf(__uint_as_float(kw[c].x), x0.x, a0); a1 = fmaf(__uint_as_float(kw[c].y), x0.y, a1);
+      a0 = fmaf(__uint_as_float(kw[c].z), x0.z, a0); a1 = fmaf(__uint_as_float(kw[c].w), x0.w, a1);
+      a2 = fmaf(__uint_as_float(kw[c + 1].x), x1.x, a2); a3 = fmaf(__uint_as_float(kw[c + 1].y), x1.y, a3);
+      a2 = fmaf(__uint_as_float(kw[c + 1].z), x1.z, a2); a3 = fmaf(__uint_as_float(kw[c + 1].w), x1.w, a3);
     }
     // segmented max over [lane, end): after the step with offset o a lane
     // holds the max of [lane, min(lane + 2o, end)); then the query norm
@@ -183,149 +154,181 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
   }
 }
 
-// Router queries split once per launch for the matrix-core scan: row
-// (query, head) of 128 floats -> 64 words of bfloat16 "hi" pairs, then 64
-// words of "lo" pairs (q = hi + lo + r, |r| <= 2^-17 |q|), and 1/||q||.
-// The arithmetic (and the order of the norm's sum) is that of the vector
-// scan's staging.  32 threads per row, one float4 each.
-__global__ __launch_bounds__(256) void route_prep_kernel(const float* __restrict__ q, int rows,
-                                                         uint32_t* __restrict__ words,
-                                                         float* __restrict__ inv_q) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = t / (kD / 4);
-  const int col = (int)(t % (kD / 4));
-  const bool ok = row < rows;
-  const float4 v = ok ? *reinterpret_cast<const float4*>(q + row * kD + col * 4)
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
-  const float x[4] = {v.x, v.y, v.z, v.w};
-  uint32_t hi[2], lo[2];
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const uint32_t h0 = f32_to_bf16(x[2 * e]), h1 = f32_to_bf16(x[2 * e + 1]);
-    hi[e] = h0 | (h1 << 16);
-    lo[e] = f32_to_bf16(x[2 * e] - __uint_as_float(h0 << 16)) |
-            (f32_to_bf16(x[2 * e + 1] - __uint_as_float(h1 << 16)) << 16);
-  }
-  float ss = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-  ss += __shfl_xor(ss, 1, 64);
-  ss += __shfl_xor(ss, 2, 64);
-  ss += __shfl_xor(ss, 4, 64);
-  ss += __shfl_xor(ss, 8, 64);
-  ss += __shfl_xor(ss, 16, 64);
-  if (!ok) return;
-  *reinterpret_cast<uint2*>(words + row * kD + col * 2) = make_uint2(hi[0], hi[1]);
-  *reinterpret_cast<uint2*>(words + row * kD + 64 + col * 2) = make_uint2(lo[0], lo[1]);
-  if (col == 0) inv_q[row] = ss > 0.f ? 1.0f / sqrtf(ss) : 0.0f;
-}
-
-// Routing scan on the matrix cores, for bf16 keys and passes of 32 or more
-// queries, where the scan is a dense contraction ([queries x 128] times
-// [128 x chunks]) that would otherwise be VALU-bound.  Workgroup = one (tile
-// of 64 chunks, router head); its key tile and every operand it needs are
-// loaded in one memory round trip.  Wave w computes one 32x32 block of
-// cosines, chunks 32*(w&1).. by queries 32*(w>>1).., with
-// v_mfma_f32_32x32x16_bf16: the float32 query enters as its two bfloat16
-// terms, read straight from the prepared rows, two MFMAs per 16-channel step,
-// fp32 accumulation, so the accuracy is that of the vector scan.  The blocks
-// go through LDS as [query][chunk] rows, then each wave folds its queries'
-// rows into per-document maxima with the segmented max.
+// Routing scan on the matrix cores, for bf16 keys: the scan is a dense
+// contraction ([queries x 128] times [128 x chunks]) that would otherwise be
+// VALU-bound, and even a pass of a few queries leaves the matrix cores far
+// from their limit.  v_mfma_f32_32x32x16_bf16 with the float32 query split
+// into two bfloat16 terms, q = hi + lo + r with |r| <= 2^-17 |q| (two MFMAs
+// per 16-channel step, fp32 accumulation): the products are those of the
+// bf16 key with the float32 query up to that remainder.
+//
+// Persistent workgroups: grid (g, router head), workgroup x takes tiles x,
+// x + g, x + 2g, ...; its query fragments are loaded and split once, and the next
+// tile's key rows, chunk table entries, norms and first piece are loaded into
+// registers while the current tile is scored, so the key stream stays in
+// flight.  Per tile: the rows go to LDS; wave w computes one 32x32 block of
+// cosines (chunks 32*(w&1).., queries 32*(w>>1)..) into LDS as [query][chunk]
+// rows; then wave w folds queries w, w+4, ...: lane c holds chunk c's cosine
+// times 1/||k_c||, and a segmented max over the tile's runs of equal
+// documents ("pieces") -- DPP shifts inside each 16-lane row, then the three
+// later rows' leading values read into scalars -- leaves each piece's maximum
+// in the run's first lane, which stores it scaled by 1/||q||.
 typedef __bf16 rbf16x8_t __attribute__((ext_vector_type(8)));
 typedef float rf32x16_t __attribute__((ext_vector_type(16)));
 
+// lane i takes lane i+O's value within its row of 16 lanes (0 past the row);
+// every lane of the wave must execute it, since a move reads its source
+// lane's register
+template <int O>
+__device__ __forceinline__ float row_down(float m) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x100 + O, 0xf, 0xf, true));
+}
+
 __global__ __launch_bounds__(256) void route_scan_mfma_kernel(
     const uint16_t* __restrict__ kr, const float* __restrict__ inv_norm,
-    const uint32_t* __restrict__ qwords, const float* __restrict__ inv_q, int B, int bg, int h_r,
+    const float* __restrict__ q, int B, int bg, int h_r,
     int64_t C, int64_t Cs, const int32_t* __restrict__ chunk_doc,
     const int32_t* __restrict__ tile_piece0, int P, float* __restrict__ piecemax) {
   constexpr int RowF = kD / 2 + 4;  // 32-bit words per staged key row (+16 B pad)
+  constexpr int NLD = 64 * 16 / 256;  // 16-byte vectors of a tile per thread
   __shared__ __attribute__((aligned(16))) uint32_t s_rows[64 * RowF];
   __shared__ float s_cos[64 * 65];  // [query][chunk], rows padded to 65
-  __shared__ float s_iq[64], s_ik[64];
+  __shared__ float s_iq[64];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, l32 = lane & 31, hl = lane >> 5;
-  const int tile = blockIdx.x, h = blockIdx.y;
-  const int64_t c0 = (int64_t)tile * kRouteTile;
-  const int nc = (int)min((int64_t)kRouteTile, C - c0);
+  const int h = blockIdx.y;
+  const int ntiles = (int)((C + kRouteTile - 1) / kRouteTile);
   const int npass = min(64, B - bg);
-  const uint16_t* rows = kr + ((size_t)h * Cs + c0) * kD;
   const int cb = wave & 1, qb = wave >> 1;
   const bool busy = 32 * qb < npass;  // wave-uniform
+  const uint16_t* head = kr + (size_t)h * Cs * kD;  // Cs: rows per head (capacity)
+  const float* head_ik = inv_norm + (size_t)h * Cs;
 
-  // ---- every global load first: key tile, this wave's query fragments
-  // (query 32*qb + l32, channels 16*kk + 8*hl .. +7, hi then lo), the tile's
-  // chunk table and norms
-  constexpr int NLD = 64 * 16 / 256;  // 16-byte vectors of the tile per thread
-  uint4 v[NLD];
-#pragma unroll
-  for (int u = 0; u < NLD; ++u) {
-    const int f = u * 256 + threadIdx.x;
-    const int row = f / 16, col = f % 16;
-    v[u] = *reinterpret_cast<const uint4*>(rows + ((size_t)min(row, nc - 1) * 16 + col) * 8);
-  }
+  // this wave's query fragments: query 32*qb + l32, channels 16*kk + 8*hl ..
+  // +7, as bfloat16 pairs of the hi terms and of the lo terms; and the
+  // pass's 1/||q|| (this lane's 64 squares plus its partner half's)
   uint4 qh[8], ql[8];
   {
     const int qi = 32 * qb + l32;
     const bool qok = busy && qi < npass;
-    const uint32_t* qw = qwords + ((size_t)(bg + (qok ? qi : 0)) * h_r + h) * kD + 4 * hl;
+    const float* qrow = q + ((size_t)(bg + (qok ? qi : 0)) * h_r + h) * kD + 8 * hl;
+    float ss = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      qh[kk] = qok ? *reinterpret_cast<const uint4*>(qw + 8 * kk) : make_uint4(0, 0, 0, 0);
-      ql[kk] = qok ? *reinterpret_cast<const uint4*>(qw + 64 + 8 * kk) : make_uint4(0, 0, 0, 0);
-    }
-  }
-  const int my_doc = lane < nc ? chunk_doc[c0 + lane] : -1;
-  if (threadIdx.x < 64) {
-    const int i = threadIdx.x;
-    s_ik[i] = i < nc ? inv_norm[(size_t)h * Cs + c0 + i] : 0.f;
-    s_iq[i] = i < npass ? inv_q[(size_t)(bg + i) * h_r + h] : 0.f;
-  }
-  const int piece0 = tile_piece0[tile];
+      const float4 a = qok ? *reinterpret_cast<const float4*>(qrow + 16 * kk) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 b = qok ? *reinterpret_cast<const float4*>(qrow + 16 * kk + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      uint32_t hi[4], lo[4];
 #pragma unroll
-  for (int u = 0; u < NLD; ++u) {
-    const int f = u * 256 + threadIdx.x;
-    const int row = f / 16, col = f % 16;
-    *reinterpret_cast<uint4*>(s_rows + row * RowF + col * 4) = row < nc ? v[u] : make_uint4(0, 0, 0, 0);
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t h0 = f32_to_bf16(x[2 * e]), h1 = f32_to_bf16(x[2 * e + 1]);
+        hi[e] = h0 | (h1 << 16);
+        lo[e] = f32_to_bf16(x[2 * e] - __uint_as_float(h0 << 16)) |
+                (f32_to_bf16(x[2 * e + 1] - __uint_as_float(h1 << 16)) << 16);
+        ss = fmaf(x[2 * e], x[2 * e], ss);
+        ss = fmaf(x[2 * e + 1], x[2 * e + 1], ss);
+      }
+      qh[kk] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      ql[kk] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    }
+    ss += __shfl_xor(ss, 32, 64);
+    if (cb == 0 && hl == 0 && qok) s_iq[qi] = ss > 0.f ? 1.0f / sqrtf(ss) : 0.0f;
   }
-  const int prev_doc = __shfl_up(my_doc, 1, 64);
-  const bool start = lane < nc && (lane == 0 || my_doc != prev_doc);
-  const uint64_t starts = __ballot(start);
-  const uint64_t later = lane == 63 ? 0 : starts & (~0ull << (lane + 1));
-  const int end = later ? __builtin_ctzll(later) : nc;
-  const int seg = __builtin_popcountll(starts & ((1ull << lane) - 1));
-  __syncthreads();
 
-  // ---- wave w: cosines of chunks 32*cb + row by queries 32*qb + column
-  if (busy) {
-    rf32x16_t acc;
+  // tile t's loads: 64 rows x 16 vectors (rows past the bank's end read the
+  // last row and are stored as zero), lane's chunk table entry and norm
+  uint4 v[NLD];
+  int nd = -1, np0 = 0;
+  float nik = 0.f;
+  auto load = [&](int t) __attribute__((always_inline)) {
+    const int64_t c0 = (int64_t)t * kRouteTile;
+    const int nc = (int)min((int64_t)kRouteTile, C - c0);
+    const uint16_t* rows = head + c0 * kD;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-    const uint32_t* krow = s_rows + (32 * cb + l32) * RowF + 4 * hl;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const rbf16x8_t a = __builtin_bit_cast(rbf16x8_t, *reinterpret_cast<const uint4*>(krow + 8 * kk));
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(rbf16x8_t, qh[kk]), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(rbf16x8_t, ql[kk]), acc, 0, 0, 0);
+    for (int u = 0; u < NLD; ++u) {
+      const int f = u * 256 + threadIdx.x;
+      const int row = f / 16, col = f % 16;
+      v[u] = *reinterpret_cast<const uint4*>(rows + ((size_t)min(row, nc - 1) * 16 + col) * 8);
     }
-    // element e: chunk row 8*(e/4) + 4*hl + e%4 of the block, query column l32
+    nd = lane < nc ? chunk_doc[c0 + lane] : -1;
+    nik = lane < nc ? head_ik[c0 + lane] : 0.f;
+    np0 = tile_piece0[t];
+  };
+  int tile = blockIdx.x;
+  if (tile < ntiles) load(tile);
+  while (tile < ntiles) {  // workgroup-uniform
+    const int nc = (int)min((int64_t)kRouteTile, C - (int64_t)tile * kRouteTile);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int c = 32 * cb + 8 * (e >> 2) + 4 * hl + (e & 3);
-      s_cos[(32 * qb + l32) * 65 + c] = acc[e] * s_ik[c];
+    for (int u = 0; u < NLD; ++u) {
+      const int f = u * 256 + threadIdx.x;
+      const int row = f / 16, col = f % 16;
+      *reinterpret_cast<uint4*>(s_rows + row * RowF + col * 4) = row < nc ? v[u] : make_uint4(0, 0, 0, 0);
     }
-  }
-  __syncthreads();
+    const int my_doc = nd, piece0 = np0;
+    const float inv_k = nik;
+    const int next = tile + (int)gridDim.x;
+    if (next < ntiles) load(next);
 
-  // ---- wave w folds queries w, w+4, ...: lane c holds chunk c's cosine
-  const int nq = max(0, min(16, (npass - wave + 3) / 4));
-  for (int j = 0; j < nq; ++j) {
-    const int qi = wave + 4 * j;
-    float m = s_cos[qi * 65 + lane];
+    // document runs inside the tile (same for every wave): this lane's run
+    // ends before lane `end`; a run's first lane writes piece piece0 + seg
+    const int prev_doc = __shfl_up(my_doc, 1, 64);
+    const bool start = lane < nc && (lane == 0 || my_doc != prev_doc);
+    const uint64_t starts = __ballot(start);
+    const uint64_t later = lane == 63 ? 0 : starts & (~0ull << (lane + 1));
+    const int end = later ? __builtin_ctzll(later) : nc;
+    const int seg = __builtin_popcountll(starts & ((1ull << lane) - 1));
+    // (the barriers wait for LDS only: the next tile's loads stay in flight)
+    lds_barrier();
+
+    // ---- wave w: cosines of chunks 32*cb + row by queries 32*qb + column
+    if (busy) {
+      rf32x16_t acc;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float u = __shfl_down(m, o, 64);
-      if (lane + o < end) m = fmaxf(m, u);
+      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+      const uint32_t* krow = s_rows + (32 * cb + l32) * RowF + 4 * hl;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const rbf16x8_t a = __builtin_bit_cast(rbf16x8_t, *reinterpret_cast<const uint4*>(krow + 8 * kk));
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(rbf16x8_t, qh[kk]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(rbf16x8_t, ql[kk]), acc, 0, 0, 0);
+      }
+      // element e: chunk row 8*(e/4) + 4*hl + e%4 of the block, query column l32
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int c = 32 * cb + 8 * (e >> 2) + 4 * hl + (e & 3);
+        s_cos[(32 * qb + l32) * 65 + c] = acc[e];
+      }
     }
-    if (start) piecemax[((size_t)(bg + qi) * h_r + h) * P + piece0 + seg] = m * s_iq[qi];
+    lds_barrier();
+
+    // ---- wave w folds queries w, w+4, ...  In-row stage: after the shift
+    // by o a lane holds the max over [lane, min(lane + 2o, end, row end));
+    // then the rows after this lane's that its run reaches add their first
+    // lane's value (x -> x / ||q|| is monotone, so it is applied last).
+    const int lim = min(end, (lane | 15) + 1);
+    const bool c1 = lane + 1 < lim, c2 = lane + 2 < lim, c4 = lane + 4 < lim, c8 = lane + 8 < lim;
+    const bool x1 = lane < 16 && 16 < end, x2 = lane < 32 && 32 < end, x3 = lane < 48 && 48 < end;
+    const int nq = max(0, min(16, (npass - wave + 3) / 4));
+    for (int j = 0; j < nq; ++j) {
+      const int qi = wave + 4 * j;
+      float m = s_cos[qi * 65 + lane] * inv_k;
+      float t = row_down<1>(m);
+      m = c1 && t > m ? t : m;
+      t = row_down<2>(m);
+      m = c2 && t > m ? t : m;
+      t = row_down<4>(m);
+      m = c4 && t > m ? t : m;
+      t = row_down<8>(m);
+      m = c8 && t > m ? t : m;
+      const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 16));
+      const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 32));
+      const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 48));
+      m = x1 && r1 > m ? r1 : m;
+      m = x2 && r2 > m ? r2 : m;
+      m = x3 && r3 > m ? r3 : m;
+      if (start) piecemax[((size_t)(bg + qi) * h_r + h) * P + piece0 + seg] = m * s_iq[qi];
+    }
+    tile = next;
   }
 }
 
@@ -466,41 +469,39 @@ __global__ __launch_bounds__(256) void project_kernel(const float* __restrict__ 
 
 }  // namespace
 
-size_t route_prep_bytes(const Bank& bk, int B) {
-  return (size_t)B * bk.desc.h_r * (kD * 4 + 4);
+
+// compute units of the current device (queried once per device)
+static int device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
 }
 
-hipError_t launch_route_scan(const Bank& bk, const float* q_route, int B, void* prep,
-                             float* piecemax, hipStream_t s) {
-  const dim3 grid((unsigned)bk.n_tiles, (unsigned)bk.desc.h_r);
-  const int rows = B * bk.desc.h_r;
-  uint32_t* qwords = (uint32_t*)prep;
-  float* inv_q = (float*)((char*)prep + (size_t)rows * kD * 4);
-  bool prepped = false;
+hipError_t launch_route_scan(const Bank& bk, const float* q_route, int B, float* piecemax,
+                             hipStream_t s) {
   timer_mark(1, true, s);
-  for (int bg = 0; bg < B; bg += 64) {
-    if (bk.desc.dtype == MSA_BF16 && std::min(64, B - bg) >= 32) {
-      if (!prepped) {
-        const unsigned pg = (unsigned)(((int64_t)rows * (kD / 4) + 255) / 256);
-        hipLaunchKernelGGL(route_prep_kernel, dim3(pg), dim3(256), 0, s, q_route, rows, qwords,
-                           inv_q);
-        prepped = true;
-      }
-      hipLaunchKernelGGL(route_scan_mfma_kernel, grid, dim3(256), 0, s,
-                         (const uint16_t*)bk.desc.kr, bk.desc.inv_norm, qwords, inv_q, B, bg,
-                         bk.desc.h_r, bk.n_chunks, bk.chunk_stride, bk.d_chunk_doc, bk.d_tile_piece0,
-                         bk.n_pieces, piecemax);
-    } else if (bk.desc.dtype == MSA_BF16) {
-      hipLaunchKernelGGL(route_scan_kernel<uint16_t>, grid, dim3(256), 0, s,
-                         (const uint16_t*)bk.desc.kr, bk.desc.inv_norm, q_route, B, bg,
-                         bk.desc.h_r, bk.n_chunks, bk.chunk_stride, bk.d_chunk_doc, bk.d_tile_piece0,
-                         bk.n_pieces, piecemax);
-    } else {
-      hipLaunchKernelGGL(route_scan_kernel<float>, grid, dim3(256), 0, s,
-                         (const float*)bk.desc.kr, bk.desc.inv_norm, q_route, B, bg,
-                         bk.desc.h_r, bk.n_chunks, bk.chunk_stride, bk.d_chunk_doc, bk.d_tile_piece0,
-                         bk.n_pieces, piecemax);
-    }
+  if (bk.desc.dtype == MSA_BF16) {
+    // persistent: about kScanWgPerCu workgroups per compute unit in all
+    const int gx = std::max(1, std::min(bk.n_tiles, (kScanWgPerCu * device_cus() + bk.desc.h_r - 1) /
+                                                        bk.desc.h_r));
+    for (int bg = 0; bg < B; bg += 64)
+      hipLaunchKernelGGL(route_scan_mfma_kernel, dim3((unsigned)gx, (unsigned)bk.desc.h_r),
+                         dim3(256), 0, s, (const uint16_t*)bk.desc.kr, bk.desc.inv_norm, q_route, B,
+                         bg, bk.desc.h_r, bk.n_chunks, bk.chunk_stride, bk.d_chunk_doc,
+                         bk.d_tile_piece0, bk.n_pieces, piecemax);
+  } else {
+    const dim3 grid((unsigned)bk.n_tiles, (unsigned)bk.desc.h_r);
+    for (int bg = 0; bg < B; bg += 64)
+      hipLaunchKernelGGL(route_scan_kernel, grid, dim3(256), 0, s, (const float*)bk.desc.kr,
+                         bk.desc.inv_norm, q_route, B, bg, bk.desc.h_r, bk.n_chunks,
+                         bk.chunk_stride, bk.d_chunk_doc, bk.d_tile_piece0, bk.n_pieces, piecemax);
   }
   timer_mark(1, false, s);
   return hipGetLastError();

@@ -27,7 +27,9 @@ EXPORTS = [
     "msa_workspace_bytes", "msa_staging_bytes", "msa_route", "msa_attend", "msa_step",
     "msa_timer_enable", "msa_timer_read", "msa_timer_reserve", "msa_bank_set_cache", "msa_cache_slot_bytes",
     "msa_bank_append", "msa_pooled_sizes", "msa_bank_set_pooled", "msa_build_pooled",
+    "msa_stream_read",
 ]
+MSA_STREAM_READ_BLOCKS = 2048
 MSA_TIMER_ATTENTION, MSA_TIMER_ROUTE = 0, 1
 MSA_MEMORY_TOKENS, MSA_MEMORY_POOLED = 0, 1
 
@@ -107,6 +109,8 @@ def _load():
     lib.msa_timer_enable.argtypes = [C.c_int]
     lib.msa_timer_read.argtypes = [C.c_int, C.POINTER(C.c_double), C.POINTER(i64)]
     lib.msa_timer_reserve.argtypes = [i64]
+    lib.msa_stream_read.argtypes = [vp, i64, vp, vp]
+    lib.msa_stream_read.restype = C.c_int
     for f in (lib.msa_timer_enable, lib.msa_timer_read, lib.msa_timer_reserve):
         f.restype = C.c_int
     for f in (lib.msa_bank_create, lib.msa_bank_destroy, lib.msa_bank_get_info,
@@ -126,6 +130,16 @@ def timer_enable(on: bool = True):
 def timer_reserve(launches: int):
     """Create the events of `launches` timed launches before a timed region."""
     _check(lib.msa_timer_reserve(int(launches)), "msa_timer_reserve")
+
+
+def stream_read(buf, out, stream=None):
+    """Stream every byte of the device tensor `buf` once (HBM read-rate
+    probe); `out`: device int32/uint32 tensor of MSA_STREAM_READ_BLOCKS words."""
+    _expect_bytes(out, 4 * MSA_STREAM_READ_BLOCKS, "out", buf.device)
+    if not buf.is_contiguous() or buf.device.type != "cuda":
+        raise ValueError("buf must be a contiguous device tensor")
+    _check(lib.msa_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out),
+                               _stream(stream)), "msa_stream_read")
 
 
 def timer_read(which: int):

@@ -90,6 +90,13 @@ def test_null_arguments(msa):
     assert msa.lib.msa_timer_read(0, None, None) == msa.MSA_EINVAL
     assert msa.lib.msa_timer_reserve(-1) == msa.MSA_EINVAL
     assert msa.lib.msa_timer_reserve(0) == msa.MSA_OK  # nothing to create: no device needed
+    # the read-rate probe validates before any launch (these pointers are never read)
+    out = C.c_void_p(4096)
+    assert msa.lib.msa_stream_read(None, 1 << 20, out, None) == msa.MSA_EINVAL
+    assert msa.lib.msa_stream_read(C.c_void_p(4096), 1 << 20, None, None) == msa.MSA_EINVAL
+    assert msa.lib.msa_stream_read(C.c_void_p(4096), 1000, out, None) == msa.MSA_EINVAL
+    assert msa.lib.msa_stream_read(C.c_void_p(4096), 0, out, None) == msa.MSA_EINVAL
+    assert msa.lib.msa_stream_read(C.c_void_p(4104), 1 << 20, out, None) == msa.MSA_EINVAL
 
 
 def test_build_script_flags():

@@ -278,3 +278,15 @@ def test_decode_local_only_and_docs_only(msa):
         ref = M.oracle_attend_decode(w, q[b], w.q_pos, [n], kv, np.zeros((0, w.h_kv, 128)),
                                      np.zeros((0, w.h_kv, 128)), w.P0)
         M.check_out(out[b].cpu().numpy(), ref, w.dtype, "docs only")
+
+
+def test_stream_read_probe_reads_every_word(msa):
+    # the HBM read-rate probe's checksum is the XOR of every 32-bit word it
+    # read: check it over a single word, a ragged size and several grid strides
+    g = torch.Generator().manual_seed(7)
+    out = torch.empty(msa.MSA_STREAM_READ_BLOCKS, dtype=torch.int32, device=DEV)
+    for n_words in (4, 4 * 12345, 4 * 2048 * 256 * 5 + 36):
+        host = torch.randint(-2**31, 2**31 - 1, (n_words,), dtype=torch.int32, generator=g)
+        msa.stream_read(host.to(DEV), out)
+        got = np.bitwise_xor.reduce(out.cpu().numpy())
+        assert got == np.bitwise_xor.reduce(host.numpy()), n_words
