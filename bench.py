@@ -509,6 +509,7 @@ def main():
         # stream's attention
         "routing": {"kernel": "cosine routing scan (overlapped with attention)", "bound": "hbm",
                     "bytes_per_launch": w.C * w.h_r * (128 * 2 + 4),
+                    "traffic": measured_traffic("route_c2_counters"),
                     "avg_launch_us": rt_ms * 1e3 / max(rt_n, 1), "launches": rt_n,
                     "achieved": w.C * w.h_r * (128 * 2 + 4) / (rt_ms * 1e-3 / max(rt_n, 1)) / 1e9,
                     "unit": "GB/s", "peak": HBM_PEAK_GBS},

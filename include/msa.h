@@ -354,7 +354,7 @@ int msa_timer_reserve(int64_t launches);
  * workgroup (its only purpose is to keep every load).  Asynchronous;
  * MSA_EINVAL on a null pointer, misalignment or a bad size, MSA_EHIP if the
  * launch fails.  Buffers are the caller's. */
-enum { MSA_STREAM_READ_BLOCKS = 2048 };
+enum { MSA_STREAM_READ_BLOCKS = 4096 };
 int msa_stream_read(const void* buf, int64_t bytes, uint32_t* out, void* stream);
 
 #ifdef __cplusplus

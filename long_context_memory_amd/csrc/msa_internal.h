@@ -228,7 +228,7 @@ hipError_t launch_rope_queries(const Bank& bk, const void* q, int n_q, int h_q, 
 hipError_t launch_route_scan(const Bank& bk, const float* q_route, int B, float* piecemax,
                              hipStream_t s);
 // HBM read-rate probe: kStreamReadBlocks workgroups; out holds one word each
-constexpr int kStreamReadBlocks = 2048;
+constexpr int kStreamReadBlocks = 4096;
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* out, hipStream_t s);
 hipError_t launch_topk(const Bank& bk, const float* piecemax, int B, int k,
                        const uint32_t* exclude, uint32_t* exclude_out, int32_t* ids,

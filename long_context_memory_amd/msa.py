@@ -29,7 +29,7 @@ EXPORTS = [
     "msa_bank_append", "msa_pooled_sizes", "msa_bank_set_pooled", "msa_build_pooled",
     "msa_stream_read",
 ]
-MSA_STREAM_READ_BLOCKS = 2048
+MSA_STREAM_READ_BLOCKS = 4096
 MSA_TIMER_ATTENTION, MSA_TIMER_ROUTE = 0, 1
 MSA_MEMORY_TOKENS, MSA_MEMORY_POOLED = 0, 1
 

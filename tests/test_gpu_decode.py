@@ -285,7 +285,7 @@ def test_stream_read_probe_reads_every_word(msa):
     # read: check it over a single word, a ragged size and several grid strides
     g = torch.Generator().manual_seed(7)
     out = torch.empty(msa.MSA_STREAM_READ_BLOCKS, dtype=torch.int32, device=DEV)
-    for n_words in (4, 4 * 12345, 4 * 2048 * 256 * 5 + 36):
+    for n_words in (4, 4 * 12345, 4 * 4096 * 256 * 3 + 36):
         host = torch.randint(-2**31, 2**31 - 1, (n_words,), dtype=torch.int32, generator=g)
         msa.stream_read(host.to(DEV), out)
         got = np.bitwise_xor.reduce(out.cpu().numpy())
