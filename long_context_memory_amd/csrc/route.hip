@@ -19,6 +19,11 @@ namespace {
 
 constexpr int kQPerWave = 16;    // queries a wave scores per pass (64 per workgroup pass)
 constexpr int kScanWgPerCu = 3;  // resident matrix-core scan workgroups per compute unit
+// LDS buffer of the matrix-core scan's piece maxima, written out in bulk so
+// that no store waits inside the tile loop (sized so that three workgroups
+// fit in 160 KiB of LDS)
+constexpr int kScanOutFloats = 4608, kScanOutTiles = 128;
+static_assert(kScanOutFloats >= 64 * 64, "one tile's block must fit");
 
 // Workgroup barrier that waits for this wave's LDS operations only (a
 // __syncthreads() would also wait for every global load in flight).
@@ -194,6 +199,10 @@ __global__ __launch_bounds__(256) void route_scan_mfma_kernel(
   __shared__ __attribute__((aligned(16))) uint32_t s_rows[64 * RowF];
   __shared__ float s_cos[64 * 65];  // [query][chunk], rows padded to 65
   __shared__ float s_iq[64];
+  // piece maxima of the tiles scored since the last flush: tile b's block is
+  // [query][piece], its first piece and piece count are in the table
+  __shared__ float s_out[kScanOutFloats];
+  __shared__ int s_tp0[kScanOutTiles], s_tnp[kScanOutTiles];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, l32 = lane & 31, hl = lane >> 5;
   const int h = blockIdx.y;
@@ -254,6 +263,22 @@ __global__ __launch_bounds__(256) void route_scan_mfma_kernel(
     nik = lane < nc ? head_ik[c0 + lane] : 0.f;
     np0 = tile_piece0[t];
   };
+  // write the buffered piece maxima to their rows (each tile's block is a
+  // contiguous run of pieces per query); every thread runs it, after a barrier
+  int n_buf = 0, off_buf = 0;  // buffered tiles and floats (workgroup-uniform)
+  auto flush = [&]() __attribute__((always_inline)) {
+    int off = 0;
+    for (int b = 0; b < n_buf; ++b) {
+      const int p0 = s_tp0[b], np = s_tnp[b], n = npass * np;
+      for (int i = threadIdx.x; i < n; i += 256) {
+        const int q = i / np;
+        piecemax[((size_t)(bg + q) * h_r + h) * P + p0 + (i - q * np)] = s_out[off + i];
+      }
+      off += n;
+    }
+    n_buf = 0;
+    off_buf = 0;
+  };
   int tile = blockIdx.x;
   if (tile < ntiles) load(tile);
   while (tile < ntiles) {  // workgroup-uniform
@@ -277,8 +302,12 @@ __global__ __launch_bounds__(256) void route_scan_mfma_kernel(
     const uint64_t later = lane == 63 ? 0 : starts & (~0ull << (lane + 1));
     const int end = later ? __builtin_ctzll(later) : nc;
     const int seg = __builtin_popcountll(starts & ((1ull << lane) - 1));
+    const int np = __builtin_popcountll(starts);  // pieces in this tile
     // (the barriers wait for LDS only: the next tile's loads stay in flight)
     lds_barrier();
+    // the previous tiles' folds are complete: flush if this tile's block
+    // would not fit (a tile's block, at most 64 x 64 floats, always fits)
+    if (n_buf == kScanOutTiles || off_buf + npass * np > kScanOutFloats) flush();
 
     // ---- wave w: cosines of chunks 32*cb + row by queries 32*qb + column
     if (busy) {
@@ -326,10 +355,18 @@ __global__ __launch_bounds__(256) void route_scan_mfma_kernel(
       m = x1 && r1 > m ? r1 : m;
       m = x2 && r2 > m ? r2 : m;
       m = x3 && r3 > m ? r3 : m;
-      if (start) piecemax[((size_t)(bg + qi) * h_r + h) * P + piece0 + seg] = m * s_iq[qi];
+      if (start) s_out[off_buf + qi * np + seg] = m * s_iq[qi];
     }
+    if (threadIdx.x == 0) {
+      s_tp0[n_buf] = piece0;
+      s_tnp[n_buf] = np;
+    }
+    ++n_buf;
+    off_buf += npass * np;
     tile = next;
   }
+  lds_barrier();
+  flush();
 }
 
 // ---------------------------------------------------------------- top-k
