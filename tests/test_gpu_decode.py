@@ -107,10 +107,11 @@ def test_route_matches_oracle(msa, name):
         assert all(int(ids[b, 0]) == c["target_doc"] for b in range(w.B))
 
 
-@pytest.mark.parametrize("B", [32, 40, 64, 70])
+@pytest.mark.parametrize("B", [1, 7, 32, 40, 64, 70])
 def test_route_large_batches_match_oracle(msa, B):
-    # 32 or more queries per pass take the matrix-core scan (70: a pass of 64
-    # and a pass of 6 on the vector scan); the bank's last tile is ragged
+    # bf16 keys take the matrix-core scan at every batch size (a pass holds up
+    # to 64 queries: 70 is a pass of 64 and a pass of 6; 1 and 7 leave most of
+    # each 32-query block empty); the bank's last tile is ragged
     c = decode_case(msa, "decode_small")
     w = c["w"]
     g = torch.Generator(device=DEV)

@@ -98,9 +98,19 @@ def test_host_bank_full_sampled(msa):
     ids_np, sc_np, out_np = ids[0].cpu().numpy(), scores[0].cpu().numpy(), out[0].cpu().numpy()
     kr_o = M.np64(kr)
     del kr
-    so = O.cosine_doc_scores(M.np64(q_route), kr_o, O.inverse_norms(kr_o), w.doc_len)
+    inv_o = O.inverse_norms(kr_o)
+    so = O.cosine_doc_scores(M.np64(q_route), kr_o, inv_o, w.doc_len)
     near = M.check_topk(ids_np, sc_np, so, w.k)
     print(f"host bank routing: {w.B} queries over {w.n_docs} documents, {near} near-tie")
+    # 72 router queries on the same bank: a pass of 64, whose buffered piece
+    # maxima outgrow a scan workgroup's LDS buffer several times over its
+    # tiles (written out early), then a pass of 8
+    q72 = torch.cat([S.route_queries(w, DEV, batch=i) for i in range(1, 10)])
+    ids72, sc72 = bank.route(q72, w.k)
+    torch.cuda.synchronize()
+    so72 = O.cosine_doc_scores(M.np64(q72), kr_o, inv_o, w.doc_len)
+    near72 = M.check_topk(ids72.cpu().numpy(), sc72.cpu().numpy(), so72, w.k)
+    print(f"host bank routing: 72 queries, {near72} near-tie")
     distinct = sorted(set(ids_np.ravel().tolist()))
     assert st.docs_copied == len(distinct)
     assert st.bytes_copied == sum(2 * w.doc_len[n] * w.h_kv * 128 * 2 for n in distinct)
