@@ -257,7 +257,7 @@ __global__ __launch_bounds__(256) void route_scan_mfma_kernel(
     for (int u = 0; u < NLD; ++u) {
       const int f = u * 256 + threadIdx.x;
       const int row = f / 16, col = f % 16;
-      v[u] = *reinterpret_cast<const uint4*>(rows + ((size_t)min(row, nc - 1) * 16 + col) * 8);
+      v[u] = ld_nt(rows + ((size_t)min(row, nc - 1) * 16 + col) * 8);
     }
     nd = lane < nc ? chunk_doc[c0 + lane] : -1;
     nik = lane < nc ? head_ik[c0 + lane] : 0.f;
