@@ -177,7 +177,9 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
 // times 1/||k_c||, and a segmented max over the tile's runs of equal
 // documents ("pieces") -- DPP shifts inside each 16-lane row, then the three
 // later rows' leading values read into scalars -- leaves each piece's maximum
-// in the run's first lane, which stores it scaled by 1/||q||.
+// in the run's first lane.  Scaled by 1/||q||, it goes to an LDS buffer that
+// is written out once per workgroup (earlier only if it fills), so that no
+// store is in flight when a wave waits for the next tile's keys.
 typedef __bf16 rbf16x8_t __attribute__((ext_vector_type(8)));
 typedef float rf32x16_t __attribute__((ext_vector_type(16)));
 
@@ -271,8 +273,8 @@ __global__ __launch_bounds__(256) void route_scan_mfma_kernel(
     for (int b = 0; b < n_buf; ++b) {
       const int p0 = s_tp0[b], np = s_tnp[b], n = npass * np;
       for (int i = threadIdx.x; i < n; i += 256) {
-        const int q = i / np;
-        piecemax[((size_t)(bg + q) * h_r + h) * P + p0 + (i - q * np)] = s_out[off + i];
+        const int qi = i / np;
+        piecemax[((size_t)(bg + qi) * h_r + h) * P + p0 + (i - qi * np)] = s_out[off + i];
       }
       off += n;
     }
