@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void pool_keys_kernel(
   for (int t = stream; t < kChunk; t += S) {
     const T* p = base + (size_t)t * E + v * VE;
     T buf[VE];
-    *reinterpret_cast<uint4*>(buf) = *reinterpret_cast<const uint4*>(p);
+    *reinterpret_cast<uint4*>(buf) = ld_nt(p);
 #pragma unroll
     for (int i = 0; i < VE; ++i) acc[i] += St<T>::load(buf[i]);
   }
@@ -140,25 +140,39 @@ __device__ __forceinline__ TileInfo tile_info(const KLayout& ly, int tile) {
   return ti;
 }
 
+// One workgroup per tile.  Thread (token t, channel group g) holds the sines
+// and cosines of pairs 8g .. 8g+7 at t's position (computed once, used for
+// every head) and moves 16-byte vectors: channels 8g.. and 64 + 8g.. of each
+// head's row.  A wave's 64 lanes cover 8 tokens x 8 groups.
 template <typename T>
 __global__ __launch_bounds__(256) void rotate_k_kernel(const T* __restrict__ in,
                                                        T* __restrict__ out, KLayout ly,
                                                        const double* __restrict__ inv_freq) {
+  constexpr int VE = 16 / sizeof(T);  // elements per 16-byte vector
+  constexpr int NG = 64 / VE;         // vectors per half row
   const TileInfo ti = tile_info(ly, blockIdx.x);
-  const int pair = threadIdx.x & 63, sub = threadIdx.x >> 6;
-  const double f = inv_freq[pair];
-  for (int tt = sub; tt < ti.n_valid; tt += 4) {
+  for (int u = threadIdx.x; u < kAttnTile * NG; u += 256) {
+    const int tt = u / NG, g = u % NG;
+    if (tt >= ti.n_valid) break;  // u grows with tt
     const int t = ti.t0 + tt;
-    const double ang = (double)(ti.pos_base + t) * f;
-    double sn, cs;
-    sincos(ang, &sn, &cs);
-    const T* src = in + (size_t)(ti.in_row0 + tt) * ly.h_kv * kD;
+    double cs[VE], sn[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) sincos((double)(ti.pos_base + t) * inv_freq[g * VE + e], &sn[e], &cs[e]);
+    const T* src = in + (size_t)(ti.in_row0 + tt) * ly.h_kv * kD + g * VE;
+    T* dst0 = out + ti.out_base + (size_t)t * kD + g * VE;
     for (int h = 0; h < ly.h_kv; ++h) {
-      const double x1 = St<T>::load(src[h * kD + pair]);
-      const double x2 = St<T>::load(src[h * kD + 64 + pair]);
-      T* dst = out + ti.out_base + ((size_t)h * ti.seg_len + t) * kD;
-      dst[pair] = St<T>::store(x1 * cs - x2 * sn);
-      dst[64 + pair] = St<T>::store(x2 * cs + x1 * sn);
+      T x1[VE], x2[VE], y1[VE], y2[VE];
+      *reinterpret_cast<uint4*>(x1) = *reinterpret_cast<const uint4*>(src + h * kD);
+      *reinterpret_cast<uint4*>(x2) = *reinterpret_cast<const uint4*>(src + h * kD + 64);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        const double a = St<T>::load(x1[e]), b = St<T>::load(x2[e]);
+        y1[e] = St<T>::store(a * cs[e] - b * sn[e]);
+        y2[e] = St<T>::store(b * cs[e] + a * sn[e]);
+      }
+      T* dst = dst0 + (size_t)h * ti.seg_len * kD;
+      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(y1);
+      *reinterpret_cast<uint4*>(dst + 64) = *reinterpret_cast<const uint4*>(y2);
     }
   }
 }
@@ -166,10 +180,14 @@ __global__ __launch_bounds__(256) void rotate_k_kernel(const T* __restrict__ in,
 // ---------------------------------------------------------------- V transpose
 // One workgroup per (tile of 64 tokens, head): [64 tokens][128] -> the tile's
 // channel-major block [128][64] (tokens past the end of a local sequence are
-// written as zeros).
+// written as zeros).  16-byte vectors in and out: rows are read as 16
+// vectors of 8 (bf16) channels, staged in LDS token-major, and each output
+// vector gathers 8 consecutive tokens of one channel.
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_v_kernel(const T* __restrict__ in,
                                                           T* __restrict__ out, KLayout ly) {
+  constexpr int VE = 16 / sizeof(T);
+  constexpr int NV = kD / VE;  // vectors per token row
   const int h = blockIdx.y;
   const TileInfo ti = tile_info(ly, blockIdx.x);
   size_t blk;  // element offset of the tile block
@@ -179,40 +197,64 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const T* __restrict__ 
     const int s = blockIdx.x / ly.tiles_per_seq, m = blockIdx.x % ly.tiles_per_seq;
     blk = (((size_t)s * ly.h_kv + h) * ly.tiles_per_seq + m) * kAttnTile * kD;
   }
-  __shared__ T tile[kAttnTile][kD + 2];
-  for (int e = threadIdx.x; e < kAttnTile * kD; e += 256) {
-    const int t = e / kD, i = e % kD;
-    tile[t][i] = t < ti.n_valid ? in[(size_t)(ti.in_row0 + t) * ly.h_kv * kD + h * kD + i]
-                                : (T)0;
+  __shared__ __attribute__((aligned(16))) T tile[kAttnTile][kD + VE];
+  for (int u = threadIdx.x; u < kAttnTile * NV; u += 256) {
+    const int t = u / NV, c = u % NV;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (t < ti.n_valid)
+      v = *reinterpret_cast<const uint4*>(in + (size_t)(ti.in_row0 + t) * ly.h_kv * kD + h * kD +
+                                          c * VE);
+    *reinterpret_cast<uint4*>(&tile[t][c * VE]) = v;
   }
   __syncthreads();
   T* dst = out + blk;
-  for (int e = threadIdx.x; e < kAttnTile * kD; e += 256) {
-    const int i = e / kAttnTile, t = e % kAttnTile;
-    dst[(size_t)i * kAttnTile + t] = tile[t][i];
+  constexpr int NT = kAttnTile / VE;  // output vectors per channel row
+  for (int u = threadIdx.x; u < kD * NT; u += 256) {
+    const int i = u / NT, t0 = (u % NT) * VE;
+    T w[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) w[e] = tile[t0 + e][i];
+    *reinterpret_cast<uint4*>(dst + (size_t)i * kAttnTile + t0) = *reinterpret_cast<const uint4*>(w);
   }
 }
 
 // ---------------------------------------------------------------- queries
+// Workgroup = kRopeRows query rows.  First the rows' angles: one (row, pair)
+// per thread, sine and cosine in float64 into LDS; then every (row, head,
+// group of pairs) moves 16-byte vectors of channels 8g.. and 64 + 8g.. (bf16).
+constexpr int kRopeRows = 4;  // 4 rows x 64 pairs = one angle per thread
+
 template <typename T>
 __global__ __launch_bounds__(256) void rope_queries_kernel(const T* __restrict__ q, int n_q,
                                                            int h_q, int pos0, int pos_step,
                                                            const double* __restrict__ inv_freq,
                                                            double scale, T* __restrict__ out) {
-  // one thread per (query row, channel pair); the angle depends only on the
-  // row's position, so its sine and cosine serve every head of the row
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)n_q * 64) return;
-  const int pair = (int)(idx & 63);
-  const int i = (int)(idx >> 6);
-  double sn, cs;
-  sincos((double)(pos0 + (int64_t)i * pos_step) * inv_freq[pair], &sn, &cs);
-#pragma unroll 8
-  for (int h = 0; h < h_q; ++h) {
-    const size_t o = ((size_t)i * h_q + h) * kD;
-    const double x1 = St<T>::load(q[o + pair]), x2 = St<T>::load(q[o + 64 + pair]);
-    out[o + pair] = St<T>::store((x1 * cs - x2 * sn) * scale);
-    out[o + 64 + pair] = St<T>::store((x2 * cs + x1 * sn) * scale);
+  constexpr int VE = 16 / sizeof(T);
+  constexpr int NG = 64 / VE;
+  __shared__ double s_cs[kRopeRows][64], s_sn[kRopeRows][64];
+  const int r0 = blockIdx.x * kRopeRows;
+  {
+    const int r = threadIdx.x >> 6, pair = threadIdx.x & 63;
+    const int i = min(r0 + r, n_q - 1);
+    sincos((double)(pos0 + (int64_t)i * pos_step) * inv_freq[pair], &s_sn[r][pair], &s_cs[r][pair]);
+  }
+  __syncthreads();
+  const int rows = min(kRopeRows, n_q - r0);
+  for (int u = threadIdx.x; u < rows * h_q * NG; u += 256) {
+    const int g = u % NG, h = (u / NG) % h_q, r = u / (NG * h_q);
+    const size_t o = ((size_t)(r0 + r) * h_q + h) * kD + g * VE;
+    T x1[VE], x2[VE], y1[VE], y2[VE];
+    *reinterpret_cast<uint4*>(x1) = *reinterpret_cast<const uint4*>(q + o);
+    *reinterpret_cast<uint4*>(x2) = *reinterpret_cast<const uint4*>(q + o + 64);
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+      const double cs = s_cs[r][g * VE + e], sn = s_sn[r][g * VE + e];
+      const double a = St<T>::load(x1[e]), b = St<T>::load(x2[e]);
+      y1[e] = St<T>::store((a * cs - b * sn) * scale);
+      y2[e] = St<T>::store((b * cs + a * sn) * scale);
+    }
+    *reinterpret_cast<uint4*>(out + o) = *reinterpret_cast<const uint4*>(y1);
+    *reinterpret_cast<uint4*>(out + o + 64) = *reinterpret_cast<const uint4*>(y2);
   }
 }
 
@@ -378,7 +420,7 @@ hipError_t launch_rope_queries(const Bank& bk, const void* q, int n_q, int h_q, 
                                int pos_step, void* q_rot, hipStream_t s) {
   if (n_q == 0) return hipSuccess;
   const double scale = 1.4426950408889634 / sqrt((double)kD);  // log2(e) / sqrt(d)
-  const unsigned grid = (unsigned)(((int64_t)n_q * 64 + 255) / 256);
+  const unsigned grid = (unsigned)((n_q + kRopeRows - 1) / kRopeRows);
   if (bk.desc.dtype == MSA_BF16)
     hipLaunchKernelGGL(rope_queries_kernel<uint16_t>, dim3(grid), dim3(256), 0, s,
                        (const uint16_t*)q, n_q, h_q, pos0, pos_step, bk.d_inv_freq, scale,
