@@ -309,13 +309,19 @@ namespace {
 // chunk j of stored K (already rotated at document positions) and of V
 // (intelliparadigm.com, section 3.1: chunk-mean pooling of the KV cache),
 // accumulated in float64 and rounded once.  One workgroup per (chunk, KV
-// head): 128 channels x 2 halves of the chunk's 256 tokens.
+// head).  K rows are read as 16-byte vectors: thread (vector column, token
+// group) sums every 16th token of the chunk; V (channel-major 64-token
+// tiles) as 16-byte runs of 8 tokens: thread (channel, half) sums two of the
+// chunk's four tiles.  Partial sums are combined in a fixed order in LDS.
 template <typename T>
 __global__ __launch_bounds__(256) void pool_kv_kernel(
     const T* __restrict__ ks, const T* __restrict__ vs, const int32_t* __restrict__ chunk_doc,
     const int32_t* __restrict__ doc_len, const int64_t* __restrict__ kv_off,
     const int64_t* __restrict__ tok_off, const int64_t* __restrict__ pool_voff, int h_kv,
     int64_t c0, T* __restrict__ pk, T* __restrict__ pv) {
+  constexpr int VE = 16 / sizeof(T);  // elements per 16-byte vector
+  constexpr int NV = kD / VE;         // vectors per K row
+  constexpr int NTG = 256 / NV;       // token groups
   const int64_t c = c0 + blockIdx.x;
   const int h = blockIdx.y;
   const int n = chunk_doc[c];
@@ -323,27 +329,46 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(
   const int64_t P = L / kChunk;
   const int64_t cfirst = tok_off[n] / kChunk;
   const int64_t j = c - cfirst;  // entry (chunk) within the document
-  const int d = threadIdx.x & (kD - 1), half = threadIdx.x >> 7;
+  const int tid = threadIdx.x;
   const int64_t base = (kv_off[n] * h_kv + (int64_t)h * L) * kD;  // this head's block
-  double sk = 0.0, sv = 0.0;
-  for (int t = 128 * half; t < 128 * half + 128; ++t) {
-    const int64_t tt = j * kChunk + t;  // token within the document
-    sk += St<T>::load(ks[base + tt * kD + d]);
-    sv += St<T>::load(vs[base + (tt / kAttnTile) * kD * kAttnTile + d * kAttnTile + tt % kAttnTile]);
+  const int64_t tok0 = j * kChunk;  // first token of the chunk within the document
+
+  const int cv = tid % NV, tg = tid / NV;
+  double ak[VE];
+#pragma unroll
+  for (int e = 0; e < VE; ++e) ak[e] = 0.0;
+  const T* kb = ks + base + tok0 * kD + cv * VE;
+  for (int t = tg; t < kChunk; t += NTG) {
+    T x[VE];
+    *reinterpret_cast<uint4*>(x) = ld_nt(kb + (size_t)t * kD);
+#pragma unroll
+    for (int e = 0; e < VE; ++e) ak[e] += St<T>::load(x[e]);
   }
-  __shared__ double red[2][kD];
-  if (half == 1) {
-    red[0][d] = sk;
-    red[1][d] = sv;
+  const int d = tid & (kD - 1), half = tid >> 7;
+  double av = 0.0;
+  for (int q = 2 * half; q < 2 * half + 2; ++q) {
+    const T* vb = vs + base + (tok0 / kAttnTile + q) * kD * kAttnTile + d * kAttnTile;
+    for (int w = 0; w < kAttnTile / VE; ++w) {
+      T x[VE];
+      *reinterpret_cast<uint4*>(x) = ld_nt(vb + w * VE);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) av += St<T>::load(x[e]);
+    }
   }
+  __shared__ double s_k[NTG][kD];
+  __shared__ double s_v[2][kD];
+#pragma unroll
+  for (int e = 0; e < VE; ++e) s_k[tg][cv * VE + e] = ak[e];
+  s_v[half][d] = av;
   __syncthreads();
-  if (half == 0) {
-    sk += red[0][d];
-    sv += red[1][d];
-    pk[(cfirst * h_kv + (int64_t)h * P + j) * kD + d] = St<T>::store(sk / (double)kChunk);
+  if (tid < kD) {
+    double sk = 0.0;
+    for (int g = 0; g < NTG; ++g) sk += s_k[g][tid];
+    const double sv = s_v[0][tid] + s_v[1][tid];
+    pk[(cfirst * h_kv + (int64_t)h * P + j) * kD + tid] = St<T>::store(sk / (double)kChunk);
     const int64_t Pp = (P + kAttnTile - 1) / kAttnTile * kAttnTile;
     pv[(pool_voff[n] * h_kv + (int64_t)h * Pp) * kD + (j / kAttnTile) * kD * kAttnTile +
-       d * kAttnTile + j % kAttnTile] = St<T>::store(sv / (double)kChunk);
+       tid * kAttnTile + j % kAttnTile] = St<T>::store(sv / (double)kChunk);
   }
 }
 
