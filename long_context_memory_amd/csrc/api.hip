@@ -112,7 +112,18 @@ int resolve_splits(const Bank& bk, int mode, int splits, int n_q, int h_q, int b
   const double avg_doc = (double)bk.n_tokens / bk.desc.n_docs;
   // expected 64-entry tiles per selected document
   const double doc_tiles = pooled ? std::ceil(avg_doc / kChunk / kAttnTile) : avg_doc / kAttnTile;
-  return decode_auto_splits(bk, n_q, k, L_loc, doc_tiles);
+  int s = decode_auto_splits(bk, n_q, k, L_loc, doc_tiles);
+  if (pooled) {
+    // compressed unions are short and mostly ragged tiles (a document's few
+    // entries fill one tile): about 5 tiles per wave, which also gives two
+    // waves per SIMD, measured best on the 1M-token bank on a single stream
+    // (61 us per launch against 72 us at the per-token rule's 8 splits; two
+    // streams' overlapping launches hide the difference)
+    const double tiles = k * doc_tiles + (L_loc + kAttnTile - 1) / kAttnTile;
+    const int t5 = (int)std::min(tiles, std::ceil(tiles / 5.0));
+    s = std::min(kMaxSplits, std::max(s, ((t5 + 3) / 4) * 4));
+  }
+  return s;
 }
 
 // The compressed-memory sources: pooled entries, 64-padded V, ln 256 each
