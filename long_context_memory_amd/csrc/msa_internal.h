@@ -90,8 +90,6 @@ inline size_t dtype_size(msa_dtype t) { return t == MSA_BF16 ? 2 : 4; }
 // --------------------------------------------------------------------------
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
 // 16-byte global load with the nontemporal hint, for data a kernel streams
@@ -110,9 +108,6 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7fffu + ((u >> 16) & 1u);
   return u >> 16;
-}
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }
 
 // double -> bfloat16, round to nearest even, directly from the 64-bit pattern
@@ -180,33 +175,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
   const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
   return (a + b) + (c + d);
-}
-
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
-}
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_max64_step(uint64_t v) {
-  const uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
-  const uint64_t o = ((uint64_t)dpp_u<CTRL>(hi) << 32) | dpp_u<CTRL>(lo);
-  return o > v ? o : v;
-}
-__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), l);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
-  return ((uint64_t)hi << 32) | lo;
-}
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = dpp_max64_step<kDppXor1>(v);
-  v = dpp_max64_step<kDppXor2>(v);
-  v = dpp_max64_step<kDppHalfMirror>(v);
-  v = dpp_max64_step<kDppRowMirror>(v);
-  uint64_t a = readlane64(v, 0), b = readlane64(v, 16), c = readlane64(v, 32),
-           d = readlane64(v, 48);
-  a = a > b ? a : b;
-  c = c > d ? c : d;
-  return a > c ? a : c;
 }
 
 // Order-preserving map of a float onto uint32 (larger float -> larger code).
