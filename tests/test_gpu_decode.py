@@ -1,5 +1,7 @@
 """GPU parity of the decode path (bank build, routing, top-k, gather, split-K
 decode attention) against the fp64 oracle, through the C ABI."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -120,6 +122,40 @@ def test_route_large_batches_match_oracle(msa, B):
     ids, scores = c["bank"].route(qr, w.k)
     torch.cuda.synchronize()
     so = O.cosine_doc_scores(M.np64(qr), c["kr_o"], c["inv_o"], w.doc_len)
+    M.check_topk(ids.cpu().numpy(), scores.cpu().numpy(), so, w.k)
+
+
+@pytest.mark.parametrize("B", [5, 70])
+def test_route_float32_keys_match_oracle(msa, B):
+    # float32 keys take the vector scan (70: a pass of 64 and a pass of 6)
+    c = decode_case(msa, "tiny_f32_small")
+    w = c["w"]
+    g = torch.Generator(device=DEV)
+    g.manual_seed(7100 + B)
+    qr = torch.randn((B, w.h_r, 128), generator=g, device=DEV)
+    ids, scores = c["bank"].route(qr, w.k)
+    torch.cuda.synchronize()
+    so = O.cosine_doc_scores(M.np64(qr), c["kr_o"], c["inv_o"], w.doc_len)
+    M.check_topk(ids.cpu().numpy(), scores.cpu().numpy(), so, w.k)
+
+
+@pytest.mark.parametrize("h_r", [1, 16])
+def test_route_router_head_counts(msa, h_r):
+    # one and sixteen router heads (the pooling kernel's and the scan's
+    # extremes) on a bf16 bank of the small decode shape
+    w = dataclasses.replace(S.workload("decode_small"), h_r=h_r, name=f"decode_small_hr{h_r}")
+    r = S.route_vectors(w, DEV)
+    bank = msa.Bank(w.doc_len, w.h_r, w.h_kv, w.dtype, DEV, rope_base=w.rope_base)
+    k_raw, v_raw = S.kv_raw(w, DEV)
+    bank.build(0, w.n_docs, r, k_raw, v_raw)
+    kr_o, inv_o = M.pool_oracle(w, r)
+    np.testing.assert_array_equal(M.np64(bank.kr.permute(1, 0, 2)), kr_o)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(7200 + h_r)
+    qr = torch.randn((9, h_r, 128), generator=g, device=DEV)
+    ids, scores = bank.route(qr, w.k)
+    torch.cuda.synchronize()
+    so = O.cosine_doc_scores(M.np64(qr), kr_o, inv_o, w.doc_len)
     M.check_topk(ids.cpu().numpy(), scores.cpu().numpy(), so, w.k)
 
 
