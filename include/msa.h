@@ -33,6 +33,8 @@
  *     nothing written).  A failed HIP launch or copy returns MSA_EHIP.
  *     msa_last_error() gives a human-readable reason for the last failure
  *     on the calling thread.
+ *   - An empty batch (B or n_q = 0) is a valid call that launches nothing;
+ *     its data pointers may then be NULL.
  *   - Head size d and routing-key size d_r are 128.  Routing chunks are 256
  *     tokens; every document length is a positive multiple of 256.
  *   - dtype: MSA_F32 or MSA_BF16, the storage type of routing keys, document

@@ -148,7 +148,9 @@ int check_attend_common(const Bank& bk, int mode, int n_q, int h_q, int k, int b
   if (mode == MSA_PREFILL && (block <= 0 || n_q % block))
     return fail(MSA_EINVAL, "prefill: n_q must be a positive multiple of block");
   if (L_loc < 0) return fail(MSA_EINVAL, "L_loc < 0");
-  if (L_loc > 0 && (!k_loc || !v_loc)) return fail(MSA_EINVAL, "local K/V pointers are NULL");
+  // (an empty batch reads nothing: its local K/V may be NULL)
+  if (L_loc > 0 && n_q > 0 && (!k_loc || !v_loc))
+    return fail(MSA_EINVAL, "local K/V pointers are NULL");
   if (mode == MSA_PREFILL && L_loc < n_q)
     return fail(MSA_EINVAL, "prefill: the queries are the last n_q local tokens (L_loc >= n_q)");
   return MSA_OK;

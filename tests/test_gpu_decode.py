@@ -125,6 +125,21 @@ def test_route_large_batches_match_oracle(msa, B):
     M.check_topk(ids.cpu().numpy(), scores.cpu().numpy(), so, w.k)
 
 
+def test_zero_query_batches(msa):
+    # empty batches are valid calls that launch nothing
+    c = decode_case(msa, "decode_small")
+    w, bank = c["w"], c["bank"]
+    ids, scores = bank.route(torch.empty((0, w.h_r, 128), device=DEV), w.k)
+    assert ids.shape == (0, w.k) and scores.shape == (0, w.k)
+    q0 = c["q"][:0]
+    out = bank.attend(q0, w.q_pos, ids, c["k_loc"][:0], c["v_loc"][:0], c["L"])
+    assert out.shape == (0, w.h_q, 128)
+    ids, scores, out, st = bank.step(q0, w.q_pos, w.k, c["k_loc"][:0], c["v_loc"][:0], c["L"],
+                                     q_route=c["q_route"][:0])
+    torch.cuda.synchronize()
+    assert out.shape[1] == 0 and st.docs_copied == 0
+
+
 @pytest.mark.parametrize("B", [5, 70])
 def test_route_float32_keys_match_oracle(msa, B):
     # float32 keys take the vector scan (70: a pass of 64 and a pass of 6)
