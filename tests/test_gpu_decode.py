@@ -24,9 +24,11 @@ _CACHE = {}
 
 
 def decode_case(msa, name):
+    """Bank, inputs and oracle keys of a named workload (or a Workload)."""
+    w = S.workload(name) if isinstance(name, str) else name
+    name = w.name
     if name in _CACHE:
         return _CACHE[name]
-    w = S.workload(name)
     r = S.route_vectors(w, DEV)
     k_raw, v_raw = S.kv_raw(w, DEV)
     bank = msa.Bank(w.doc_len, w.h_r, w.h_kv, w.dtype, DEV, rope_base=w.rope_base)
@@ -233,6 +235,26 @@ def test_decode_step_matches_oracle(msa, name):
     ref = oracle_decode(c, ids_np, so)
     mx, rel = M.check_out(out[0].cpu().numpy(), ref, w.dtype, name)
     print(f"{name}: max abs {mx:.3e} rel rms {rel:.3e}")
+
+
+@pytest.mark.parametrize("h_q,k,n_docs", [(8, 4, 48), (16, 4, 48), (64, 4, 48), (32, 64, 72)])
+def test_decode_gqa_groups_and_max_k(msa, h_q, k, n_docs):
+    # one, two and eight query heads per KV head, and the largest k (64
+    # selected documents, 32K document tokens per query), on the small bf16
+    # decode shape with unplanted router queries
+    base = S.workload("decode_small")
+    w = dataclasses.replace(base, h_q=h_q, k=k, doc_len=[512] * n_docs, plant=None,
+                            name=f"decode_small_hq{h_q}_k{k}")
+    c = decode_case(msa, w)
+    ids, scores, out, _ = c["bank"].step(c["q"], w.q_pos, w.k, c["k_loc"], c["v_loc"], c["L"],
+                                         q_route=c["q_route"])
+    torch.cuda.synchronize()
+    so = oracle_scores(c)
+    ids_np = ids[0].cpu().numpy()
+    M.check_topk(ids_np, scores[0].cpu().numpy(), so, w.k)
+    ref = oracle_decode(c, ids_np, so)
+    mx, rel = M.check_out(out[0].cpu().numpy(), ref, w.dtype, w.name)
+    print(f"{w.name}: max abs {mx:.3e} rel rms {rel:.3e}")
 
 
 def test_decode_power_wrong_document_is_caught(msa):
