@@ -97,3 +97,20 @@ def test_prefill_vector_path_g2(msa):
     for blk in range(w.B // w.block):
         ref, _ = oracle_block(c, kr_o, inv_o, blk, c["ids"][blk].cpu().numpy())
         M.check_out(out[blk * w.block:(blk + 1) * w.block], ref, w.dtype, f"g2 block {blk}")
+
+
+def test_prefill_float32_bank(msa):
+    # float32 storage takes the per-query vector kernel; outputs within the
+    # float32 tolerance
+    w = dataclasses.replace(S.workload("prefill_small"), dtype="f32", doc_len=[2048] * 6, B=128,
+                            L_loc=150, name="prefill_small_f32")
+    c = run_prefill(msa, w)
+    kr_o, inv_o = M.pool_oracle(w, c["r"])
+    qb = O.block_mean_queries(M.np64(c["rt"]), w.block)
+    so = O.cosine_doc_scores(qb, kr_o, inv_o, w.doc_len)
+    M.check_topk(c["ids"].cpu().numpy(), c["scores"].cpu().numpy(), so, w.k)
+    out = c["out"].cpu().numpy()
+    for blk in range(w.B // w.block):
+        ref, _ = oracle_block(c, kr_o, inv_o, blk, c["ids"][blk].cpu().numpy())
+        mx, rel = M.check_out(out[blk * w.block:(blk + 1) * w.block], ref, w.dtype, f"f32 block {blk}")
+        print(f"f32 block {blk}: max abs {mx:.3e} rel rms {rel:.3e}")
