@@ -25,6 +25,13 @@
  *     two events) and frees them in msa_bank_destroy.  The one exception on
  *     the hot path: msa_step on a host-resident bank regrows those pinned id
  *     buffers once when a call selects more documents than they hold.
+ *   - Every data array (device, or pinned host for a host-resident store)
+ *     starts on a 16-byte boundary, as hipMalloc, hipHostMalloc and torch
+ *     allocations do; a misaligned array is MSA_EINVAL.
+ *   - No call records a memset: the library clears device memory with a
+ *     kernel, so the kernel launches of a device-bank call can be captured
+ *     into a HIP graph (a host-resident bank's msa_step synchronises and
+ *     cannot).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Calls are asynchronous on that stream unless stated; results are valid
  *     once the stream has completed the work.

@@ -66,6 +66,14 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
+// The kernels move 16-byte vectors: every data array starts on a 16-byte
+// boundary (NULL passes; its own check comes first)
+bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+template <typename... P>
+bool all_al16(P... p) {
+  return (al16(p) && ...);
+}
+
 // Workspace layout shared by msa_workspace_bytes and the entry points.
 struct WsLayout {
   size_t piecemax = 0, keys = 0, route_end = 0, qroute = 0, qrot = 0, part = 0, srcids = 0, srcoff = 0,
@@ -151,6 +159,7 @@ int check_attend_common(const Bank& bk, int mode, int n_q, int h_q, int k, int b
   // (an empty batch reads nothing: its local K/V may be NULL)
   if (L_loc > 0 && n_q > 0 && (!k_loc || !v_loc))
     return fail(MSA_EINVAL, "local K/V pointers are NULL");
+  if (!all_al16(k_loc, v_loc)) return fail(MSA_EINVAL, "local K/V must be 16-byte aligned");
   if (mode == MSA_PREFILL && L_loc < n_q)
     return fail(MSA_EINVAL, "prefill: the queries are the last n_q local tokens (L_loc >= n_q)");
   return MSA_OK;
@@ -387,6 +396,8 @@ int msa_bank_create(const msa_bank_desc* d, msa_bank** out) {
   if (d->kv_loc != MSA_KV_DEVICE && d->kv_loc != MSA_KV_HOST) return fail(MSA_EINVAL, "kv_loc");
   if (!d->kr || !d->inv_norm) return fail(MSA_EINVAL, "kr / inv_norm are NULL");
   if (!d->k_store || !d->v_store) return fail(MSA_EINVAL, "k_store / v_store are NULL");
+  if (!all_al16(d->kr, d->inv_norm, d->k_store, d->v_store))
+    return fail(MSA_EINVAL, "kr, inv_norm, k_store and v_store must be 16-byte aligned");
   if (d->chunk_cap < 0) return fail(MSA_EINVAL, "chunk_cap < 0");
 
   Bank* bk = new Bank();
@@ -488,6 +499,8 @@ int msa_build_bank(const msa_bank* b, int32_t doc0, int32_t doc1, const void* ro
     return fail(MSA_EINVAL, "k_raw and v_raw must both be given or both be NULL");
   if (k_raw && bk.desc.kv_loc != MSA_KV_DEVICE)
     return fail(MSA_EUNSUPPORTED, "K/V of a host-resident store are not written by the library");
+  if (!all_al16(route_vec, k_raw, v_raw))
+    return fail(MSA_EINVAL, "route_vec, k_raw and v_raw must be 16-byte aligned");
   hipStream_t s = (hipStream_t)stream;
   if (route_vec) MSA_CHECK_HIP(launch_pool_keys(bk, doc0, doc1, route_vec, s));
   else MSA_CHECK_HIP(launch_key_norms(bk, doc0, doc1, s));
@@ -502,6 +515,7 @@ int msa_prepare_local(const msa_bank* b, const void* k_raw, const void* v_raw, i
   if (pos0 < 0) return fail(MSA_EINVAL, "pos0 < 0");
   if (n_seq == 0 || L == 0) return MSA_OK;
   if (!k_loc || !v_loc || !k_raw || !v_raw) return fail(MSA_EINVAL, "NULL pointer");
+  if (!all_al16(k_loc, v_loc, k_raw, v_raw)) return fail(MSA_EINVAL, "16-byte alignment");
   MSA_CHECK_HIP(launch_prepare_local(*as_bank(b), k_raw, v_raw, n_seq, L, pos0, k_loc, v_loc,
                                      (hipStream_t)stream));
   return MSA_OK;
@@ -533,6 +547,7 @@ int msa_bank_set_cache(msa_bank* b, void* cache, size_t cache_bytes) {
   if (!b) return fail(MSA_EINVAL, "NULL bank");
   Bank& bk = *reinterpret_cast<Bank*>(b);
   if (bk.desc.kv_loc != MSA_KV_HOST) return fail(MSA_EINVAL, "a device cache needs a host-resident bank");
+  if (!al16(cache)) return fail(MSA_EINVAL, "the cache must be 16-byte aligned");
   std::lock_guard<std::mutex> lock(bk.host_mu);
   if (bk.attn_pending) {  // the previous cached step's attention may still read the old cache
     MSA_CHECK_HIP(hipEventSynchronize(bk.attn_done));
@@ -569,6 +584,7 @@ int msa_pooled_sizes(const msa_bank* b, int64_t* k_elems, int64_t* v_elems) {
 int msa_bank_set_pooled(msa_bank* b, void* pool_k, void* pool_v) {
   if (!b) return fail(MSA_EINVAL, "NULL bank");
   if ((pool_k == nullptr) != (pool_v == nullptr)) return fail(MSA_EINVAL, "pool_k and pool_v");
+  if (!all_al16(pool_k, pool_v)) return fail(MSA_EINVAL, "pool_k / pool_v must be 16-byte aligned");
   Bank& bk = *reinterpret_cast<Bank*>(b);
   bk.pool_k = pool_k;
   bk.pool_v = pool_v;
@@ -596,6 +612,7 @@ int msa_route(const msa_bank* b, const float* q_route, int32_t B, int32_t k,
   if (k > kMaxK) return fail(MSA_EUNSUPPORTED, "k must be <= 64");
   if (B == 0) return MSA_OK;
   if (!q_route || !ids || !scores || !ws) return fail(MSA_EINVAL, "NULL pointer");
+  if (!all_al16(q_route, ws)) return fail(MSA_EINVAL, "q_route and ws must be 16-byte aligned");
   const WsLayout L = ws_layout(bk, MSA_DECODE, B, bk.desc.h_kv, k, 1, 1, 4);
   const size_t need = L.route_end;
   if (ws_bytes < need) return fail(MSA_ENOMEM, "workspace too small for msa_route");
@@ -615,6 +632,8 @@ int msa_attend(const msa_bank* b, const msa_attend_args* a, void* stream) {
   if (st) return st;
   if (a->n_q == 0) return MSA_OK;
   if (!a->q || !a->out || !a->ws || (a->k > 0 && !a->ids)) return fail(MSA_EINVAL, "NULL pointer");
+  if (!all_al16(a->q, a->out, a->ws, a->src_k, a->src_v))
+    return fail(MSA_EINVAL, "q, out, ws and source K/V must be 16-byte aligned");
   if (a->q_pos < 0) return fail(MSA_EINVAL, "q_pos < 0");
   AttnSources src{bk.desc.k_store, bk.desc.v_store, bk.d_kv_off, bk.d_doc_len, bk.desc.n_docs};
   const bool pooled = a->memory == MSA_MEMORY_POOLED;
@@ -675,6 +694,8 @@ int msa_step(const msa_bank* b, const msa_step_args* a, void* stream, void* copy
   if (a->n_q == 0) return MSA_OK;
   if (!a->q || !a->ids || !a->scores || !a->out || !a->ws) return fail(MSA_EINVAL, "NULL pointer");
   if (prefill ? !a->route_tokens : !a->q_route) return fail(MSA_EINVAL, "router input is NULL");
+  if (!all_al16(a->q, a->out, a->ws, a->q_route, a->route_tokens, a->staging, a->w_proj))
+    return fail(MSA_EINVAL, "q, out, ws, router input, w_proj and staging must be 16-byte aligned");
   if (a->q_pos < 0) return fail(MSA_EINVAL, "q_pos < 0");
   const bool pooled = a->memory == MSA_MEMORY_POOLED;
   if (a->memory != MSA_MEMORY_TOKENS && !pooled) return fail(MSA_EINVAL, "memory");
@@ -716,7 +737,7 @@ int msa_step(const msa_bank* b, const msa_step_args* a, void* stream, void* copy
   uint32_t* excl = a->exclude;
   if (a->exclude_selected && !excl) {
     excl = (uint32_t*)(w + L.excl);
-    MSA_CHECK_HIP(hipMemsetAsync(excl, 0, (size_t)n_groups * W * 4, s));
+    MSA_CHECK_HIP(launch_fill_zero(excl, (size_t)n_groups * W * 4, s));
   }
   float* q_route = (float*)(w + L.qroute);
   if (prefill) {

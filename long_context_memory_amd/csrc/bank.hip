@@ -380,8 +380,8 @@ hipError_t launch_pool_kv(const Bank& bk, int doc0, int doc1, hipStream_t s) {
   const size_t esz = dtype_size(bk.desc.dtype);
   const size_t row = (size_t)bk.desc.h_kv * kD * esz;
   // V rows past a document's last entry (tile padding) are zero
-  hipError_t e = hipMemsetAsync((char*)bk.pool_v + (size_t)bk.pool_voff[doc0] * row, 0,
-                                (size_t)(bk.pool_voff[doc1] - bk.pool_voff[doc0]) * row, s);
+  hipError_t e = launch_fill_zero((char*)bk.pool_v + (size_t)bk.pool_voff[doc0] * row,
+                                 (size_t)(bk.pool_voff[doc1] - bk.pool_voff[doc0]) * row, s);
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)nc, (unsigned)bk.desc.h_kv);
   if (bk.desc.dtype == MSA_BF16)

@@ -209,6 +209,9 @@ hipError_t launch_route_scan(const Bank& bk, const float* q_route, int B, float*
 // HBM read-rate probe: kStreamReadBlocks workgroups; out holds one word each
 constexpr int kStreamReadBlocks = 4096;
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* out, hipStream_t s);
+// zero `bytes` (a multiple of 4) at a 4-byte-aligned device address with a
+// kernel (no memset node if the caller captures the stream into a graph)
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_topk(const Bank& bk, const float* piecemax, int B, int k,
                        const uint32_t* exclude, uint32_t* exclude_out, int32_t* ids,
                        float* scores, uint64_t* keys, hipStream_t s);

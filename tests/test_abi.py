@@ -66,6 +66,10 @@ def _desc(msa, **kw):
     (dict(k_store=None), 1),
     (dict(kv_tokens=100), 1),
     (dict(kv_loc=5), 1),
+    (dict(kr=24), 1),  # arrays must start on a 16-byte boundary
+    (dict(inv_norm=20), 1),
+    (dict(k_store=8), 1),
+    (dict(v_store=40), 1),
 ])
 def test_bank_create_rejects_bad_descriptors(msa, bad, code):
     d, _keep = _desc(msa, **bad)

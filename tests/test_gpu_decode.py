@@ -142,6 +142,26 @@ def test_zero_query_batches(msa):
     assert out.shape[1] == 0 and st.docs_copied == 0
 
 
+def test_misaligned_arrays_are_rejected(msa):
+    # a contiguous view that starts 2 bytes into its storage: refused before
+    # any launch, and the output is left as it was
+    c = decode_case(msa, "decode_small")
+    w, bank = c["w"], c["bank"]
+    flat = torch.empty(c["q"].numel() + 8, dtype=c["q"].dtype, device=DEV)
+    q_bad = flat[1:1 + c["q"].numel()].view(c["q"].shape)
+    q_bad.copy_(c["q"])
+    ids, _ = bank.route(c["q_route"], w.k)
+    out = torch.full((w.B, w.h_q, 128), 3.0, device=DEV)
+    with pytest.raises(msa.MSAError) as e:
+        bank.attend(q_bad, w.q_pos, ids, c["k_loc"], c["v_loc"], c["L"], out=out)
+    assert e.value.status == msa.MSA_EINVAL
+    assert "aligned" in msa.lib.msa_last_error().decode()
+    with pytest.raises(msa.MSAError):
+        bank.step(q_bad, w.q_pos, w.k, c["k_loc"], c["v_loc"], c["L"], q_route=c["q_route"])
+    torch.cuda.synchronize()
+    assert bool((out == 3.0).all())
+
+
 @pytest.mark.parametrize("B", [5, 70])
 def test_route_float32_keys_match_oracle(msa, B):
     # float32 keys take the vector scan (70: a pass of 64 and a pass of 6)
