@@ -24,6 +24,7 @@ sys.path.insert(0, ROOT)
 METRIC = "routed decode queries/sec at 1M-token bank; % peak HBM GB/s; prefill MFMA %"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0  # dense bf16
+TIMER_PERIOD = 5  # two-stream decode legs: HIP events bracket every 5th launch
 
 
 def log(msg):
@@ -465,7 +466,10 @@ def main():
     torch.cuda.synchronize()
     log("timed")
     msa.timer_reserve(2 * args.steps)  # attention + routing intervals, events made up front
-    msa.timer_enable(True)
+    # events bracket every TIMER_PERIOD-th launch of the timed region (an odd
+    # period samples both streams); bracketing every launch costs the step
+    # about 2% (four event records per step on the streams)
+    msa.timer_enable(True, TIMER_PERIOD)
     msa.timer_read(msa.MSA_TIMER_ATTENTION)
     msa.timer_read(msa.MSA_TIMER_ROUTE)
     torch.cuda.synchronize()
@@ -542,7 +546,7 @@ def main():
             pstep(i)
         torch.cuda.synchronize()
         msa.timer_reserve(2 * args.pooled_steps)
-        msa.timer_enable(True)
+        msa.timer_enable(True, TIMER_PERIOD)
         msa.timer_read(msa.MSA_TIMER_ATTENTION)
         msa.timer_read(msa.MSA_TIMER_ROUTE)
         t0 = time.perf_counter()

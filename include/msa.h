@@ -338,15 +338,18 @@ int msa_step(const msa_bank* bank, const msa_step_args* args, void* stream,
              void* copy_stream, msa_step_stats* stats);
 
 /* Kernel timing for measurement.  While enabled on the calling thread, the
- * library brackets every launch of the kernel class `which` with a pair of
- * HIP events on the stream it launches on.  msa_timer_read synchronises
- * those events, returns the accumulated milliseconds and the number of
- * launches since the last read, and clears them.
+ * library brackets launches of the kernel class `which` with a pair of HIP
+ * events on the stream it launches on: every `period`-th launch of each
+ * class, counted from the enabling call (period 1 = every launch; a larger
+ * period keeps the events' own cost on the stream small).  msa_timer_read
+ * synchronises those events, returns the accumulated milliseconds and the
+ * number of bracketed launches since the last read, and clears them.
  *   which: MSA_TIMER_ATTENTION (decode or prefill attention kernel),
  *          MSA_TIMER_ROUTE (routing scan: the scan launches of one call,
- *          as one interval). */
+ *          as one interval).
+ *   period: <= 0 disables the timer. */
 enum { MSA_TIMER_ATTENTION = 0, MSA_TIMER_ROUTE = 1 };
-int msa_timer_enable(int on);
+int msa_timer_enable(int period);
 int msa_timer_read(int which, double* total_ms, int64_t* launches);
 /* Create the events for `launches` timed launches ahead of a timed region
  * (events are otherwise created on first use, on the host, inside it).

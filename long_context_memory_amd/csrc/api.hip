@@ -18,6 +18,9 @@ void set_error(const std::string& msg) { g_last_error = msg; }
 // ---- kernel timing (measurement only; off by default)
 struct TimerState {
   bool on = false;
+  int64_t period = 1;         // bracket every period-th launch of a class
+  int64_t seq[2] = {0, 0};    // launches of each class since enabling
+  bool skipping[2] = {false, false};  // the open launch is not bracketed
   std::vector<std::pair<hipEvent_t, hipEvent_t>> done[2];
   std::vector<hipEvent_t> pool;
   hipEvent_t open[2] = {nullptr, nullptr};
@@ -37,6 +40,8 @@ static hipEvent_t timer_event() {
 
 void timer_mark(int which, bool begin, hipStream_t s) {
   if (!g_timer.on || which < 0 || which > 1) return;
+  if (begin) g_timer.skipping[which] = g_timer.seq[which]++ % g_timer.period != 0;
+  if (g_timer.skipping[which]) return;
   hipEvent_t e = timer_event();
   if (!e) return;
   (void)hipEventRecord(e, s);
@@ -208,8 +213,11 @@ const char* msa_last_error(void) { return g_last_error.c_str(); }
 
 int msa_version(void) { return 10200; }
 
-int msa_timer_enable(int on) {
-  g_timer.on = on != 0;
+int msa_timer_enable(int period) {
+  g_timer.on = period > 0;
+  g_timer.period = std::max(1, period);
+  g_timer.seq[0] = g_timer.seq[1] = 0;
+  g_timer.skipping[0] = g_timer.skipping[1] = false;
   return MSA_OK;
 }
 

@@ -123,8 +123,12 @@ def _load():
 lib = _load()
 
 
-def timer_enable(on: bool = True):
-    _check(lib.msa_timer_enable(int(bool(on))), "msa_timer_enable")
+def timer_enable(on: bool = True, period: int = 1):
+    """Bracket every `period`-th attention and routing launch with HIP events
+    (on = False disables)."""
+    if on and int(period) < 1:
+        raise ValueError("period must be >= 1")
+    _check(lib.msa_timer_enable(int(period) if on else 0), "msa_timer_enable")
 
 
 def timer_reserve(launches: int):

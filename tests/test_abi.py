@@ -94,6 +94,9 @@ def test_null_arguments(msa):
     assert msa.lib.msa_timer_read(0, None, None) == msa.MSA_EINVAL
     assert msa.lib.msa_timer_reserve(-1) == msa.MSA_EINVAL
     assert msa.lib.msa_timer_reserve(0) == msa.MSA_OK  # nothing to create: no device needed
+    with pytest.raises(ValueError):
+        msa.timer_enable(True, 0)
+    assert msa.lib.msa_timer_enable(0) == msa.MSA_OK  # disabling needs no device
     # the read-rate probe validates before any launch (these pointers are never read)
     out = C.c_void_p(4096)
     assert msa.lib.msa_stream_read(None, 1 << 20, out, None) == msa.MSA_EINVAL

@@ -142,6 +142,23 @@ def test_zero_query_batches(msa):
     assert out.shape[1] == 0 and st.docs_copied == 0
 
 
+def test_timer_brackets_every_period_th_launch(msa):
+    c = decode_case(msa, "decode_small")
+    w, bank = c["w"], c["bank"]
+    ids, _ = bank.route(c["q_route"], w.k)
+    torch.cuda.synchronize()
+    msa.timer_reserve(8)
+    msa.timer_enable(True, 3)
+    for _ in range(7):  # launches 0, 3 and 6 are bracketed
+        bank.attend(c["q"], w.q_pos, ids, c["k_loc"], c["v_loc"], c["L"])
+    ms, n = msa.timer_read(msa.MSA_TIMER_ATTENTION)
+    msa.timer_enable(False)
+    assert n == 3 and ms > 0.0
+    bank.attend(c["q"], w.q_pos, ids, c["k_loc"], c["v_loc"], c["L"])  # disabled: not timed
+    ms, n = msa.timer_read(msa.MSA_TIMER_ATTENTION)
+    assert n == 0 and ms == 0.0
+
+
 def test_misaligned_arrays_are_rejected(msa):
     # a contiguous view that starts 2 bytes into its storage: refused before
     # any launch, and the output is left as it was
