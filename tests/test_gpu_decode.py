@@ -314,8 +314,9 @@ def test_decode_splits_and_determinism(msa, name):
     c = decode_case(msa, name)
     w = c["w"]
     ids, _ = c["bank"].route(c["q_route"], w.k)
+    # 256 (the maximum) exceeds the tiles of every union: empty splits merge as nothing
     outs = [c["bank"].attend(c["q"], w.q_pos, ids, c["k_loc"], c["v_loc"], c["L"], splits=s)
-            for s in (4, 8, 64)]
+            for s in (4, 8, 64, 256)]
     again = c["bank"].attend(c["q"], w.q_pos, ids, c["k_loc"], c["v_loc"], c["L"], splits=8)
     torch.cuda.synchronize()
     assert torch.equal(outs[1], again)  # deterministic

@@ -83,9 +83,11 @@ def test_prefill_small_matches_oracle(msa):
 def test_prefill_splits_agree(msa):
     w = S.workload("prefill_small")
     a = run_prefill(msa, w, splits=1)["out"]
-    b = run_prefill(msa, w, splits=5)["out"]
     scale = float(a.abs().max())
-    assert float((a - b).abs().max()) <= 2.0 ** -8 * scale
+    # 200 splits exceed a block's ~100 tiles: empty splits merge as nothing
+    for s in (5, 200):
+        b = run_prefill(msa, w, splits=s)["out"]
+        assert float((a - b).abs().max()) <= 2.0 ** -8 * scale, s
 
 
 def test_prefill_vector_path_g2(msa):
