@@ -309,6 +309,30 @@ def test_decode_power_wrong_document_is_caught(msa):
         M.check_out(out[0].cpu().numpy(), ref_bad, w.dtype, "power")
 
 
+def test_decode_skips_empty_id_slots(msa):
+    # -1 (an empty top-k slot) and ids outside [0, n_docs) select nothing:
+    # the output is the oracle's over the remaining documents
+    c = decode_case(msa, "decode_small")
+    w = c["w"]
+    ids, _ = c["bank"].route(c["q_route"], w.k)
+    ids = ids.clone()
+    ids[0::2, -1] = -1
+    ids[1, 0] = w.n_docs + 5
+    ids[2, :] = -1  # local context only
+    out = c["bank"].attend(c["q"], w.q_pos, ids, c["k_loc"], c["v_loc"], c["L"])
+    torch.cuda.synchronize()
+    q, lk, lv = M.np64(c["q"]), M.np64(c["lk"]), M.np64(c["lv"])
+    ids_np = ids.cpu().numpy()
+    cache = {}
+    for b in range(w.B):
+        sel = [int(n) for n in ids_np[b] if 0 <= n < w.n_docs]
+        for n in sel:
+            if n not in cache:
+                cache[n] = M.oracle_doc_kv(w, c["k_raw"], c["v_raw"], n)
+        ref = M.oracle_attend_decode(w, q[b], w.q_pos, sel, cache, lk[b], lv[b], w.P0)
+        M.check_out(out[b].cpu().numpy(), ref, w.dtype, f"query {b}")
+
+
 @pytest.mark.parametrize("name", ["tiny_f32_small", "decode_small"])
 def test_decode_splits_and_determinism(msa, name):
     c = decode_case(msa, name)
