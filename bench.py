@@ -225,7 +225,7 @@ def prefill_bench(steps, warmup, splits=0):
             "attention": {"bound": "mfma", "achieved": flops / att_s / 1e12,
                           "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                           "frac": flops / att_s / 1e12 / MFMA_PEAK_TFLOPS,
-                          "traffic": measured_traffic("prefill_c3_counters"),
+                          "traffic": measured_traffic("prefill_8m_counters"),
                           "flops_per_launch": flops, "avg_launch_us": att_s * 1e6,
                           "hbm_GBs": kv_bytes / att_s / 1e9}}
 
@@ -500,7 +500,7 @@ def main():
                    "rotating_batches": args.batches},
         "roofline": {"kernel": "decode attention (split-K)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic("decode_c2_counters"),
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic("decode_1m_counters"),
                      "bytes_per_launch": kv_bytes, "avg_launch_us": att_avg_us,
                      "launches": att_n,
                      # the two streams' launches overlap, so a launch's duration
@@ -513,7 +513,7 @@ def main():
         # stream's attention
         "routing": {"kernel": "cosine routing scan (overlapped with attention)", "bound": "hbm",
                     "bytes_per_launch": w.C * w.h_r * (128 * 2 + 4),
-                    "traffic": measured_traffic("route_c2_counters"),
+                    "traffic": measured_traffic("route_1m_counters"),
                     "avg_launch_us": rt_ms * 1e3 / max(rt_n, 1), "launches": rt_n,
                     "achieved": w.C * w.h_r * (128 * 2 + 4) / (rt_ms * 1e-3 / max(rt_n, 1)) / 1e9,
                     "unit": "GB/s", "peak": HBM_PEAK_GBS},

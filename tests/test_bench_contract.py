@@ -28,7 +28,7 @@ def test_code_tokens_ignore_comments_and_layout():
 
 
 def test_traffic_records_are_complete():
-    for name in ("decode_c2_counters", "prefill_c3_counters", "route_c2_counters"):
+    for name in ("decode_1m_counters", "prefill_8m_counters", "route_1m_counters"):
         path = os.path.join(ROOT, "profiles", name + ".json")
         with open(path) as f:
             rec = json.load(f)
