@@ -37,15 +37,18 @@ def run_prefill(msa, w, splits=0):
                 scores=scores[0], out=out[0], bank=bank, k_loc=k_loc, v_loc=v_loc)
 
 
-def oracle_block(c, kr_o, inv_o, blk, ids_gpu, queries=None):
+def oracle_block(c, kr_o, inv_o, blk, ids_gpu, queries=None, sel=None):
     """Oracle outputs of block `blk` (optionally a subset of its queries) with
-    the oracle's own selection, or the GPU's when it is a valid near-tie."""
+    the oracle's own selection, or the GPU's when it is a valid near-tie, or
+    the documents `sel` when given (no routing)."""
     w = c["w"]
     L, Lq, bsz = w.L_loc, w.B, w.block
-    qb = O.block_mean_queries(M.np64(c["rt"][blk * bsz:(blk + 1) * bsz]), bsz)
-    so = O.cosine_doc_scores(qb, kr_o, inv_o, w.doc_len)
-    o_ids, _ = O.select_topk(so, w.k)
-    sel = o_ids[0] if set(o_ids[0].tolist()) == set(ids_gpu.tolist()) else ids_gpu
+    so = None
+    if sel is None:
+        qb = O.block_mean_queries(M.np64(c["rt"][blk * bsz:(blk + 1) * bsz]), bsz)
+        so = O.cosine_doc_scores(qb, kr_o, inv_o, w.doc_len)
+        o_ids, _ = O.select_topk(so, w.k)
+        sel = o_ids[0] if set(o_ids[0].tolist()) == set(ids_gpu.tolist()) else ids_gpu
     kv = [M.oracle_doc_kv(w, c["k_raw"], c["v_raw"], n) for n in sel]
     lk = O.round_to_storage(O.rope_rotate(M.np64(c["lk"]), (w.P0 + np.arange(L))[:, None],
                                           w.rope_base), w.dtype)
@@ -78,6 +81,28 @@ def test_prefill_small_matches_oracle(msa):
         ref, _ = oracle_block(c, kr_o, inv_o, blk, c["ids"][blk].cpu().numpy())
         mx, rel = M.check_out(out[blk * w.block:(blk + 1) * w.block], ref, w.dtype, f"block {blk}")
         print(f"block {blk}: max abs {mx:.3e} rel rms {rel:.3e}")
+
+
+def test_prefill_skips_empty_id_slots(msa):
+    # -1 and out-of-range ids select nothing: each block attends to its
+    # remaining documents (block 2: none, the causal local context only)
+    w = S.workload("prefill_small")
+    c = run_prefill(msa, w)
+    ids = c["ids"].clone()
+    ids[0, -1] = -1
+    ids[1, 0] = w.n_docs + 3
+    ids[2, :] = -1
+    k_loc, v_loc = c["k_loc"], c["v_loc"]
+    q_pos = w.P0 + (w.L_loc - w.B)
+    out = c["bank"].attend(c["q"], q_pos, ids, k_loc, v_loc, w.L_loc, mode=msa.MSA_PREFILL,
+                           block=w.block)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    ids_np = ids.cpu().numpy()
+    for blk in range(w.B // w.block):
+        sel = [int(n) for n in ids_np[blk] if 0 <= n < w.n_docs]
+        ref, _ = oracle_block(c, None, None, blk, None, sel=sel)
+        M.check_out(out[blk * w.block:(blk + 1) * w.block], ref, w.dtype, f"block {blk}")
 
 
 def test_prefill_splits_agree(msa):
