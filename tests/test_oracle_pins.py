@@ -430,3 +430,40 @@ def test_pooled_decode_step_reduces_to_decode_step_on_constant_chunks():
     np.testing.assert_array_equal(ia, ib)
     np.testing.assert_allclose(b, a, rtol=0, atol=1e-12)
 
+
+
+# ---------------------------------------------------------------- helpers, pinned directly
+def test_chunk_offsets_hand_values():
+    # documents of 1, 2 and 3 chunks own chunks [0,1), [1,3), [3,6)
+    np.testing.assert_array_equal(O.chunk_offsets([256, 512, 768]), [0, 1, 3, 6])
+    with pytest.raises(ValueError):
+        O.chunk_offsets([256, 300])
+    with pytest.raises(ValueError):
+        O.chunk_offsets([0])
+
+
+def test_rope_frequencies_closed_form():
+    # theta_0 = 1, theta_{d/2-1} = base^(-(d-2)/d), a constant ratio base^(-2/d)
+    d, base = 128, 10000.0
+    th = O.rope_frequencies(d, base)
+    assert th.shape == (64,) and th[0] == 1.0
+    assert math.isclose(th[-1], base ** (-(d - 2) / d), rel_tol=1e-15)
+    np.testing.assert_allclose(th[1:] / th[:-1], base ** (-2.0 / d), rtol=1e-14)
+    # d = 4: angles 1 and base^-1/2, by hand
+    np.testing.assert_allclose(O.rope_frequencies(4, 100.0), [1.0, 0.1], rtol=1e-15)
+
+
+def test_union_kv_order_and_rows():
+    # rows tagged by (document, token): the union holds the selected
+    # documents' rows in rank order, then the local rows
+    doc_len = [2, 3, 1]
+    T = sum(doc_len)
+    bank_k = np.arange(T, dtype=np.float64).reshape(T, 1, 1) * np.ones((1, 1, 4))
+    bank_v = -bank_k
+    loc_k = np.full((2, 1, 4), 100.0)
+    loc_v = np.full((2, 1, 4), 200.0)
+    K, V = O.union_kv([2, 0], bank_k, bank_v, doc_len, loc_k, loc_v)
+    np.testing.assert_array_equal(K[:, 0, 0], [5, 0, 1, 100, 100])
+    np.testing.assert_array_equal(V[:, 0, 0], [-5, 0, -1, 200, 200])
+    K, V = O.union_kv([], bank_k, bank_v, doc_len, loc_k, loc_v)
+    assert K.shape == (2, 1, 4)
