@@ -83,10 +83,14 @@ def test_prefill_small_matches_oracle(msa):
         print(f"block {blk}: max abs {mx:.3e} rel rms {rel:.3e}")
 
 
-def test_prefill_skips_empty_id_slots(msa):
+@pytest.mark.parametrize("g", [4, 2])
+def test_prefill_skips_empty_id_slots(msa, g):
     # -1 and out-of-range ids select nothing: each block attends to its
-    # remaining documents (block 2: none, the causal local context only)
+    # remaining documents (block 2: none, the causal local context only);
+    # G = 4 runs the matrix-core kernel, G = 2 the vector kernel
     w = S.workload("prefill_small")
+    if w.h_q != g * w.h_kv:
+        w = dataclasses.replace(w, h_q=g * w.h_kv, name=f"prefill_small_g{g}")
     c = run_prefill(msa, w)
     ids = c["ids"].clone()
     ids[0, -1] = -1
