@@ -107,11 +107,16 @@ def cpu_baseline(w, r_dev, k_raw_dev, v_raw_dev, batch_inputs, budget_s=12.0):
     import numpy as np
     import torch
     from oracle import msa_oracle as O
+    from threadpoolctl import threadpool_info, threadpool_limits
+    cores = len(os.sched_getaffinity(0))
+    limits = threadpool_limits(limits=cores, user_api="blas")  # BLAS on every allowed core
+    blas = [f"{i.get('internal_api')} {i.get('version')} ({i.get('num_threads')} threads)"
+            for i in threadpool_info() if i.get("user_api") == "blas"]
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        deps = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas_build = f"{deps.get('name')} {deps.get('version')}"
     except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
+        blas_build = None
 
     f64 = lambda t: t.detach().to("cpu", torch.float32).double().numpy()  # noqa: E731
     off = np.concatenate([[0], np.cumsum(w.doc_len)])
@@ -151,7 +156,9 @@ def cpu_baseline(w, r_dev, k_raw_dev, v_raw_dev, batch_inputs, budget_s=12.0):
         dt = time.perf_counter() - t0
         if dt >= budget_s or n >= 50:
             break
+    limits.restore_original_limits()
     return {"value": w.B * n / dt, "unit": "queries/s", "cores": int(cores), "kind": "oracle",
+            "blas": blas, "blas_build": blas_build,
             "sample": f"{n} full 16-query decode step(s) of the 1M-token bank: cosine routing "
                       "over all 4096 chunks x 8 heads, top-16, gather, GQA attention over "
                       "12,288 tokens x 32 heads per query (bank build and local RoPE are "
@@ -230,12 +237,16 @@ def prefill_bench(steps, warmup, splits=0):
                           "hbm_GBs": kv_bytes / att_s / 1e9}}
 
 
-def host_bank_bench(steps, warmup, cache_gb=0.0):
+def host_bank_bench(steps, warmup, cache_gb=200.0, window=4):
     """The 100M-token host-resident bank (12,207 x 8192 + one 256-token
     document; routing keys in HBM, K/V in pinned host memory backed by 384
-    document slots): 8-query decode steps, each copying its selected
-    documents' K/V to the GPU.  Reports queries/s, the host-to-device rate
-    of those copies and, for reference, a plain pinned 1 GiB copy."""
+    document slots): 8-query decode steps, each reading its selected
+    documents' K/V from host memory.  Two runs on one bank: (1) every
+    selected document copied into device staging each step; (2) a device
+    document cache of cache_gb with a prefetch window: batch i + window is
+    routed and its documents copied into the cache while batch i steps.
+    Reports queries/s, the host-to-device rate of the copies, a plain pinned
+    1 GiB copy's rate in the same run, and the routing scan's HBM rate."""
     import torch
     from long_context_memory_amd import msa, synth as S
 
@@ -252,49 +263,11 @@ def host_bank_bench(steps, warmup, cache_gb=0.0):
     q = S.queries(w, dev)
     lk, lv = S.local_raw(w, dev)
     k_loc, v_loc, L = bank.prepare_local(lk, lv, w.P0)
+    main, side, cs = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
     ws = bank.workspace(msa.MSA_DECODE, w.B, w.h_q, w.k)
-    stg = None
-    slots = 0
-    if cache_gb > 0:
-        # device document cache: each step routes fresh queries, so hits
-        # come from the cache holding a share of the bank, not from repeats
-        slot = bank.cache_slot_bytes()
-        slots = int(cache_gb * 1e9) // slot
-        bank.set_cache(torch.empty(slots * slot, dtype=torch.uint8, device=dev))
-        warmup = max(warmup, -(-slots // (w.B * w.k)) + 4)
-    else:
-        stg = bank.staging(w.B, w.k)
-    cs = torch.cuda.Stream()
-    torch.cuda.synchronize()
-    copied = [0, 0, 0]
-
-    def step(i, count):
-        q_route = S.route_queries(w, dev, batch=i)
-        _, _, _, st = bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=q_route, ws=ws,
-                                staging=stg, copy_stream=cs)
-        if count:
-            copied[0] += st.bytes_copied
-            copied[1] += st.docs_copied
-            copied[2] += st.docs_cached
-
-    log(f"host bank: {warmup} warm-up steps, cache slots {slots}")
-    for i in range(warmup):
-        step(i, False)
-    torch.cuda.synchronize()
-    msa.timer_reserve(2 * steps)
-    msa.timer_enable(True)
-    msa.timer_read(msa.MSA_TIMER_ATTENTION)
-    msa.timer_read(msa.MSA_TIMER_ROUTE)
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(warmup + i, True)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    msa.timer_read(msa.MSA_TIMER_ATTENTION)
-    rt_ms, rt_n = msa.timer_read(msa.MSA_TIMER_ROUTE)
-    msa.timer_enable(False)
+    ws_side = bank.workspace(msa.MSA_DECODE, w.B, w.h_q, w.k)
     rt_bytes = w.C * w.h_r * (128 * 2 + 4)  # every routing key (bf16) and its norm
-    bank.set_cache(None)
+
     # a plain pinned host -> device copy of 1 GiB, for the link's own rate
     hsrc = torch.empty(1 << 28, dtype=torch.float32, pin_memory=True)
     ddst = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -305,20 +278,75 @@ def host_bank_bench(steps, warmup, cache_gb=0.0):
         ddst.copy_(hsrc, non_blocking=True)
     torch.cuda.synchronize()
     link = 5 * (1 << 30) / (time.perf_counter() - tc) / 1e9
+    del hsrc, ddst
+
+    def run(n_warm, n_steps, cached):
+        total = n_warm + n_steps
+        qrs = [S.route_queries(w, dev, batch=i) for i in range(total + window)]
+        stg = None if cached else bank.staging(w.B, w.k)
+        copied = [0, 0, 0]  # bytes, documents copied, documents found cached
+
+        def count(st):
+            copied[0] += st.bytes_copied
+            copied[1] += st.docs_copied
+            copied[2] += st.docs_cached
+
+        if cached:
+            for i in range(window):
+                bank.prefetch(qrs[i], w.k, ws=ws_side, stream=side, copy_stream=cs)
+        t0 = None
+        for i in range(total):
+            if i == n_warm:
+                torch.cuda.synchronize()
+                msa.timer_reserve(2 * n_steps)
+                msa.timer_enable(True)
+                msa.timer_read(msa.MSA_TIMER_ATTENTION)
+                msa.timer_read(msa.MSA_TIMER_ROUTE)
+                copied[:] = [0, 0, 0]
+                t0 = time.perf_counter()
+            if cached:
+                count(bank.prefetch(qrs[i + window], w.k, ws=ws_side, stream=side,
+                                    copy_stream=cs))
+            _, _, _, st = bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=qrs[i], ws=ws,
+                                    staging=stg, stream=main, copy_stream=cs)
+            count(st)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        msa.timer_read(msa.MSA_TIMER_ATTENTION)
+        rt_ms, rt_n = msa.timer_read(msa.MSA_TIMER_ROUTE)
+        msa.timer_enable(False)
+        return {"queries_per_s": w.B * n_steps / dt, "ms_per_step": dt * 1e3 / n_steps,
+                "steps": n_steps, "h2d_GBs": copied[0] / dt / 1e9,
+                "h2d_frac_of_pinned_copy": copied[0] / dt / 1e9 / link,
+                "docs_copied_per_step": copied[1] / n_steps,
+                "bytes_copied_per_step": copied[0] / n_steps,
+                "docs_cached_per_step": copied[2] / n_steps,
+                "routing_avg_launch_us": rt_ms * 1e3 / max(rt_n, 1),
+                "routing_GBs": rt_bytes / (rt_ms * 1e-3 / max(rt_n, 1)) / 1e9}
+
+    log(f"host bank: staging path, {warmup} + {steps} steps")
+    plain = run(warmup, steps, False)
+    slot = bank.cache_slot_bytes()
+    slots = int(cache_gb * 1e9) // slot
+    bank.set_cache(torch.empty(slots * slot, dtype=torch.uint8, device=dev))
+    # each step routes fresh queries: hits come from the cache holding a share
+    # of the bank, so the cache is filled before the timed steps
+    fill = -(-slots // (w.B * w.k)) + 4
+    log(f"host bank: cache of {slots} slots, prefetch window {window}, {fill} + {steps} steps")
+    cached = run(fill, steps, True)
+    bank.set_cache(None)
+    cached.update({"cache_slots": slots, "cache_bytes": slots * slot,
+                   "cache_share_of_documents": slots / w.n_docs, "prefetch_window": window,
+                   "hit_rate": cached["docs_cached_per_step"] /
+                   max(1e-9, cached["docs_cached_per_step"] + cached["docs_copied_per_step"])})
     return {"workload": "100M-token host-resident bank: 12,207 docs x 8192 + one 256-token doc "
                         "(390,625 chunks, bf16 keys in HBM), K/V in pinned host memory (384 "
                         "document slots), B=8, top-16, local 4096",
-            "queries_per_s": w.B * steps / dt, "ms_per_step": dt * 1e3 / steps, "steps": steps,
-            "h2d_GBs": copied[0] / dt / 1e9, "docs_copied_per_step": copied[1] / steps,
-            "bytes_copied_per_step": copied[0] / steps, "pinned_copy_GBs": link,
-            "h2d_frac_of_pinned_copy": copied[0] / dt / 1e9 / link,
+            "pinned_copy_GBs": link, "staging": plain, "cached_prefetch": cached,
             "routing": {"bound": "hbm", "bytes_per_launch": rt_bytes,
-                        "avg_launch_us": rt_ms * 1e3 / max(rt_n, 1),
-                        "achieved": rt_bytes / (rt_ms * 1e-3 / max(rt_n, 1)) / 1e9,
-                        "peak": HBM_PEAK_GBS, "unit": "GB/s"},
-            "cache": {"slots": slots, "bytes": slots * bank.cache_slot_bytes(),
-                      "share_of_documents": slots / w.n_docs,
-                      "hit_rate": copied[2] / max(1, copied[1] + copied[2])} if slots else None}
+                        "avg_launch_us": plain["routing_avg_launch_us"],
+                        "achieved": plain["routing_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": plain["routing_GBs"] / HBM_PEAK_GBS}}
 
 
 def interleave_bench(steps, warmup):
@@ -406,12 +434,17 @@ def main():
     ap.add_argument("--prefill-splits", type=int, default=0, help="token splits (0: automatic)")
     ap.add_argument("--pooled-steps", type=int, default=0,
                     help="also time compressed-memory decode on the same bank (0 skips it)")
-    ap.add_argument("--host-bank-steps", type=int, default=0,
-                    help="also run the 100M-token host-bank leg (0 skips it)")
-    ap.add_argument("--host-cache-gb", type=float, default=0.0,
-                    help="device document cache for the host-bank leg, GB (0: none)")
-    ap.add_argument("--interleave-steps", type=int, default=0,
-                    help="also run the 3-hop interleave leg over 32 Mi tokens (0 skips it)")
+    ap.add_argument("--single-stream-steps", type=int, default=300,
+                    help="decode steps on one stream, every attention launch event-timed "
+                         "(the kernel's isolated duration; 0 skips it)")
+    ap.add_argument("--host-bank-steps", type=int, default=8,
+                    help="timed steps of each 100M-token host-bank run (0 skips the leg)")
+    ap.add_argument("--host-cache-gb", type=float, default=200.0,
+                    help="device document cache of the host-bank leg's second run, GB")
+    ap.add_argument("--prefetch-window", type=int, default=4,
+                    help="batches routed and prefetched ahead in the cached host-bank run")
+    ap.add_argument("--interleave-steps", type=int, default=3,
+                    help="timed 3-hop steps over the 32 Mi-token bank (0 skips the leg)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -459,6 +492,39 @@ def main():
         q, q_route, k_loc, v_loc, L = batches[i % args.batches]
         bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=q_route, ws=ws[si],
                   outputs=outs[i % args.batches], stream=streams[si], splits=args.splits)
+
+    single = None
+    if args.single_stream_steps > 0:
+        # one stream, every launch bracketed: the decode kernel's own duration
+        # with nothing overlapping it, and the serial route -> top-k ->
+        # attention -> merge chain of a step (this also brings the chip to its
+        # steady clock before the timed region)
+        log("single-stream leg")
+        n1 = args.single_stream_steps
+        def sstep(i):
+            q, q_route, k_loc, v_loc, L = batches[i % args.batches]
+            bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=q_route, ws=ws[0],
+                      outputs=outs[i % args.batches], stream=streams[0], splits=args.splits)
+        for i in range(20):
+            sstep(i)
+        torch.cuda.synchronize()
+        msa.timer_reserve(2 * n1)
+        msa.timer_enable(True, 1)
+        msa.timer_read(msa.MSA_TIMER_ATTENTION)
+        msa.timer_read(msa.MSA_TIMER_ROUTE)
+        t1 = time.perf_counter()
+        for i in range(n1):
+            sstep(i)
+        torch.cuda.synchronize()
+        sdt = time.perf_counter() - t1
+        s_att_ms, s_att_n = msa.timer_read(msa.MSA_TIMER_ATTENTION)
+        s_rt_ms, s_rt_n = msa.timer_read(msa.MSA_TIMER_ROUTE)
+        msa.timer_enable(False)
+        single = {"steps": n1, "ms_per_step": sdt * 1e3 / n1, "queries_per_s": w.B * n1 / sdt,
+                  "decode_avg_launch_us": s_att_ms * 1e3 / max(s_att_n, 1),
+                  "routing_avg_launch_us": s_rt_ms * 1e3 / max(s_rt_n, 1),
+                  "note": "every launch event-timed (the events sit on the stream, so the "
+                          "step time here includes their cost)"}
 
     log("warmup")
     for i in range(args.warmup):
@@ -521,6 +587,14 @@ def main():
         "tokens_attended_per_s": qps * (w.k * 512 + w.L_loc),
         "bank_build_s": build_s,
     }
+    if single is not None:
+        iso = kv_bytes / (single["decode_avg_launch_us"] * 1e-6) / 1e9
+        single.update({"decode_achieved_GBs": iso, "decode_frac": iso / HBM_PEAK_GBS})
+        res["roofline"]["isolated"] = {"achieved": iso, "frac": iso / HBM_PEAK_GBS,
+                                       "avg_launch_us": single["decode_avg_launch_us"],
+                                       "launches": single["steps"],
+                                       "source": "single-stream leg"}
+        res["single_stream"] = single
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(w, r, k_raw, v_raw, raw0)
@@ -577,12 +651,11 @@ def main():
         res["prefill"] = prefill_bench(args.prefill_steps, 3, args.prefill_splits)
     if args.host_bank_steps > 0:
         torch.cuda.empty_cache()
-        res["host_bank"] = host_bank_bench(args.host_bank_steps, 2)
-        if args.host_cache_gb > 0:
-            res["host_bank_cached"] = host_bank_bench(args.host_bank_steps, 2, args.host_cache_gb)
+        res["host_bank"] = host_bank_bench(args.host_bank_steps, 2, args.host_cache_gb,
+                                           args.prefetch_window)
     if args.interleave_steps > 0:
         torch.cuda.empty_cache()
-        res["interleave"] = interleave_bench(args.interleave_steps, 2)
+        res["interleave"] = interleave_bench(args.interleave_steps, 1)
     print(json.dumps(res))
 
 

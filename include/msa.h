@@ -22,9 +22,13 @@
  *     memory on the current device; "host" pointers are ordinary CPU memory.
  *     The library allocates only in msa_bank_create (small per-bank tables;
  *     for a host-resident bank also pinned id buffers for 4096 selections and
- *     two events) and frees them in msa_bank_destroy.  The one exception on
- *     the hot path: msa_step on a host-resident bank regrows those pinned id
- *     buffers once when a call selects more documents than they hold.
+ *     65 events) and frees them in msa_bank_destroy.  The one exception on
+ *     the hot path: msa_step or msa_prefetch on a host-resident bank regrows
+ *     those pinned id buffers once when a call selects more documents than
+ *     they hold.
+ *   - A host-resident K/V store (MSA_KV_HOST) must be pinned host memory
+ *     (hipHostMalloc, or torch's pin_memory) over its whole extent;
+ *     msa_bank_create refuses pageable memory with MSA_EINVAL.
  *   - Every data array (device, or pinned host for a host-resident store)
  *     starts on a 16-byte boundary, as hipMalloc, hipHostMalloc and torch
  *     allocations do; a misaligned array is MSA_EINVAL.
@@ -315,8 +319,10 @@ int msa_build_pooled(const msa_bank* bank, int32_t doc_begin, int32_t doc_end, v
  * resident: a selected document already in a slot is read from there, any
  * other is copied from the host store into the least recently used slot
  * that the same hop does not need (its `staging` is then unused and may be
- * NULL).  Before a slot is overwritten, the previous step's attention on
- * this bank has completed.  Results are identical with and without a cache.
+ * NULL).  A copy into a slot waits, on the copy stream, for the last
+ * attention that read the slot and for its previous fill; an attention
+ * waits for the fills of the slots it reads.  Results are identical with and
+ * without a cache.
  * Errors: MSA_EINVAL for a device-resident bank; MSA_ENOMEM if no slot
  * fits; msa_step fails with MSA_ENOMEM when one hop selects more distinct
  * documents than there are slots.  Resets the cache's contents; not to be
@@ -329,13 +335,41 @@ size_t msa_cache_slot_bytes(const msa_bank* bank);
  * "Komponenty": Memory Interleave).  Prefill: each block of `block` query
  * tokens routes with the mean of its router vectors and shares one top-k set.
  * Host-resident banks: after top-k the ids are read back (the call blocks
- * once per hop on `stream`), each distinct selected document is copied into
- * `staging` -- or, with a device cache attached, found in the cache or
- * copied into a cache slot -- on `copy_stream` (NULL = `stream`), and
- * attention waits for the copies.  `stats` (host, may be NULL) receives copy
- * and cache-hit counts. */
+ * once per hop on `stream`, i.e. until the stream's earlier work is done),
+ * each distinct selected document is copied into `staging` -- or, with a
+ * device cache attached, found in the cache or copied into a cache slot --
+ * on `copy_stream` (NULL = `stream`), and attention waits, on the device,
+ * for the copies it reads (including a cached document's copy that an
+ * earlier call or msa_prefetch left in flight).  The call returns once the
+ * attention is enqueued; `staging` may be reused by the next call on the
+ * same `stream`.  `stats` (host, may be NULL) receives copy and cache-hit
+ * counts. */
 int msa_step(const msa_bank* bank, const msa_step_args* args, void* stream,
              void* copy_stream, msa_step_stats* stats);
+
+/* Asynchronous prefetch into the device cache of a host-resident bank
+ * (intelliparadigm.com, section 5.2: prefetch memory ahead of its use so that
+ * IO overlaps compute, over a window of upcoming requests; "MSA" card,
+ * "Pułapki implementacyjne": pinned memory and asynchronous copies against
+ * the CPU-GPU bandwidth bottleneck).  Routes B router queries exactly as
+ * msa_route does (q_route: device [B][h_r][d_r] float32; exclude as there),
+ * on `stream`, reads the selection back (blocking once on `stream`), and
+ * makes every distinct selected document resident: a document already in
+ * the cache is marked recently used, any other is copied into the least
+ * recently used slot on `copy_stream` (NULL = `stream`).  The copies are
+ * left in flight: a later msa_step that selects these documents finds them
+ * in the cache and its attention waits for them on the device.  Running
+ * route + prefetch for batch i + W while batch i steps keeps the host link
+ * busy without gaps.
+ *   ws: device workspace of at least msa_workspace_bytes(bank, MSA_DECODE,
+ *     B, h_kv, k, 1, 1, 0) bytes (must not be in use by another call).
+ *   stats (host, may be NULL): copies issued and documents already cached.
+ * Errors: MSA_EINVAL without an attached cache or on a device-resident bank;
+ * MSA_ENOMEM when the selection has more distinct documents than the cache
+ * has slots; k and B as in msa_route. */
+int msa_prefetch(const msa_bank* bank, const float* q_route, int32_t B, int32_t k,
+                 const uint32_t* exclude, void* ws, size_t ws_bytes, void* stream,
+                 void* copy_stream, msa_step_stats* stats);
 
 /* Kernel timing for measurement.  While enabled on the calling thread, the
  * library brackets launches of the kernel class `which` with a pair of HIP

@@ -192,6 +192,62 @@ hipError_t host_buffers_reserve(Bank& bk, size_t cap) {
 // per msa_step); a larger step regrows them once
 constexpr size_t kHostIdsInitial = 4096;
 
+// ---- ordering events of a host-resident bank (host_mu held)
+// Record the next ring event on stream s and return its tag (sequence + 1).
+// The entry's previous record is synchronised first, so a tag older than
+// the ring always names completed work.
+hipError_t ring_record(Bank& bk, hipStream_t s, uint64_t* tag) {
+  const uint64_t q = bk.ring_seq;
+  hipEvent_t e = bk.ring[q % Bank::kRing];
+  if (q >= (uint64_t)Bank::kRing) {
+    const hipError_t r = hipEventSynchronize(e);
+    if (r != hipSuccess) return r;
+  }
+  const hipError_t r = hipEventRecord(e, s);
+  if (r != hipSuccess) return r;
+  bk.ring_seq = q + 1;
+  *tag = q + 1;
+  return hipSuccess;
+}
+
+// True while the work a tag names may still be running (its ring entry has
+// not been recorded again since).
+bool ring_live(const Bank& bk, uint64_t tag) {
+  return tag != 0 && bk.ring_seq - (tag - 1) <= (uint64_t)Bank::kRing;
+}
+
+// Make stream s wait, on the device, for the work a tag names.
+hipError_t ring_wait(Bank& bk, hipStream_t s, uint64_t tag) {
+  if (!ring_live(bk, tag)) return hipSuccess;
+  return hipStreamWaitEvent(s, bk.ring[(tag - 1) % Bank::kRing], 0);
+}
+
+// Wait on the host for every recorded ring event.
+hipError_t ring_drain(Bank& bk) {
+  const uint64_t n = std::min<uint64_t>(bk.ring_seq, Bank::kRing);
+  for (uint64_t q = bk.ring_seq - n; q < bk.ring_seq; ++q) {
+    const hipError_t r = hipEventSynchronize(bk.ring[q % Bank::kRing]);
+    if (r != hipSuccess) return r;
+  }
+  return hipSuccess;
+}
+
+// A host-resident store must be pinned host memory from its first to its
+// last byte: copies from pageable memory would run synchronously (and
+// through a bounce buffer).
+bool pinned_host_range(const void* p, size_t bytes) {
+  for (const char* q : {(const char*)p, (const char*)p + (bytes ? bytes - 1 : 0)}) {
+    hipPointerAttribute_t at{};
+    const hipError_t e = hipPointerGetAttributes(&at, q);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();  // leave no error behind for the next call to report
+      return false;
+    }
+    if (at.type != hipMemoryTypeHost) return false;
+  }
+  return true;
+}
+
 }  // namespace msa
 
 using namespace msa;
@@ -424,10 +480,16 @@ int msa_bank_create(const msa_bank_desc* d, msa_bank** out) {
     return st;
   }
   if (d->kv_loc == MSA_KV_HOST) {
+    const size_t store_bytes = (size_t)d->kv_tokens * d->h_kv * kD * dtype_size(d->dtype);
+    if (!pinned_host_range(d->k_store, store_bytes) || !pinned_host_range(d->v_store, store_bytes)) {
+      msa_bank_destroy(reinterpret_cast<msa_bank*>(bk));
+      return fail(MSA_EINVAL, "a host-resident K/V store must be pinned host memory "
+                              "(hipHostMalloc) over its whole kv_tokens extent");
+    }
     hipError_t e = host_buffers_reserve(*bk, kHostIdsInitial);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&bk->copies_done, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&bk->tables_done, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&bk->attn_done, hipEventDisableTiming);
+    for (int i = 0; i < Bank::kRing && e == hipSuccess; ++i)
+      e = hipEventCreateWithFlags(&bk->ring[i], hipEventDisableTiming);
     if (e != hipSuccess) {
       msa_bank_destroy(reinterpret_cast<msa_bank*>(bk));
       return fail(MSA_EHIP, std::string("host-bank buffers: ") + hipGetErrorString(e));
@@ -475,10 +537,10 @@ int msa_bank_destroy(msa_bank* b) {
   if (!b) return MSA_OK;
   Bank* bk = reinterpret_cast<Bank*>(b);
   if (bk->tables_pending) (void)hipEventSynchronize(bk->tables_done);
-  if (bk->copies_done) (void)hipEventDestroy(bk->copies_done);
   if (bk->tables_done) (void)hipEventDestroy(bk->tables_done);
-  if (bk->attn_pending) (void)hipEventSynchronize(bk->attn_done);
-  if (bk->attn_done) (void)hipEventDestroy(bk->attn_done);
+  if (bk->ring[0]) (void)ring_drain(*bk);
+  for (hipEvent_t e : bk->ring)
+    if (e) (void)hipEventDestroy(e);
   if (bk->dev_mem) (void)hipFree(bk->dev_mem);
   if (bk->h_ids) (void)hipHostFree(bk->h_ids);
   if (bk->h_src) (void)hipHostFree(bk->h_src);
@@ -557,14 +619,14 @@ int msa_bank_set_cache(msa_bank* b, void* cache, size_t cache_bytes) {
   if (bk.desc.kv_loc != MSA_KV_HOST) return fail(MSA_EINVAL, "a device cache needs a host-resident bank");
   if (!al16(cache)) return fail(MSA_EINVAL, "the cache must be 16-byte aligned");
   std::lock_guard<std::mutex> lock(bk.host_mu);
-  if (bk.attn_pending) {  // the previous cached step's attention may still read the old cache
-    MSA_CHECK_HIP(hipEventSynchronize(bk.attn_done));
-    bk.attn_pending = false;
-  }
+  // earlier steps' copies and attention may still use the old cache
+  MSA_CHECK_HIP(ring_drain(bk));
   bk.cache = nullptr;
   bk.cache_slots = 0;
   bk.cache_doc.clear();
   bk.cache_epoch.clear();
+  bk.slot_fill.clear();
+  bk.slot_read.clear();
   bk.cache_lru.clear();
   bk.cache_pos.clear();
   bk.cache_slot_of.clear();
@@ -576,6 +638,8 @@ int msa_bank_set_cache(msa_bank* b, void* cache, size_t cache_bytes) {
   bk.cache_slots = n;
   bk.cache_doc.assign(n, -1);
   bk.cache_epoch.assign(n, 0);
+  bk.slot_fill.assign(n, 0);
+  bk.slot_read.assign(n, 0);
   bk.cache_pos.resize(n);
   for (int64_t i = 0; i < n; ++i) bk.cache_pos[i] = bk.cache_lru.insert(bk.cache_lru.end(), (int32_t)i);
   return MSA_OK;
@@ -609,6 +673,149 @@ int msa_build_pooled(const msa_bank* b, int32_t doc0, int32_t doc1, void* stream
   MSA_CHECK_HIP(launch_pool_kv(bk, doc0, doc1, (hipStream_t)stream));
   return MSA_OK;
 }
+
+}  // extern "C"
+
+namespace {
+
+// Where one hop's distinct selected documents of a host-resident bank sit on
+// the device, and what the attention must wait for before reading them.
+struct Resident {
+  char* kbase = nullptr;         // K of compact index j at kbase + off[j] * token bytes
+  char* vbase = nullptr;         // V likewise
+  std::vector<uint64_t> waits;   // ring tags of copies the attention waits for
+  std::vector<int32_t> slots;    // cache slots in use (with a cache)
+};
+
+// Make the distinct documents `docs` resident on the device (host_mu held):
+// with a cache, documents already in a slot stay (hits) and the others are
+// copied from the host store into least recently used slots; without one,
+// every document is copied into `staging`, in order.  Copies go on stream
+// cs.  A copy into a slot first waits, on cs, for the slot's last reader and
+// its previous fill.  slot_off / slot_len receive each compact index's token
+// offset from the bases and its length.
+int make_resident(Bank& bk, const std::vector<int32_t>& docs, void* staging, size_t staging_bytes,
+                  hipStream_t cs, msa_step_stats* stats, int64_t* slot_off, int32_t* slot_len,
+                  Resident* r) {
+  const int32_t n = (int32_t)docs.size();
+  const size_t tok_bytes = (size_t)bk.desc.h_kv * kD * dtype_size(bk.desc.dtype);
+  auto copy_doc = [&](int32_t id, char* kdst, char* vdst) -> hipError_t {
+    const size_t bytes = (size_t)bk.doc_len[id] * tok_bytes;
+    const size_t src_o = (size_t)bk.kv_off[id] * tok_bytes;
+    hipError_t e = hipMemcpyAsync(kdst, (const char*)bk.desc.k_store + src_o, bytes,
+                                  hipMemcpyHostToDevice, cs);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(vdst, (const char*)bk.desc.v_store + src_o, bytes, hipMemcpyHostToDevice, cs);
+    if (stats) {
+      stats->docs_copied += 1;
+      stats->bytes_copied += (int64_t)(2 * bytes);
+    }
+    return e;
+  };
+  std::vector<int32_t> filled;
+  if (bk.cache) {
+    if (n > bk.cache_slots)
+      return fail(MSA_ENOMEM, "one hop selects more distinct documents than the cache has slots");
+    const size_t slot_k = (size_t)bk.max_doc_len * tok_bytes;
+    r->kbase = bk.cache;
+    r->vbase = bk.cache + (size_t)bk.cache_slots * slot_k;
+    const uint64_t ep = ++bk.hop_epoch;
+    auto touch = [&](int32_t slot) {
+      bk.cache_lru.splice(bk.cache_lru.begin(), bk.cache_lru, bk.cache_pos[slot]);
+      bk.cache_epoch[slot] = ep;
+    };
+    r->slots.assign(n, -1);
+    // hits first: they move to the front, so no miss of this hop evicts them;
+    // a hit whose fill may still be in flight is waited for
+    for (int32_t j = 0; j < n; ++j) {
+      auto h = bk.cache_slot_of.find(docs[j]);
+      if (h == bk.cache_slot_of.end()) continue;
+      r->slots[j] = h->second;
+      touch(h->second);
+      if (ring_live(bk, bk.slot_fill[h->second])) r->waits.push_back(bk.slot_fill[h->second]);
+      if (stats) stats->docs_cached += 1;
+    }
+    std::vector<uint64_t> before;  // what cs waits for before overwriting victims
+    std::vector<int32_t> victims;
+    for (int32_t j = 0; j < n; ++j) {
+      if (r->slots[j] >= 0) continue;
+      const int32_t victim = bk.cache_lru.back();
+      if (bk.cache_epoch[victim] == ep) return fail(MSA_ENOMEM, "cache slots exhausted");
+      if (bk.cache_doc[victim] >= 0) bk.cache_slot_of.erase(bk.cache_doc[victim]);
+      bk.cache_doc[victim] = docs[j];
+      bk.cache_slot_of[docs[j]] = victim;
+      touch(victim);
+      r->slots[j] = victim;
+      victims.push_back(j);
+      for (uint64_t t : {bk.slot_read[victim], bk.slot_fill[victim]})
+        if (ring_live(bk, t)) before.push_back(t);
+    }
+    std::sort(before.begin(), before.end());
+    before.erase(std::unique(before.begin(), before.end()), before.end());
+    for (uint64_t t : before) MSA_CHECK_HIP(ring_wait(bk, cs, t));
+    for (int32_t j : victims) {
+      const int32_t v = r->slots[j];
+      MSA_CHECK_HIP(copy_doc(docs[j], r->kbase + (size_t)v * slot_k, r->vbase + (size_t)v * slot_k));
+      filled.push_back(v);
+    }
+    for (int32_t j = 0; j < n; ++j) {
+      slot_off[j] = (int64_t)r->slots[j] * bk.max_doc_len;
+      slot_len[j] = (int32_t)bk.doc_len[docs[j]];
+    }
+  } else {
+    const size_t half = staging_bytes / 2;
+    r->kbase = (char*)staging;
+    r->vbase = r->kbase + half;
+    int64_t tok = 0;
+    for (int32_t j = 0; j < n; ++j) {
+      slot_off[j] = tok;
+      slot_len[j] = (int32_t)bk.doc_len[docs[j]];
+      MSA_CHECK_HIP(copy_doc(docs[j], r->kbase + (size_t)tok * tok_bytes,
+                             r->vbase + (size_t)tok * tok_bytes));
+      tok += bk.doc_len[docs[j]];
+    }
+    if (n > 0) filled.push_back(-1);
+  }
+  if (!filled.empty()) {
+    uint64_t tag = 0;
+    MSA_CHECK_HIP(ring_record(bk, cs, &tag));
+    for (int32_t v : filled)
+      if (v >= 0) bk.slot_fill[v] = tag;
+    r->waits.push_back(tag);
+  }
+  std::sort(r->waits.begin(), r->waits.end());
+  r->waits.erase(std::unique(r->waits.begin(), r->waits.end()), r->waits.end());
+  return MSA_OK;
+}
+
+// Read one hop's selected ids back and reduce them to distinct documents:
+// docs[j] is compact index j's document, slot_ids[i] selection i's compact
+// index (-1 for an empty slot).  Blocks on stream s.
+int read_back_ids(Bank& bk, const int32_t* ids, size_t n_sel, hipStream_t s,
+                  std::vector<int32_t>* docs, int32_t* slot_ids) {
+  MSA_CHECK_HIP(hipMemcpyAsync(bk.h_ids, ids, n_sel * 4, hipMemcpyDeviceToHost, s));
+  MSA_CHECK_HIP(hipStreamSynchronize(s));
+  std::unordered_map<int32_t, int32_t> slot_of;  // document -> compact index
+  const int N = bk.desc.n_docs;
+  for (size_t i = 0; i < n_sel; ++i) {
+    const int32_t id = bk.h_ids[i];
+    if (id < 0 || id >= N) {
+      if (slot_ids) slot_ids[i] = -1;
+      continue;
+    }
+    auto it = slot_of.find(id);
+    if (it == slot_of.end()) {
+      it = slot_of.emplace(id, (int32_t)docs->size()).first;
+      docs->push_back(id);
+    }
+    if (slot_ids) slot_ids[i] = it->second;
+  }
+  return MSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
 
 int msa_route(const msa_bank* b, const float* q_route, int32_t B, int32_t k,
               const uint32_t* exclude, int32_t* ids, float* scores, void* ws, size_t ws_bytes,
@@ -681,10 +888,17 @@ int msa_attend(const msa_bank* b, const msa_attend_args* a, void* stream) {
   return MSA_OK;
 }
 
-int msa_step(const msa_bank* b, const msa_step_args* a, void* stream, void* copy_stream,
-             msa_step_stats* stats) {
+}  // extern "C"
+
+namespace {
+
+// msa_step: route -> top-k -> gather -> attend for every hop
+int step_impl(const msa_bank* b, const msa_step_args* a, void* stream, void* copy_stream,
+              msa_step_stats* stats) {
   if (!b || !a) return fail(MSA_EINVAL, "NULL bank or args");
   Bank& bk = *const_cast<Bank*>(as_bank(b));
+  void* const ws_ptr = a->ws;
+  const size_t ws_bytes = a->ws_bytes;
   const int N = bk.desc.n_docs;
   int st = check_attend_common(bk, a->mode, a->n_q, a->h_q, a->k, a->block, a->L_loc, a->k_loc,
                                a->v_loc);
@@ -700,9 +914,9 @@ int msa_step(const msa_bank* b, const msa_step_args* a, void* stream, void* copy
     stats->docs_cached = 0;
   }
   if (a->n_q == 0) return MSA_OK;
-  if (!a->q || !a->ids || !a->scores || !a->out || !a->ws) return fail(MSA_EINVAL, "NULL pointer");
+  if (!a->q || !a->ids || !a->scores || !a->out || !ws_ptr) return fail(MSA_EINVAL, "NULL pointer");
   if (prefill ? !a->route_tokens : !a->q_route) return fail(MSA_EINVAL, "router input is NULL");
-  if (!all_al16(a->q, a->out, a->ws, a->q_route, a->route_tokens, a->staging, a->w_proj))
+  if (!all_al16(a->q, a->out, ws_ptr, a->q_route, a->route_tokens, a->staging, a->w_proj))
     return fail(MSA_EINVAL, "q, out, ws, router input, w_proj and staging must be 16-byte aligned");
   if (a->q_pos < 0) return fail(MSA_EINVAL, "q_pos < 0");
   const bool pooled = a->memory == MSA_MEMORY_POOLED;
@@ -717,9 +931,7 @@ int msa_step(const msa_bank* b, const msa_step_args* a, void* stream, void* copy
   const int splits =
       resolve_splits(bk, a->mode, a->splits, a->n_q, a->h_q, a->block, k, a->L_loc, pooled);
   const WsLayout L = ws_layout(bk, a->mode, a->n_q, a->h_q, k, a->block, a->hops, splits);
-  if (a->ws_bytes < L.total) return fail(MSA_ENOMEM, "workspace too small for msa_step");
-  const size_t esz = dtype_size(bk.desc.dtype);
-  const size_t tok_bytes = (size_t)bk.desc.h_kv * kD * esz;
+  if (ws_bytes < L.total) return fail(MSA_ENOMEM, "workspace too small for msa_step");
   // The host part of a host-resident bank's step (id readback, copy issue,
   // remap tables) uses the bank's pinned buffers: one step at a time.
   std::unique_lock<std::mutex> host_lock;
@@ -738,7 +950,7 @@ int msa_step(const msa_bank* b, const msa_step_args* a, void* stream, void* copy
         return fail(MSA_ENOMEM, "staging buffer too small");
     }
   }
-  char* w = (char*)a->ws;
+  char* w = (char*)ws_ptr;
   hipStream_t s = (hipStream_t)stream;
   hipStream_t cs = copy_stream ? (hipStream_t)copy_stream : s;
   const int W = (N + 31) / 32;
@@ -768,109 +980,21 @@ int msa_step(const msa_bank* b, const msa_step_args* a, void* stream, void* copy
                              : AttnSources{bk.desc.k_store, bk.desc.v_store, bk.d_kv_off,
                                            bk.d_doc_len, N};
     const int32_t* att_ids = ids;
+    Resident res;
     if (host) {
       // top-k -> K/V fetch is sequential: read the ids back, then make each
       // distinct selected document resident on the device (a cache hit, or
       // a copy into a cache slot or into staging) and remap the ids to a
       // compact table of those documents
-      MSA_CHECK_HIP(hipMemcpyAsync(bk.h_ids, ids, (size_t)n_groups * k * 4,
-                                   hipMemcpyDeviceToHost, s));
-      MSA_CHECK_HIP(hipStreamSynchronize(s));
-      std::unordered_map<int32_t, int32_t> slot_of;  // document -> compact index
-      std::vector<int32_t> docs;                      // compact index -> document
+      std::vector<int32_t> docs;
       int32_t* slot_ids = bk.h_src;                        // [n_groups*k]
       int32_t* slot_len = bk.h_src + (size_t)n_groups * k;  // [n_slots]
       int64_t* slot_off = bk.h_src_off;                    // [n_slots]
-      for (size_t i = 0; i < (size_t)n_groups * k; ++i) {
-        const int32_t id = bk.h_ids[i];
-        if (id < 0 || id >= N) {
-          slot_ids[i] = -1;
-          continue;
-        }
-        auto it = slot_of.find(id);
-        if (it == slot_of.end()) {
-          it = slot_of.emplace(id, (int32_t)docs.size()).first;
-          docs.push_back(id);
-        }
-        slot_ids[i] = it->second;
-      }
+      st = read_back_ids(bk, ids, (size_t)n_groups * k, s, &docs, slot_ids);
+      if (st) return st;
       const int32_t n_slots = (int32_t)docs.size();
-      auto copy_doc = [&](int32_t id, char* kdst, char* vdst) -> hipError_t {
-        const size_t bytes = (size_t)bk.doc_len[id] * tok_bytes;
-        const size_t src_o = (size_t)bk.kv_off[id] * tok_bytes;
-        hipError_t e = hipMemcpyAsync(kdst, (const char*)bk.desc.k_store + src_o, bytes,
-                                      hipMemcpyHostToDevice, cs);
-        if (e == hipSuccess)
-          e = hipMemcpyAsync(vdst, (const char*)bk.desc.v_store + src_o, bytes,
-                             hipMemcpyHostToDevice, cs);
-        if (stats) {
-          stats->docs_copied += 1;
-          stats->bytes_copied += (int64_t)(2 * bytes);
-        }
-        return e;
-      };
-      char* kbase;
-      char* vbase;
-      if (bk.cache) {
-        if (n_slots > bk.cache_slots)
-          return fail(MSA_ENOMEM, "one hop selects more distinct documents than the cache has slots");
-        const size_t slot_k = (size_t)bk.max_doc_len * tok_bytes;
-        kbase = bk.cache;
-        vbase = bk.cache + (size_t)bk.cache_slots * slot_k;
-        const uint64_t ep = ++bk.hop_epoch;
-        auto touch = [&](int32_t slot) {
-          bk.cache_lru.splice(bk.cache_lru.begin(), bk.cache_lru, bk.cache_pos[slot]);
-          bk.cache_epoch[slot] = ep;
-        };
-        std::vector<int32_t> where(n_slots, -1);
-        bool evict = false;
-        // hits first: they move to the front, so no miss of this hop evicts them
-        for (int32_t j = 0; j < n_slots; ++j) {
-          auto h = bk.cache_slot_of.find(docs[j]);
-          if (h != bk.cache_slot_of.end()) {
-            where[j] = h->second;
-            touch(h->second);
-            if (stats) stats->docs_cached += 1;
-          } else {
-            evict = true;
-          }
-        }
-        if (evict && bk.attn_pending) {  // no earlier attention may still read a victim
-          MSA_CHECK_HIP(hipEventSynchronize(bk.attn_done));
-          bk.attn_pending = false;
-        }
-        for (int32_t j = 0; j < n_slots; ++j) {
-          if (where[j] >= 0) continue;
-          const int32_t victim = bk.cache_lru.back();
-          if (bk.cache_epoch[victim] == ep) return fail(MSA_ENOMEM, "cache slots exhausted");
-          if (bk.cache_doc[victim] >= 0) bk.cache_slot_of.erase(bk.cache_doc[victim]);
-          bk.cache_doc[victim] = docs[j];
-          bk.cache_slot_of[docs[j]] = victim;
-          touch(victim);
-          where[j] = victim;
-          MSA_CHECK_HIP(copy_doc(docs[j], kbase + (size_t)victim * slot_k,
-                                 vbase + (size_t)victim * slot_k));
-        }
-        for (int32_t j = 0; j < n_slots; ++j) {
-          slot_off[j] = (int64_t)where[j] * bk.max_doc_len;
-          slot_len[j] = (int32_t)bk.doc_len[docs[j]];
-        }
-      } else {
-        if (!a->staging) return fail(MSA_EINVAL, "host-resident bank needs a staging buffer");
-        if (a->staging_bytes < msa_staging_bytes(b, n_groups, k))
-          return fail(MSA_ENOMEM, "staging buffer too small");
-        const size_t half = a->staging_bytes / 2;
-        kbase = (char*)a->staging;
-        vbase = kbase + half;
-        int64_t tok = 0;
-        for (int32_t j = 0; j < n_slots; ++j) {
-          slot_off[j] = tok;
-          slot_len[j] = (int32_t)bk.doc_len[docs[j]];
-          MSA_CHECK_HIP(copy_doc(docs[j], kbase + (size_t)tok * tok_bytes,
-                                 vbase + (size_t)tok * tok_bytes));
-          tok += bk.doc_len[docs[j]];
-        }
-      }
+      st = make_resident(bk, docs, a->staging, a->staging_bytes, cs, stats, slot_off, slot_len, &res);
+      if (st) return st;
       int32_t* d_ids = (int32_t*)(w + L.srcids);
       int64_t* d_off = (int64_t*)(w + L.srcoff);
       int32_t* d_len = (int32_t*)(w + L.srclen);
@@ -882,11 +1006,8 @@ int msa_step(const msa_bank* b, const msa_step_args* a, void* stream, void* copy
       }
       MSA_CHECK_HIP(hipEventRecord(bk.tables_done, s));
       bk.tables_pending = true;
-      if (cs != s) {
-        MSA_CHECK_HIP(hipEventRecord(bk.copies_done, cs));
-        MSA_CHECK_HIP(hipStreamWaitEvent(s, bk.copies_done, 0));
-      }
-      src = AttnSources{kbase, vbase, d_off, d_len, n_slots};
+      for (uint64_t t : res.waits) MSA_CHECK_HIP(ring_wait(bk, s, t));
+      src = AttnSources{res.kbase, res.vbase, d_off, d_len, n_slots};
       att_ids = d_ids;
     }
     if (prefill)
@@ -897,17 +1018,70 @@ int msa_step(const msa_bank* b, const msa_step_args* a, void* stream, void* copy
       MSA_CHECK_HIP(launch_decode(bk, a->q, a->q_pos, a->n_q, a->h_q, att_ids, k, src,
                                   a->k_loc, a->v_loc, a->L_loc, splits, (float*)(w + L.part),
                                   out, s));
-    if (host && bk.cache) {
-      MSA_CHECK_HIP(hipEventRecord(bk.attn_done, s));
-      bk.attn_pending = true;
+    if (host && bk.cache) {  // no later copy overwrites these slots before this attention ends
+      uint64_t tag = 0;
+      MSA_CHECK_HIP(ring_record(bk, s, &tag));
+      for (int32_t v : res.slots) bk.slot_read[v] = tag;
     }
     if (hop + 1 < a->hops) {
       MSA_CHECK_HIP(launch_project(out, a->w_proj, a->n_q, a->h_q * kD, kD, q_route, s));
       qr = q_route;
     }
   }
-  if (host) MSA_CHECK_HIP(hipStreamSynchronize(s));  // pinned remap tables are reused next call
   return MSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int msa_step(const msa_bank* b, const msa_step_args* a, void* stream, void* copy_stream,
+             msa_step_stats* stats) {
+  return step_impl(b, a, stream, copy_stream, stats);
+}
+
+int msa_prefetch(const msa_bank* b, const float* q_route, int32_t B, int32_t k,
+                 const uint32_t* exclude, void* ws, size_t ws_bytes, void* stream,
+                 void* copy_stream, msa_step_stats* stats) {
+  if (!b) return fail(MSA_EINVAL, "NULL bank");
+  Bank& bk = *const_cast<Bank*>(as_bank(b));
+  if (bk.desc.kv_loc != MSA_KV_HOST || !bk.cache)
+    return fail(MSA_EINVAL, "prefetch needs a host-resident bank with a device cache attached");
+  if (B < 0) return fail(MSA_EINVAL, "B < 0");
+  if (k < 1 || k > bk.desc.n_docs) return fail(MSA_EINVAL, "k must be in [1, n_docs]");
+  if (k > kMaxK) return fail(MSA_EUNSUPPORTED, "k must be <= 64");
+  if (stats) {
+    stats->docs_copied = 0;
+    stats->bytes_copied = 0;
+    stats->docs_cached = 0;
+  }
+  if (B == 0) return MSA_OK;
+  if (!q_route || !ws) return fail(MSA_EINVAL, "NULL pointer");
+  if (!all_al16(q_route, ws)) return fail(MSA_EINVAL, "q_route and ws must be 16-byte aligned");
+  const WsLayout L = ws_layout(bk, MSA_DECODE, B, bk.desc.h_kv, k, 1, 1, 4);
+  if (ws_bytes < L.total) return fail(MSA_ENOMEM, "workspace too small for msa_prefetch");
+  char* w = (char*)ws;
+  hipStream_t s = (hipStream_t)stream;
+  hipStream_t cs = copy_stream ? (hipStream_t)copy_stream : s;
+  // the selection lands in the workspace's remap-table area
+  int32_t* ids = (int32_t*)(w + L.srcids);
+  float* scores = (float*)(w + L.srcoff);
+  MSA_CHECK_HIP(launch_route_scan(bk, q_route, B, (float*)(w + L.piecemax), s));
+  MSA_CHECK_HIP(launch_topk(bk, (const float*)(w + L.piecemax), B, k, exclude, nullptr, ids,
+                            scores, (uint64_t*)(w + L.keys), s));
+  std::lock_guard<std::mutex> lock(bk.host_mu);
+  if (bk.tables_pending && (size_t)B * k > bk.h_ids_cap) {  // regrowing frees the table buffers
+    MSA_CHECK_HIP(hipEventSynchronize(bk.tables_done));
+    bk.tables_pending = false;
+  }
+  if (host_buffers_reserve(bk, (size_t)B * k) != hipSuccess) return fail(MSA_ENOMEM, "pinned id buffers");
+  std::vector<int32_t> docs;
+  int st = read_back_ids(bk, ids, (size_t)B * k, s, &docs, nullptr);
+  if (st) return st;
+  std::vector<int64_t> off(docs.size());
+  std::vector<int32_t> len(docs.size());
+  Resident res;
+  return make_resident(bk, docs, nullptr, 0, cs, stats, off.data(), len.data(), &res);
 }
 
 }  // extern "C"

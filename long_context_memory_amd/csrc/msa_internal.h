@@ -49,14 +49,20 @@ struct Bank {
   void* pool_v = nullptr;            // per document [h_kv][ceil(P/64)][d][64], zero-padded
   // host-resident banks: pinned buffers for reading back selected ids and
   // staging the remap tables, and the events that order the copies.  The
-  // host part of msa_step holds host_mu while it uses them.
+  // host part of msa_step / msa_prefetch holds host_mu while it uses them.
   int32_t* h_ids = nullptr;
   size_t h_ids_cap = 0;
   int32_t* h_src = nullptr;  // pinned [2 * cap] remap table staging
   int64_t* h_src_off = nullptr;
-  hipEvent_t copies_done = nullptr;  // document copies on the copy stream
   hipEvent_t tables_done = nullptr;  // remap tables read out of h_src / h_src_off
   bool tables_pending = false;
+  // Ordering events: a ring of kRing events, recorded in sequence.  An
+  // entry is synchronised before it is recorded again, so work tagged with a
+  // sequence number older than the ring has completed.  Tags are stored as
+  // sequence + 1 (0 = nothing to wait for).
+  static constexpr int kRing = 64;
+  hipEvent_t ring[kRing] = {};
+  uint64_t ring_seq = 0;  // sequence number of the next record
   // device document cache of a host-resident bank (msa_bank_set_cache):
   // slot s holds one document's K at cache + s * slot K bytes and its V in
   // the second half; an LRU list of slots, most recently used first
@@ -64,12 +70,12 @@ struct Bank {
   int64_t cache_slots = 0;
   std::vector<int32_t> cache_doc;     // [slots] document in the slot, or -1
   std::vector<uint64_t> cache_epoch;  // [slots] last hop that used the slot
+  std::vector<uint64_t> slot_fill;    // [slots] tag of the copy that filled the slot
+  std::vector<uint64_t> slot_read;    // [slots] tag of the last attention that read it
   std::list<int32_t> cache_lru;
   std::vector<std::list<int32_t>::iterator> cache_pos;
   std::unordered_map<int32_t, int32_t> cache_slot_of;  // document -> slot
   uint64_t hop_epoch = 0;
-  hipEvent_t attn_done = nullptr;  // the last cached step's attention
-  bool attn_pending = false;
   std::mutex host_mu;
 };
 

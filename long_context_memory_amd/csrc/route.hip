@@ -464,6 +464,113 @@ __global__ __launch_bounds__(kTopkGroup) void topk_level_kernel(TopkLevel a) {
   }
 }
 
+// Single-launch top-k for banks of up to kFusedDocs documents: one workgroup
+// of 1024 threads per query, two documents per thread.  A threshold select:
+// the valid scores' range [lo, hi] is cut into 256 equal bins, an LDS
+// histogram finds the bin holding the k-th best score, and only the keys in
+// that bin or above survive (bins are monotone in the score, so every key
+// below lies under at least k survivors).  The survivors -- about k, or
+// all of them in a degenerate range -- are ranked exactly by their 64-bit
+// keys and the k best written in rank order.  The keys are those of the
+// level kernel, so both select the same documents in the same order.
+constexpr int kFusedThreads = 1024;
+constexpr int kFusedWaves = kFusedThreads / 64;
+constexpr int kFusedDocs = 2 * kFusedThreads;
+constexpr int kBins = 256;
+
+__device__ __forceinline__ int score_bin(float s, float lo, float scale) {
+  return min(kBins - 1, max(0, (int)((s - lo) * scale)));
+}
+
+__global__ __launch_bounds__(kFusedThreads) void topk_fused_kernel(TopkLevel a) {
+  __shared__ __attribute__((aligned(16))) uint64_t s_surv[kFusedDocs];
+  __shared__ int s_hist[kBins];
+  __shared__ float s_lo[kFusedWaves], s_hi[kFusedWaves];
+  __shared__ int s_cnt[kFusedWaves];
+  __shared__ int s_cut, s_n;
+  const int b = blockIdx.x, t = threadIdx.x;
+  const int wave = t >> 6, lane = t & 63;
+  const int k = a.k;
+  const float* pm = a.piecemax + (size_t)b * a.h_r * a.P;
+  const uint32_t* excl = a.exclude ? a.exclude + (size_t)b * a.W : nullptr;
+  const int n0 = t, n1 = t + kFusedThreads;
+  const uint64_t k0 = n0 < a.N ? doc_key(pm, a.h_r, a.P, a.doc_piece0, excl, n0) : 0;
+  const uint64_t k1 = n1 < a.N ? doc_key(pm, a.h_r, a.P, a.doc_piece0, excl, n1) : 0;
+  const float s0 = float_from_order_key((uint32_t)(k0 >> 32));
+  const float s1 = float_from_order_key((uint32_t)(k1 >> 32));
+  // the valid scores' range and count, per wave
+  float lo = INFINITY, hi = -INFINITY;
+  if (k0) lo = fminf(lo, s0), hi = fmaxf(hi, s0);
+  if (k1) lo = fminf(lo, s1), hi = fmaxf(hi, s1);
+  lo = -wave_max(-lo);
+  hi = wave_max(hi);
+  const int cnt = __builtin_popcountll(__ballot(k0 != 0)) + __builtin_popcountll(__ballot(k1 != 0));
+  if (lane == 0) {
+    s_lo[wave] = lo;
+    s_hi[wave] = hi;
+    s_cnt[wave] = cnt;
+  }
+  if (t < kBins) s_hist[t] = 0;
+  if (t == 0) s_n = 0;
+  if (t < k) {
+    a.ids[(size_t)b * k + t] = -1;
+    a.scores[(size_t)b * k + t] = -INFINITY;
+  }
+  __syncthreads();
+  int valid = 0;
+  lo = INFINITY;
+  hi = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kFusedWaves; ++w) {
+    lo = fminf(lo, s_lo[w]);
+    hi = fmaxf(hi, s_hi[w]);
+    valid += s_cnt[w];
+  }
+  if (valid == 0) return;
+  const float scale = hi > lo ? (float)kBins / (hi - lo) : 0.f;
+  if (k0) atomicAdd(&s_hist[score_bin(s0, lo, scale)], 1);
+  if (k1) atomicAdd(&s_hist[score_bin(s1, lo, scale)], 1);
+  __syncthreads();
+  // the bin holding the k-th best score: wave 0, four bins per lane counted
+  // from the top
+  if (wave == 0) {
+    const int top = kBins - 1 - 4 * lane;
+    const int c = s_hist[top] + s_hist[top - 1] + s_hist[top - 2] + s_hist[top - 3];
+    int incl = c;  // inclusive prefix over lanes (bins from the top down)
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += u;
+    }
+    const int need = min(k, valid);
+    const uint64_t reach = __ballot(incl >= need);  // lanes whose bins reach k
+    if (lane == __builtin_ctzll(reach)) {
+      int acc = incl - c, bin = top;
+      for (;; --bin) {
+        acc += s_hist[bin];
+        if (acc >= need) break;
+      }
+      s_cut = bin;
+    }
+  }
+  __syncthreads();
+  const int cut = s_cut;
+  if (k0 && score_bin(s0, lo, scale) >= cut) s_surv[atomicAdd(&s_n, 1)] = k0;
+  if (k1 && score_bin(s1, lo, scale) >= cut) s_surv[atomicAdd(&s_n, 1)] = k1;
+  __syncthreads();
+  const int S = s_n;
+  for (int i = t; i < S; i += kFusedThreads) {
+    const uint64_t key = s_surv[i];
+    int rank = 0;
+    for (int j = 0; j < S; ++j) rank += s_surv[j] > key;
+    if (rank >= k) continue;
+    const int n = (int)(~(uint32_t)(key & 0xffffffffu));
+    a.ids[(size_t)b * k + rank] = n;
+    a.scores[(size_t)b * k + rank] = float_from_order_key((uint32_t)(key >> 32));
+    if (a.exclude_out) atomicOr(&a.exclude_out[(size_t)b * a.W + (n >> 5)], 1u << (n & 31));
+  }
+}
+
 // ---------------------------------------------------------------- prefill routing
 // block-mean router query per (block, head): mean of the block's rows
 template <typename T>
@@ -567,6 +674,11 @@ hipError_t launch_topk(const Bank& bk, const float* piecemax, int B, int k,
   a.ids = ids;
   a.scores = scores;
   a.exclude_out = exclude_out;
+  if (N <= kFusedDocs && k <= kMaxK) {
+    a.final_level = 1;
+    hipLaunchKernelGGL(topk_fused_kernel, dim3((unsigned)B), dim3(kFusedThreads), 0, s, a);
+    return hipGetLastError();
+  }
   const size_t half = topk_scratch_keys(N, k) / 2;
   uint64_t* bufs[2] = {cand, cand + (size_t)B * half};
   int M = N, lvl = 0;

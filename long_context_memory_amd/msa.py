@@ -27,7 +27,7 @@ EXPORTS = [
     "msa_workspace_bytes", "msa_staging_bytes", "msa_route", "msa_attend", "msa_step",
     "msa_timer_enable", "msa_timer_read", "msa_timer_reserve", "msa_bank_set_cache", "msa_cache_slot_bytes",
     "msa_bank_append", "msa_pooled_sizes", "msa_bank_set_pooled", "msa_build_pooled",
-    "msa_stream_read",
+    "msa_stream_read", "msa_prefetch",
 ]
 MSA_STREAM_READ_BLOCKS = 4096
 MSA_TIMER_ATTENTION, MSA_TIMER_ROUTE = 0, 1
@@ -109,6 +109,8 @@ def _load():
     lib.msa_timer_enable.argtypes = [C.c_int]
     lib.msa_timer_read.argtypes = [C.c_int, C.POINTER(C.c_double), C.POINTER(i64)]
     lib.msa_timer_reserve.argtypes = [i64]
+    lib.msa_prefetch.argtypes = [vp, vp, i32, i32, vp, vp, C.c_size_t, vp, vp, C.POINTER(StepStats)]
+    lib.msa_prefetch.restype = C.c_int
     lib.msa_stream_read.argtypes = [vp, i64, vp, vp]
     lib.msa_stream_read.restype = C.c_int
     for f in (lib.msa_timer_enable, lib.msa_timer_read, lib.msa_timer_reserve):
@@ -231,11 +233,29 @@ class Bank:
         self.C = T // 256
         self.chunk_cap = int(chunk_cap) if chunk_cap else self.C
         self.kv_tokens = int(kv_tokens) if kv_tokens is not None else T
+        n = self.kv_tokens * self.h_kv * 128
+        # caller-supplied arrays: the library writes and reads them through
+        # bare pointers, so their extent, type and placement are checked here
+        if kr is not None:
+            _expect(kr, (self.h_r, self.chunk_cap, 128), self.dtype, "kr", self.device)
+        if inv_norm is not None:
+            _expect(inv_norm, (self.h_r, self.chunk_cap), torch.float32, "inv_norm", self.device)
+        if (k_store is None) != (v_store is None):
+            raise ValueError("k_store and v_store go together")
+        if k_store is not None:
+            for t, name in ((k_store, "k_store"), (v_store, "v_store")):
+                if t.dtype != self.dtype:
+                    raise ValueError(f"{name}: dtype {t.dtype}, expected {self.dtype}")
+                _expect_bytes(t, n * t.element_size(), name)
+                if self.kv_host:
+                    if t.device.type != "cpu" or not t.is_pinned():
+                        raise ValueError(f"{name}: a host-resident store must be pinned host memory")
+                else:
+                    _expect_bytes(t, 0, name, self.device)
         self.kr = kr if kr is not None else torch.empty(
             (self.h_r, self.chunk_cap, 128), dtype=self.dtype, device=self.device)
         self.inv_norm = inv_norm if inv_norm is not None else torch.empty(
             (self.h_r, self.chunk_cap), dtype=torch.float32, device=self.device)
-        n = self.kv_tokens * self.h_kv * 128
         if k_store is None:
             if self.kv_host:
                 k_store = torch.empty(n, dtype=self.dtype, pin_memory=True)
@@ -363,6 +383,25 @@ class Bank:
         nbytes = 0 if cache is None else cache.numel() * cache.element_size()
         _check(lib.msa_bank_set_cache(self.handle, _ptr(cache), nbytes), "msa_bank_set_cache")
         self.cache = cache
+
+    def prefetch(self, q_route, k: int, exclude=None, ws=None, stream=None, copy_stream=None):
+        """Route q_route [B, h_r, 128] and start copying every selected
+        document not yet in the attached device cache (copies left in
+        flight on copy_stream).  Returns the copy/hit counts (StepStats)."""
+        B = int(q_route.shape[0])
+        _expect(q_route, (B, self.h_r, 128), torch.float32, "q_route", self.device)
+        if exclude is not None:
+            _expect(exclude, (B, (self.n_docs + 31) // 32), torch.int32, "exclude", self.device)
+        need = self.workspace_bytes(MSA_DECODE, B, self.h_kv, k, 1, 1, 0)
+        if ws is None:
+            ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
+        _expect_bytes(ws, need, "ws", self.device)
+        st = StepStats()
+        cs = None if copy_stream is None else _stream(copy_stream)
+        _check(lib.msa_prefetch(self.handle, _ptr(q_route), B, int(k), _ptr(exclude), _ptr(ws),
+                                ws.numel() * ws.element_size(), _stream(stream), cs, C.byref(st)),
+               "msa_prefetch")
+        return st
 
     def staging(self, n_groups, k):
         n = int(lib.msa_staging_bytes(self.handle, n_groups, k))

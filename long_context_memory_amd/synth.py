@@ -47,6 +47,7 @@ class Workload:
     mode: str = "decode"            # "decode" | "prefill" | "interleave"
     plant: Optional[str] = None     # "pooled_key" | "direction" | None
     plant_strength: float = 0.1
+    plant_batches: int = 1          # "direction": query batches with planted targets
     block: int = 64                 # prefill routing block
     hops: int = 1
     exclude_selected: bool = False
@@ -110,7 +111,7 @@ def workload(name: str) -> Workload:
                         pos0=1024, plant="pooled_key", seed=1001)
     if name == "decode_1m":
         return Workload("decode_1m", "bf16", [512] * 2048, h_r=8, h_kv=8, h_q=32, k=16, B=16,
-                        L_loc=4096, plant="direction", seed=1002)
+                        L_loc=4096, plant="direction", plant_batches=4, seed=1002)
     if name == "prefill_8m":
         return Workload("prefill_8m", "bf16", [2048] * 4096, h_r=8, h_kv=8, h_q=32, k=16, B=2048,
                         L_loc=2048, mode="prefill", block=64, seed=1003)
@@ -228,13 +229,16 @@ def host_kv_raw(w: Workload, device="cpu", t0: int = 0, t1: Optional[int] = None
             token_rows(w, "host_v", (w.h_kv, w.d), t0, t1, device, total=total))
 
 
-def planted_targets(w: Workload):
-    """For "direction" planting: query b's k target documents (disjoint across
-    the batch) and, for each, the chunk inside it that carries the planted
+def planted_targets(w: Workload, batch: int = 0):
+    """For "direction" planting: query b's k target documents in query batch
+    `batch` (< w.plant_batches; disjoint across every planted batch's
+    queries) and, for each, the chunk inside it that carries the planted
     direction.  Returns (targets [B, k], chunk_in_doc [B, k])."""
-    perm = permutation(w.n_docs, w.seed, "targets")[: w.B * w.k].reshape(w.B, w.k)
+    n = w.B * w.k
+    perm = permutation(w.n_docs, w.seed, "targets")[batch * n:(batch + 1) * n].reshape(w.B, w.k)
     nch = np.asarray(w.doc_len)[perm] // CHUNK
-    pick = integers(w.B * w.k, 1 << 30, w.seed, "target_chunk").reshape(w.B, w.k) % nch
+    name = "target_chunk" if batch == 0 else f"target_chunk/{batch}"
+    pick = integers(n, 1 << 30, w.seed, name).reshape(w.B, w.k) % nch
     return perm, pick
 
 
@@ -246,22 +250,26 @@ def route_vectors(w: Workload, device="cpu", t0: int = 0, t1: Optional[int] = No
     t1 = w.T if t1 is None else t1
     r = token_rows(w, "route", (w.h_r, w.d_r), t0, t1, device, torch.float32)
     if w.plant == "direction":
-        tgt, pick = planted_targets(w)
-        u = normal((w.B, w.h_r, w.d_r), w.seed, "route_query", device)
+        if w.plant_batches * w.B * w.k > w.n_docs:
+            raise ValueError("planted targets must be disjoint: too few documents")
         off = doc_token_offsets(w)
-        for b in range(w.B):
-            for j in range(w.k):
-                s = int(off[tgt[b, j]] + pick[b, j] * CHUNK)
-                lo, hi = max(s, t0), min(s + CHUNK, t1)
-                if lo < hi:
-                    r[lo - t0:hi - t0] += w.plant_strength * u[b]
+        for i in range(w.plant_batches):
+            tgt, pick = planted_targets(w, i)
+            u = route_queries(w, device, batch=i)
+            for b in range(w.B):
+                for j in range(w.k):
+                    s = int(off[tgt[b, j]] + pick[b, j] * CHUNK)
+                    lo, hi = max(s, t0), min(s + CHUNK, t1)
+                    if lo < hi:
+                        r[lo - t0:hi - t0] += w.plant_strength * u[b]
     return r.to(w.torch_dtype)
 
 
 def route_queries(w: Workload, device="cpu", batch: int = 0):
-    """Decode router queries [B, h_r, d_r], float32.  "direction": the planted
-    directions themselves (batch 0) or fresh N(0,1) draws for other batches;
-    unplanted: N(0, 1).  ("pooled_key" planting needs the pooled key of the
+    """Decode router queries [B, h_r, d_r], float32, N(0, 1).  With
+    "direction" planting, a batch below w.plant_batches is the planted
+    directions themselves (its targets' chunks carry them); other batches
+    are fresh draws.  ("pooled_key" planting needs the pooled key of the
     target chunk, which the caller supplies to ``pooled_key_query``.)"""
     name = "route_query" if batch == 0 else f"route_query/{batch}"
     return normal((w.B, w.h_r, w.d_r), w.seed, name, device)

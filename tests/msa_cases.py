@@ -41,10 +41,15 @@ def pool_oracle(w, r, slice_docs=256):
 
 def check_topk(ids_gpu, scores_gpu, oracle_scores, k, tie=TOPK_TIE, score_tol=SCORE_TOL):
     """Top-k acceptance: ids equal the oracle's (order may differ only between
-    documents whose oracle scores are within `tie`), except where the oracle's
-    k-th and (k+1)-th scores are within `tie`: then every returned document
-    must score >= s_k - tie and every document above s_k + tie must be
-    returned.  Returned scores match the oracle's within `score_tol`.
+    documents whose oracle scores are within `tie` but not equal), except
+    where the oracle's k-th and (k+1)-th scores are within `tie` but not
+    equal: then every returned document must score >= s_k - tie and every
+    document above s_k + tie must be returned.  Exact ties follow the lower-id
+    rule everywhere: when the k-th and (k+1)-th oracle scores are equal the
+    ids and their order must be the oracle's exactly, no document may be
+    passed over for a higher id of exactly the same oracle score, and
+    returned documents of equal oracle score come in increasing id order.
+    Returned scores match the oracle's within `score_tol`.
     Returns the number of rows that fell in the near-tie case."""
     ids_gpu = np.asarray(ids_gpu)
     scores_gpu = np.asarray(scores_gpu, dtype=np.float64)
@@ -63,13 +68,25 @@ def check_topk(ids_gpu, scores_gpu, oracle_scores, k, tie=TOPK_TIE, score_tol=SC
         for r in range(k - 1):
             assert (scores_gpu[b, r] > scores_gpu[b, r + 1]) or (
                 scores_gpu[b, r] == scores_gpu[b, r + 1] and g[r] < g[r + 1]), f"row {b}: order"
+        # exact ties, anywhere: a returned document never outranks (or
+        # displaces) a lower id of exactly the same oracle score
+        for r in range(k):
+            same = np.nonzero(oracle_scores[b] == sg[r])[0]
+            lower = same[same < g[r]]
+            assert set(lower.tolist()) <= set(g[:r].tolist()), \
+                f"row {b}: id {g[r]} taken before a lower id of equal score {lower}"
         s_k = o_vals[k - 1]
         s_k1 = o_vals[k] if N > k else -np.inf
-        if s_k - s_k1 >= tie:
+        # the cut inside an exact tie (identical documents) with no other
+        # score near it: the lower-id rule fixes the set, as a clear gap does
+        vals = oracle_scores[b]
+        exact_cut = s_k == s_k1 and not np.any((np.abs(vals - s_k) < tie) & (vals != s_k))
+        if exact_cut or s_k - s_k1 >= tie:
             assert set(g.tolist()) == set(o_ids[:k].tolist()), f"row {b}: ids {g} vs {o_ids[:k]}"
             for r in range(k - 1):  # order differs from the oracle's only inside a near-tie
                 if g[r] != o_ids[r]:
-                    assert abs(sg[r] - oracle_scores[b, o_ids[r]]) < tie, f"row {b}: rank {r}"
+                    s_o = oracle_scores[b, o_ids[r]]
+                    assert abs(sg[r] - s_o) < tie and sg[r] != s_o, f"row {b}: rank {r}"
         else:
             near += 1
             assert np.all(sg >= s_k - tie), f"row {b}: below the near-tie window"
@@ -198,3 +215,33 @@ def oracle_prefill_rows(w, q, lk, lv, doc_kv, sel, blk, queries):
         outs.append(O.gqa_attention(qr, K, V, mask)[0])
     return np.stack(outs)
 
+
+
+def check_decode_step(w, ids, scores, out, q, q_route, lk, lv, kr_o, inv_o, doc_kv, what=""):
+    """A GPU decode step (ids, scores [B, k]; out [B, h_q, d]) against the
+    oracle for the same inputs: top-k acceptance on the oracle's document
+    scores, then attention over the oracle's selection (the GPU's where it is
+    a valid alternative inside a near-tie).  doc_kv(n) gives the oracle's
+    stored (K_rot, V) of document n.  Returns (max abs, rel RMS) error."""
+    ids, scores = np.asarray(ids), np.asarray(scores)
+    so = O.cosine_doc_scores(np64(q_route), kr_o, inv_o, w.doc_len)
+    check_topk(ids, scores, so, w.k)
+    o_ids, _ = O.select_topk(so, w.k)
+    qn, lkn, lvn = np64(q), np64(lk), np64(lv)
+    refs = []
+    for b in range(ids.shape[0]):
+        sel = o_ids[b] if set(o_ids[b].tolist()) == set(ids[b].tolist()) else ids[b]
+        kv = {int(n): doc_kv(int(n)) for n in sel}
+        refs.append(oracle_attend_decode(w, qn[b], w.q_pos, sel, kv, lkn[b], lvn[b], w.P0))
+    return check_out(np.asarray(out), np.stack(refs), w.dtype, what)
+
+
+def memo(fn):
+    """fn(n) cached per argument (oracle document K/V are reused across steps)."""
+    cache = {}
+
+    def get(n):
+        if n not in cache:
+            cache[n] = fn(n)
+        return cache[n]
+    return get

@@ -90,3 +90,27 @@ def test_buffers_of_too_few_bytes_are_refused():
     with pytest.raises(ValueError, match="need"):
         msa._expect_bytes(torch.zeros(10, dtype=torch.uint8), 11, "ws")
     msa._expect_bytes(torch.zeros(3, dtype=torch.float32), 12, "ws")
+
+
+def test_bank_refuses_caller_arrays_of_the_wrong_extent_type_or_place():
+    # every check runs before the library is called (CPU tensors never reach it)
+    kw = dict(h_r=2, h_kv=8, dtype="bf16", device="cpu")
+    docs = [512] * 4  # 8 chunks, 2048 tokens
+    with pytest.raises(ValueError, match="kr"):
+        msa.Bank(docs, kr=torch.zeros((2, 7, 128), dtype=torch.bfloat16), **kw)
+    with pytest.raises(ValueError, match="kr"):
+        msa.Bank(docs, kr=torch.zeros((2, 8, 128)), **kw)  # float32 keys for a bf16 bank
+    with pytest.raises(ValueError, match="inv_norm"):
+        msa.Bank(docs, inv_norm=torch.zeros((2, 8), dtype=torch.float64), **kw)
+    with pytest.raises(ValueError, match="inv_norm"):
+        msa.Bank(docs, chunk_cap=16, inv_norm=torch.zeros((2, 8)), **kw)  # capacity rows
+    short = torch.zeros(2048 * 8 * 128 - 1, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="k_store"):
+        msa.Bank(docs, k_store=short, v_store=short, **kw)
+    full = torch.zeros(2048 * 8 * 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="together"):
+        msa.Bank(docs, k_store=full, **kw)
+    with pytest.raises(ValueError, match="v_store"):
+        msa.Bank(docs, k_store=full, v_store=full.float(), **kw)
+    with pytest.raises(ValueError, match="pinned"):  # pageable memory for a host-resident store
+        msa.Bank(docs, kv_loc="host", k_store=full, v_store=full, **kw)

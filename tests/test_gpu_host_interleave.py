@@ -152,8 +152,9 @@ def test_host_bank_concurrent_steps(msa):
         assert len(r) == 4 and all(torch.equal(o, ref) for o in r)
 
 
-def host_batches(c, n):
-    """n query batches for the host-bank workload (batch 0 = the case's)."""
+def host_batches(c, n, raw=False):
+    """n query batches for the host-bank workload (batch 0 = the case's):
+    (q, q_route, k_loc, v_loc, L) each, plus the raw local K/V with raw."""
     w, bank = c["w"], c["bank"]
     out = []
     for i in range(n):
@@ -161,21 +162,32 @@ def host_batches(c, n):
         qr = S.route_queries(w, DEV, batch=i)
         lk, lv = S.local_raw(w, DEV, batch=i)
         k_loc, v_loc, L = bank.prepare_local(lk, lv, w.P0)
-        out.append((q, qr, k_loc, v_loc, L))
+        out.append((q, qr, k_loc, v_loc, L) + ((lk, lv) if raw else ()))
     return out
 
 
+def host_oracle_check(c, batch, ids, scores, out, what):
+    """One host-bank decode step (ids/scores [B, k], out [B, h_q, d]) against
+    the oracle, on the inputs of `batch` (from host_batches(..., raw=True))."""
+    q, qr, _, _, _, lk, lv = batch
+    doc_kv = c.setdefault("oracle_kv", M.memo(lambda n: host_doc_kv(c, n)))
+    return M.check_decode_step(c["w"], ids, scores, out, q, qr, lk, lv, c["kr_o"], c["inv_o"],
+                               doc_kv, what)
+
+
 def test_host_cache_identical_results_and_counts(msa):
-    """A device document cache smaller than the bank (forcing evictions)
-    gives bit-identical results to the uncached copy path; every step's
-    distinct documents are either hits or copies, and a repeated batch is
-    served from the cache alone."""
+    """A device document cache smaller than the bank (forcing evictions):
+    every step matches the oracle and is bit-identical to the uncached copy
+    path; every step's distinct documents are either hits or copies, and a
+    repeated batch is served from the cache alone."""
     c = host_case(msa, "host_small")
     w, bank = c["w"], c["bank"]
-    batches = host_batches(c, 3)
+    batches = host_batches(c, 3, raw=True)
     ref = []
-    for q, qr, k_loc, v_loc, L in batches:
-        ids, _, out, _ = bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=qr)
+    for i, (q, qr, k_loc, v_loc, L, _, _) in enumerate(batches):
+        ids, sc, out, _ = bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=qr)
+        torch.cuda.synchronize()
+        host_oracle_check(c, batches[i], ids[0].cpu(), sc[0].cpu(), out[0].cpu(), f"uncached {i}")
         ref.append((ids.clone(), out.clone()))
     n_slots = 10  # < 24 documents, >= one step's <= 8 distinct selections
     cache = torch.empty(n_slots * bank.cache_slot_bytes(), dtype=torch.uint8, device=DEV)
@@ -184,9 +196,11 @@ def test_host_cache_identical_results_and_counts(msa):
         order = [0, 1, 2, 0, 0, 2, 1, 1]
         prev = None
         for i in order:
-            q, qr, k_loc, v_loc, L = batches[i]
-            ids, _, out, st = bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=qr)
+            q, qr, k_loc, v_loc, L, _, _ = batches[i]
+            ids, sc, out, st = bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=qr)
             torch.cuda.synchronize()
+            host_oracle_check(c, batches[i], ids[0].cpu(), sc[0].cpu(), out[0].cpu(),
+                              f"cached batch {i}")
             assert torch.equal(ids, ref[i][0]) and torch.equal(out, ref[i][1]), f"batch {i}"
             distinct = len(set(ids[0].cpu().numpy().ravel().tolist()))
             assert st.docs_cached + st.docs_copied == distinct
@@ -196,7 +210,7 @@ def test_host_cache_identical_results_and_counts(msa):
     finally:
         bank.set_cache(None)
     # detached: the staging path again
-    q, qr, k_loc, v_loc, L = batches[0]
+    q, qr, k_loc, v_loc, L, _, _ = batches[0]
     _, _, out, st = bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=qr)
     torch.cuda.synchronize()
     assert torch.equal(out, ref[0][1]) and st.docs_cached == 0
@@ -259,6 +273,113 @@ def test_host_cache_concurrent_streams(msa):
     assert not errors, errors
     for r in results:
         assert len(r) == 6 and all(torch.equal(o, refs[i]) for i, o in r)
+
+
+@pytest.mark.parametrize("window,n_slots", [(1, 24), (2, 10)])
+def test_host_prefetch_window_matches_oracle(msa, window, n_slots):
+    """A prefetch window: batch i + window is routed and its documents
+    copied into the cache (copies left in flight on the copy stream) while
+    batch i steps; nothing in the loop synchronises the device.  Every step
+    matches the oracle and the uncached results bit for bit.  With room for
+    window + 2 batches' <= 8 distinct documents (the batches in flight, the
+    one stepping and the one before it, used more recently than the
+    prefetches) a prefetched batch's step copies nothing; with 10 slots,
+    prefetches and steps evict each other's documents while copies are in
+    flight."""
+    c = host_case(msa, "host_small")
+    w, bank = c["w"], c["bank"]
+    batches = host_batches(c, 5, raw=True)
+    refs = []
+    for q, qr, k_loc, v_loc, L, _, _ in batches:
+        ids, _, out, _ = bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=qr)
+        refs.append((ids.clone(), out.clone()))
+    torch.cuda.synchronize()
+    with pytest.raises(msa.MSAError, match="cache"):  # no cache attached
+        bank.prefetch(batches[0][1], w.k)
+    bank.set_cache(torch.empty(n_slots * bank.cache_slot_bytes(), dtype=torch.uint8, device=DEV))
+    main, side, cs = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    ws_main = bank.workspace(msa.MSA_DECODE, w.B, w.h_q, w.k)
+    ws_side = bank.workspace(msa.MSA_DECODE, w.B, w.h_q, w.k)
+    results, pre = [], []
+    try:
+        for i in range(window):
+            pre.append(bank.prefetch(batches[i][1], w.k, ws=ws_side, stream=side, copy_stream=cs))
+        for i in range(len(batches)):
+            if i + window < len(batches):
+                pre.append(bank.prefetch(batches[i + window][1], w.k, ws=ws_side, stream=side,
+                                         copy_stream=cs))
+            q, qr, k_loc, v_loc, L, _, _ = batches[i]
+            ids, sc, out, st = bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=qr, ws=ws_main,
+                                         stream=main, copy_stream=cs)
+            results.append((ids, sc, out, st.docs_copied, st.docs_cached))
+        torch.cuda.synchronize()
+    finally:
+        bank.set_cache(None)
+    for i, (ids, sc, out, copied, cached) in enumerate(results):
+        host_oracle_check(c, batches[i], ids[0].cpu(), sc[0].cpu(), out[0].cpu(), f"prefetched {i}")
+        assert torch.equal(ids, refs[i][0]) and torch.equal(out, refs[i][1]), f"batch {i}"
+        distinct = len(set(ids[0].cpu().numpy().ravel().tolist()))
+        assert copied + cached == distinct
+        if n_slots >= 8 * (window + 2):
+            assert copied == 0, f"batch {i}: {copied} documents copied after a prefetch"
+    assert sum(p.docs_copied for p in pre) > 0
+
+
+def test_host_steps_back_to_back_without_syncs(msa):
+    """Host-bank steps issued back to back on one stream, with a copy stream
+    and distinct outputs, and no device synchronisation between them (the
+    call no longer waits for its attention): each equals its serial result."""
+    c = host_case(msa, "host_small")
+    w, bank = c["w"], c["bank"]
+    batches = host_batches(c, 3)
+    refs = []
+    for q, qr, k_loc, v_loc, L in batches:
+        _, _, out, _ = bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=qr)
+        torch.cuda.synchronize()
+        refs.append(out.clone())
+    for cached in (False, True):
+        if cached:  # evictions every step: 9 slots for up to 8 distinct documents a step
+            bank.set_cache(torch.empty(9 * bank.cache_slot_bytes(), dtype=torch.uint8, device=DEV))
+        main, cs = torch.cuda.Stream(), torch.cuda.Stream()
+        outs = []
+        try:
+            for r in range(8):
+                q, qr, k_loc, v_loc, L = batches[r % 3]
+                _, _, out, _ = bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=qr,
+                                         stream=main, copy_stream=cs)
+                outs.append((r % 3, out))
+            torch.cuda.synchronize()
+        finally:
+            if cached:
+                bank.set_cache(None)
+        for i, out in outs:
+            assert torch.equal(out, refs[i]), f"cached={cached} batch {i}"
+
+
+def test_pageable_host_store_is_refused(msa):
+    """msa_bank_create refuses a host-resident store in pageable memory (its
+    copies would run synchronously); the binding refuses it before the
+    library is called, so the descriptor goes to the C ABI directly."""
+    import ctypes as C
+    kr = torch.zeros((1, 2, 128), dtype=torch.bfloat16, device=DEV)
+    inv = torch.zeros((1, 2), dtype=torch.float32, device=DEV)
+    n = 512 * 8 * 128
+    pageable = torch.zeros(n, dtype=torch.bfloat16)
+    pinned = torch.zeros(n, dtype=torch.bfloat16, pin_memory=True)
+    dl = (C.c_int64 * 2)(256, 256)
+    for ks, vs, ok in ((pageable, pinned, False), (pinned, pageable, False), (pinned, pinned, True)):
+        d = msa.BankDesc(msa.MSA_BF16, 2, dl, None, 512, 1, 128, 8, 128, 10000.0, msa.MSA_KV_HOST,
+                         kr.data_ptr(), inv.data_ptr(), ks.data_ptr(), vs.data_ptr(), 0)
+        h = C.c_void_p()
+        st = msa.lib.msa_bank_create(C.byref(d), C.byref(h))
+        if ok:
+            assert st == msa.MSA_OK, msa.lib.msa_last_error()
+            msa.lib.msa_bank_destroy(h)
+        else:
+            assert st == msa.MSA_EINVAL and not h.value
+            assert b"pinned" in msa.lib.msa_last_error()
+    x = torch.ones(4, device=DEV)  # no error left behind for the next call
+    assert float((x + 1).sum()) == 8.0
 
 
 # --------------------------------------------------------------------------
