@@ -347,6 +347,24 @@ size_t msa_cache_slot_bytes(const msa_bank* bank);
 int msa_step(const msa_bank* bank, const msa_step_args* args, void* stream,
              void* copy_stream, msa_step_stats* stats);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): msa_step
+ * on a device-resident bank with its workspace taken from scratch memory the
+ * library holds on each device -- a 64 MiB device-code array, created with
+ * the library's code on that device and kept until the process ends.
+ * args->ws and args->ws_bytes are not read (staging and the copy stream do
+ * not apply to a device-resident bank).  Nothing is allocated.  Every call
+ * on one device shares that device's scratch, which keeps the last call's
+ * contents (the call clears what must start at zero, the exclusion bitmap
+ * of a multi-hop step): calls that overlap in time on one device race, so
+ * issue them on one stream or order them.
+ * Errors: as msa_step; MSA_ENOMEM (nothing launched) when the request needs
+ * more workspace than the scratch holds (msa_workspace_bytes with the
+ * splits it resolves to: a 16-query decode of a 1M-token bank needs about
+ * 2.4 MB, an 8M-token 2048-token prefill about 36 MB); MSA_EUNSUPPORTED on a
+ * host-resident bank. */
+int msa_step_static(const msa_bank* bank, const msa_step_args* args, void* stream);
+
 /* Asynchronous prefetch into the device cache of a host-resident bank
  * (intelliparadigm.com, section 5.2: prefetch memory ahead of its use so that
  * IO overlaps compute, over a window of upcoming requests; "MSA" card,

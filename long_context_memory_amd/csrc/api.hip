@@ -892,13 +892,39 @@ int msa_attend(const msa_bank* b, const msa_attend_args* a, void* stream) {
 
 namespace {
 
-// msa_step: route -> top-k -> gather -> attend for every hop
+// Scratch of msa_step_static: device memory the library owns, one copy per
+// GPU (a file-scope device array), for callers that cannot allocate.  Host
+// code never uses the array's name as an address: the address comes from
+// hipGetSymbolAddress on each device, kept per device.
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int static_scratch(void** out) {
+  int dev = 0;
+  MSA_CHECK_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MSA_EUNSUPPORTED, "device index beyond 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    MSA_CHECK_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(MSA_EHIP, "hipGetSymbolAddress returned no address for the scratch");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MSA_OK;
+}
+
+// msa_step with the workspace taken from the arguments (ws_override NULL) or
+// from ws_override / ws_override_bytes (the static scratch).
 int step_impl(const msa_bank* b, const msa_step_args* a, void* stream, void* copy_stream,
-              msa_step_stats* stats) {
+              msa_step_stats* stats, void* ws_override, size_t ws_override_bytes) {
   if (!b || !a) return fail(MSA_EINVAL, "NULL bank or args");
   Bank& bk = *const_cast<Bank*>(as_bank(b));
-  void* const ws_ptr = a->ws;
-  const size_t ws_bytes = a->ws_bytes;
+  void* const ws_ptr = ws_override ? ws_override : a->ws;
+  const size_t ws_bytes = ws_override ? ws_override_bytes : a->ws_bytes;
   const int N = bk.desc.n_docs;
   int st = check_attend_common(bk, a->mode, a->n_q, a->h_q, a->k, a->block, a->L_loc, a->k_loc,
                                a->v_loc);
@@ -931,7 +957,13 @@ int step_impl(const msa_bank* b, const msa_step_args* a, void* stream, void* cop
   const int splits =
       resolve_splits(bk, a->mode, a->splits, a->n_q, a->h_q, a->block, k, a->L_loc, pooled);
   const WsLayout L = ws_layout(bk, a->mode, a->n_q, a->h_q, k, a->block, a->hops, splits);
-  if (ws_bytes < L.total) return fail(MSA_ENOMEM, "workspace too small for msa_step");
+  if (ws_bytes < L.total) {
+    if (ws_override)
+      return fail(MSA_ENOMEM, "msa_step_static: this request needs " + std::to_string(L.total) +
+                                  " bytes of scratch, more than the " +
+                                  std::to_string(kStaticScratchBytes) + " the library holds per device");
+    return fail(MSA_ENOMEM, "workspace too small for msa_step");
+  }
   // The host part of a host-resident bank's step (id readback, copy issue,
   // remap tables) uses the bank's pinned buffers: one step at a time.
   std::unique_lock<std::mutex> host_lock;
@@ -1037,7 +1069,19 @@ extern "C" {
 
 int msa_step(const msa_bank* b, const msa_step_args* a, void* stream, void* copy_stream,
              msa_step_stats* stats) {
-  return step_impl(b, a, stream, copy_stream, stats);
+  return step_impl(b, a, stream, copy_stream, stats, nullptr, 0);
+}
+
+int msa_step_static(const msa_bank* b, const msa_step_args* a, void* stream) {
+  if (!b || !a) return fail(MSA_EINVAL, "NULL bank or args");
+  const Bank& bk = *as_bank(b);
+  if (bk.desc.kv_loc != MSA_KV_DEVICE)
+    return fail(MSA_EUNSUPPORTED, "msa_step_static: device-resident banks only (a host-resident "
+                                  "step reads ids back into pinned buffers it may have to grow)");
+  void* p = nullptr;
+  const int st = static_scratch(&p);
+  if (st) return st;
+  return step_impl(b, a, stream, nullptr, nullptr, p, kStaticScratchBytes);
 }
 
 int msa_prefetch(const msa_bank* b, const float* q_route, int32_t B, int32_t k,

@@ -27,7 +27,7 @@ EXPORTS = [
     "msa_workspace_bytes", "msa_staging_bytes", "msa_route", "msa_attend", "msa_step",
     "msa_timer_enable", "msa_timer_read", "msa_timer_reserve", "msa_bank_set_cache", "msa_cache_slot_bytes",
     "msa_bank_append", "msa_pooled_sizes", "msa_bank_set_pooled", "msa_build_pooled",
-    "msa_stream_read", "msa_prefetch",
+    "msa_stream_read", "msa_prefetch", "msa_step_static",
 ]
 MSA_STREAM_READ_BLOCKS = 4096
 MSA_TIMER_ATTENTION, MSA_TIMER_ROUTE = 0, 1
@@ -111,6 +111,8 @@ def _load():
     lib.msa_timer_reserve.argtypes = [i64]
     lib.msa_prefetch.argtypes = [vp, vp, i32, i32, vp, vp, C.c_size_t, vp, vp, C.POINTER(StepStats)]
     lib.msa_prefetch.restype = C.c_int
+    lib.msa_step_static.argtypes = [vp, C.POINTER(StepArgs), vp]
+    lib.msa_step_static.restype = C.c_int
     lib.msa_stream_read.argtypes = [vp, i64, vp, vp]
     lib.msa_stream_read.restype = C.c_int
     for f in (lib.msa_timer_enable, lib.msa_timer_read, lib.msa_timer_reserve):
