@@ -145,3 +145,87 @@ def test_prefill_float32_bank(msa):
         ref, _ = oracle_block(c, kr_o, inv_o, blk, c["ids"][blk].cpu().numpy())
         mx, rel = M.check_out(out[blk * w.block:(blk + 1) * w.block], ref, w.dtype, f"f32 block {blk}")
         print(f"f32 block {blk}: max abs {mx:.3e} rel rms {rel:.3e}")
+
+
+# channels of the rotary pairs (i, i + 64) with i >= 40: their angle moves
+# by under 0.31 rad across the 192 query positions of the small prefill
+LOWF = np.zeros(128, dtype=bool)
+LOWF[40:64] = LOWF[104:128] = True
+
+
+def dominant_token_case(w):
+    """Queries and raw K with one key (document n_docs - 1, token 777, every
+    KV head) aligned with query heads 0 and 1 of each group: about 300 log2
+    units above every other score of theirs.  Heads 2 and 3 have no
+    component along that key (zero in its channels), so their rows stay
+    ordinary.  Returns (q, k_raw, v_raw, big document, token offset)."""
+    big, pk = w.n_docs - 1, 777
+    q = S.queries(w, DEV).clone()
+    k_raw, v_raw = S.kv_raw(w, DEV)
+    k_raw = k_raw.clone()
+    lowf = torch.tensor(LOWF, device=DEV)
+    spike_head = torch.arange(w.h_q, device=DEV) % w.G < 2
+    q0 = torch.where(lowf, q[0, 0], torch.zeros_like(q[0, 0]))
+    rest = q[:, ~spike_head]
+    rest[..., lowf] = 0
+    q[:, ~spike_head] = rest
+    q[:, spike_head] = q0
+    # the key q0 takes at the middle query position, expressed at the
+    # document-local position pk; scaled so q0 . k ~ 300 log2 units
+    p_mid = w.P0 + (w.L_loc - w.B) + w.B // 2
+    q0n = M.np64(q0)
+    k = O.rope_rotate(q0n, p_mid - pk, w.rope_base)
+    k *= 300.0 * np.sqrt(w.d) / np.log2(np.e) / float(q0n @ q0n)
+    t = int(S.doc_token_offsets(w)[big]) + pk
+    k_raw[t] = torch.tensor(k, dtype=k_raw.dtype, device=DEV)
+    return q, k_raw, v_raw, big, t
+
+
+@pytest.mark.parametrize("splits", [1, 0])
+def test_prefill_late_dominant_token(msa, splits):
+    """A document ranked last holds a key that outscores everything the
+    block's first tiles gave query heads 0 and 1 by far more than a softmax
+    kept relative to the first tile's maximum can hold (2^300 overflows
+    float32): the kernel must notice and recompute with each row's true
+    maximum.  Heads 2 and 3 share the workgroups and keep ordinary scores.
+    One split, and the automatic split count (partials merged)."""
+    w = S.workload("prefill_small")
+    q, k_raw, v_raw, big, t_big = dominant_token_case(w)
+    r = S.route_vectors(w, DEV)
+    bank = msa.Bank(w.doc_len, w.h_r, w.h_kv, w.dtype, DEV, rope_base=w.rope_base)
+    bank.build(0, w.n_docs, r, k_raw, v_raw)
+    lk, lv = S.local_raw(w, DEV)
+    k_loc, v_loc, L = bank.prepare_local(lk[None], lv[None], w.P0)
+    nb = w.B // w.block
+    ids = torch.tensor([[b, b + 4, big] for b in range(nb)], dtype=torch.int32, device=DEV)
+    q_pos = w.P0 + (w.L_loc - w.B)
+    out = bank.attend(q, q_pos, ids, k_loc, v_loc, L, mode=msa.MSA_PREFILL, block=w.block,
+                      splits=splits)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    c = dict(w=w, q=q, k_raw=k_raw, v_raw=v_raw, lk=lk, lv=lv)
+    # the case is what it says: for every row of heads 0 and 1 the key
+    # exceeds the first tile's maximum by over 128 log2 units
+    kb = M.oracle_doc_kv(w, k_raw, v_raw, big)[0]
+    spike_heads = [h for h in range(w.h_q) if h % w.G < 2]
+    t0 = t_big - int(S.doc_token_offsets(w)[big])
+    for blk in range(nb):
+        k_first = M.oracle_doc_kv(w, k_raw, v_raw, blk)[0][:64]
+        for i in (0, w.block - 1):
+            qi = blk * w.block + i
+            pos = w.P0 + (w.L_loc - w.B) + qi
+            qr = O.rope_rotate(M.np64(q[qi]), np.full((w.h_q,), pos), w.rope_base)
+            for h in spike_heads:
+                g = h // w.G
+                s_big = qr[h] @ kb[t0, g] / np.sqrt(w.d) * np.log2(np.e)
+                s_first = np.max(k_first[:, g] @ qr[h]) / np.sqrt(w.d) * np.log2(np.e)
+                assert s_big - s_first > 128, (blk, i, h, s_big, s_first)
+    v_big = M.np64(v_raw[t_big])
+    for blk in range(nb):
+        ref, _ = oracle_block(c, None, None, blk, None, sel=ids[blk].tolist())
+        got = out[blk * w.block:(blk + 1) * w.block]
+        # heads 0 and 1: all weight on the one token
+        for h in spike_heads:
+            assert np.allclose(ref[:, h], v_big[h // w.G], atol=1e-12)
+        mx, rel = M.check_out(got, ref, w.dtype, f"block {blk} splits {splits}")
+        print(f"block {blk}: max abs {mx:.3e} rel rms {rel:.3e}")
