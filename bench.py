@@ -170,7 +170,7 @@ def prefill_bench(steps, warmup, splits=0):
     """Blocked prefill on the 8M-token bank (4096 docs x 2048 tokens): 2048
     query tokens in 32 blocks of 64, top-16 per block, causal 2048-token local
     context, 32 query / 8 KV heads.  Returns tokens/s and the attention
-    kernel's MFMA utilisation (algorithmic flops / event-timed duration)."""
+    kernel's roofline (algorithmic bytes and flops / event-timed duration)."""
     import torch
     from long_context_memory_amd import msa, synth as S
 
@@ -229,12 +229,29 @@ def prefill_bench(steps, warmup, splits=0):
                         "tokens in 32 blocks of 64, top-16 per block, causal 2048-token local "
                         "context, h_q=32, h_kv=8, d=128, bf16",
             "tokens_per_s": w.B * steps / dt, "ms_per_step": dt * 1e3 / steps, "steps": steps,
-            "attention": {"bound": "mfma", "achieved": flops / att_s / 1e12,
-                          "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                          "frac": flops / att_s / 1e12 / MFMA_PEAK_TFLOPS,
-                          "traffic": measured_traffic("prefill_8m_counters"),
-                          "flops_per_launch": flops, "avg_launch_us": att_s * 1e6,
-                          "hbm_GBs": kv_bytes / att_s / 1e9}}
+            "attention": prefill_roofline(flops, kv_bytes, att_s)}
+
+
+def prefill_roofline(flops, kv_bytes, att_s):
+    """The blocked prefill's roofline.  Each block's K/V tiles are read once
+    and meet 256 query rows (64 queries x 4 heads of a KV head): 256 flop per
+    byte, under the 2.5 PFLOP/s / 8 TB/s = 312 ridge, so the binding bound is
+    HBM (bytes / 8 TB/s exceeds flops / 2.5 PFLOP/s).  Both fractions are
+    reported."""
+    t_hbm = kv_bytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (MFMA_PEAK_TFLOPS * 1e12)
+    gbs, tfs = kv_bytes / att_s / 1e9, flops / att_s / 1e12
+    hbm_bound = t_hbm >= t_mfma
+    return {"bound": "hbm" if hbm_bound else "mfma",
+            "achieved": gbs if hbm_bound else tfs,
+            "peak": HBM_PEAK_GBS if hbm_bound else MFMA_PEAK_TFLOPS,
+            "unit": "GB/s" if hbm_bound else "TFLOP/s",
+            "frac": max(t_hbm, t_mfma) / att_s,
+            "traffic": measured_traffic("prefill_8m_counters"),
+            "bytes_per_launch": kv_bytes, "flops_per_launch": flops,
+            "avg_launch_us": att_s * 1e6,
+            "hbm_GBs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+            "mfma_TFLOPs": tfs, "mfma_frac": tfs / MFMA_PEAK_TFLOPS}
 
 
 def host_bank_bench(steps, warmup, cache_gb=200.0, window=4):
@@ -268,16 +285,28 @@ def host_bank_bench(steps, warmup, cache_gb=200.0, window=4):
     ws_side = bank.workspace(msa.MSA_DECODE, w.B, w.h_q, w.k)
     rt_bytes = w.C * w.h_r * (128 * 2 + 4)  # every routing key (bf16) and its norm
 
-    # a plain pinned host -> device copy of 1 GiB, for the link's own rate
+    # plain pinned host -> device copies of 1 GiB, for the link's own rate:
+    # one 1 GiB copy, and the same bytes as 64 copies of 16 MiB (the size of
+    # one 8192-token document's K or V, as the step copies them)
     hsrc = torch.empty(1 << 28, dtype=torch.float32, pin_memory=True)
     ddst = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-    ddst.copy_(hsrc, non_blocking=True)
-    torch.cuda.synchronize()
-    tc = time.perf_counter()
-    for _ in range(5):
-        ddst.copy_(hsrc, non_blocking=True)
-    torch.cuda.synchronize()
-    link = 5 * (1 << 30) / (time.perf_counter() - tc) / 1e9
+
+    def copy_rate(chunks):
+        n = (1 << 28) // chunks
+        with torch.cuda.stream(cs):
+            for c in range(chunks):
+                ddst[c * n:(c + 1) * n].copy_(hsrc[c * n:(c + 1) * n], non_blocking=True)
+        torch.cuda.synchronize()
+        tc = time.perf_counter()
+        with torch.cuda.stream(cs):
+            for _ in range(5):
+                for c in range(chunks):
+                    ddst[c * n:(c + 1) * n].copy_(hsrc[c * n:(c + 1) * n], non_blocking=True)
+        torch.cuda.synchronize()
+        return 5 * (1 << 30) / (time.perf_counter() - tc) / 1e9
+
+    link_one, link_chunked = copy_rate(1), copy_rate(64)
+    link = max(link_one, link_chunked)
     del hsrc, ddst
 
     def run(n_warm, n_steps, cached):
@@ -342,7 +371,8 @@ def host_bank_bench(steps, warmup, cache_gb=200.0, window=4):
     return {"workload": "100M-token host-resident bank: 12,207 docs x 8192 + one 256-token doc "
                         "(390,625 chunks, bf16 keys in HBM), K/V in pinned host memory (384 "
                         "document slots), B=8, top-16, local 4096",
-            "pinned_copy_GBs": link, "staging": plain, "cached_prefetch": cached,
+            "pinned_copy_GBs": link, "pinned_copy_1GiB_GBs": link_one,
+            "pinned_copy_16MiB_GBs": link_chunked, "staging": plain, "cached_prefetch": cached,
             "routing": {"bound": "hbm", "bytes_per_launch": rt_bytes,
                         "avg_launch_us": plain["routing_avg_launch_us"],
                         "achieved": plain["routing_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -435,8 +465,9 @@ def main():
     ap.add_argument("--pooled-steps", type=int, default=0,
                     help="also time compressed-memory decode on the same bank (0 skips it)")
     ap.add_argument("--single-stream-steps", type=int, default=300,
-                    help="decode steps on one stream, every attention launch event-timed "
-                         "(the kernel's isolated duration; 0 skips it)")
+                    help="decode steps on one stream, timed once without events (the step) "
+                         "and once with every launch event-timed (the kernel's isolated "
+                         "duration); 0 skips it")
     ap.add_argument("--host-bank-steps", type=int, default=8,
                     help="timed steps of each 100M-token host-bank run (0 skips the leg)")
     ap.add_argument("--host-cache-gb", type=float, default=200.0,
@@ -508,23 +539,32 @@ def main():
         for i in range(20):
             sstep(i)
         torch.cuda.synchronize()
-        msa.timer_reserve(2 * n1)
-        msa.timer_enable(True, 1)
-        msa.timer_read(msa.MSA_TIMER_ATTENTION)
-        msa.timer_read(msa.MSA_TIMER_ROUTE)
+        # the step as a caller sees it: no events on the stream
         t1 = time.perf_counter()
         for i in range(n1):
             sstep(i)
         torch.cuda.synchronize()
         sdt = time.perf_counter() - t1
+        # the same steps again with every launch bracketed by events: the
+        # kernels' own durations (events on a single stream serialise its
+        # launches, so this pass's wall time is not the step's)
+        msa.timer_reserve(2 * n1)
+        msa.timer_enable(True, 1)
+        msa.timer_read(msa.MSA_TIMER_ATTENTION)
+        msa.timer_read(msa.MSA_TIMER_ROUTE)
+        for i in range(n1):
+            sstep(i)
+        torch.cuda.synchronize()
         s_att_ms, s_att_n = msa.timer_read(msa.MSA_TIMER_ATTENTION)
         s_rt_ms, s_rt_n = msa.timer_read(msa.MSA_TIMER_ROUTE)
         msa.timer_enable(False)
+        dec_us = s_att_ms * 1e3 / max(s_att_n, 1)
         single = {"steps": n1, "ms_per_step": sdt * 1e3 / n1, "queries_per_s": w.B * n1 / sdt,
-                  "decode_avg_launch_us": s_att_ms * 1e3 / max(s_att_n, 1),
+                  "decode_avg_launch_us": dec_us,
                   "routing_avg_launch_us": s_rt_ms * 1e3 / max(s_rt_n, 1),
-                  "note": "every launch event-timed (the events sit on the stream, so the "
-                          "step time here includes their cost)"}
+                  "step_over_decode": sdt * 1e6 / n1 / dec_us,
+                  "note": "ms_per_step from a pass with no events; launch durations from a "
+                          "second pass of the same steps with every launch event-timed"}
 
     log("warmup")
     for i in range(args.warmup):
