@@ -431,3 +431,73 @@ def test_stream_read_probe_reads_every_word(msa):
         msa.stream_read(host.to(DEV), out)
         got = np.bitwise_xor.reduce(out.cpu().numpy())
         assert got == np.bitwise_xor.reduce(host.numpy()), n_words
+
+
+# channels of the rotary pairs (i, i + 64) with i >= 40
+LOWF = np.zeros(128, dtype=bool)
+LOWF[40:64] = LOWF[104:128] = True
+
+
+def dominant_key_case(w):
+    """Queries and raw K where one key of document n_docs - 1 (token 100,
+    every KV head) is aligned with query heads 0 and 1 of each group, about
+    300 log2 units above any other score of theirs; heads 2 and 3 are zero
+    in that key's channels.  Returns (q, k_raw, v_raw, big document, token
+    row of the key)."""
+    big, pk = w.n_docs - 1, 100
+    q = S.queries(w, DEV).clone()
+    k_raw, v_raw = S.kv_raw(w, DEV)
+    k_raw = k_raw.clone()
+    lowf = torch.tensor(LOWF, device=DEV)
+    spike_head = torch.arange(w.h_q, device=DEV) % w.G < 2
+    q0 = torch.where(lowf, q[0, 0], torch.zeros_like(q[0, 0]))
+    rest = q[:, ~spike_head]
+    rest[..., lowf] = 0
+    q[:, ~spike_head] = rest
+    q[:, spike_head] = q0
+    q0n = M.np64(q0)
+    k = O.rope_rotate(q0n, w.q_pos - pk, w.rope_base)  # rotated at pk it equals q0 at q_pos
+    k *= 300.0 * np.sqrt(w.d) / np.log2(np.e) / float(q0n @ q0n)
+    t = int(S.doc_token_offsets(w)[big]) + pk
+    k_raw[t] = torch.tensor(k, dtype=k_raw.dtype, device=DEV)
+    return q, k_raw, v_raw, big, t
+
+
+@pytest.mark.parametrize("splits", [1, 0])
+def test_decode_late_dominant_key(msa, splits):
+    """A key ranked last that outscores everything before it by far more
+    than float32 can hold as a ratio (2^300): the online softmax must move
+    its reference there, and the earlier probabilities must vanish rather
+    than overflow.  Query heads 2 and 3 share the key heads with ordinary
+    scores.  One split and the automatic split count (partials merged)."""
+    w = S.workload("decode_small")
+    q, k_raw, v_raw, big, t_big = dominant_key_case(w)
+    r = S.route_vectors(w, DEV)
+    bank = msa.Bank(w.doc_len, w.h_r, w.h_kv, w.dtype, DEV, rope_base=w.rope_base)
+    bank.build(0, w.n_docs, r, k_raw, v_raw)
+    lk, lv = S.local_raw(w, DEV)
+    k_loc, v_loc, L = bank.prepare_local(lk, lv, w.P0)
+    sel = [[(5 * b + j) % (w.n_docs - 1) for j in range(w.k - 1)] + [big] for b in range(w.B)]
+    ids = torch.tensor(sel, dtype=torch.int32, device=DEV)
+    out = bank.attend(q, w.q_pos, ids, k_loc, v_loc, L, splits=splits)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    qn, lkn, lvn = M.np64(q), M.np64(lk), M.np64(lv)
+    doc_kv = {n: M.oracle_doc_kv(w, k_raw, v_raw, n) for n in set(sum(sel, []))}
+    spike_heads = [h for h in range(w.h_q) if h % w.G < 2]
+    v_big = M.np64(v_raw[t_big])
+    # the case is what it says: the key leads every other document score of
+    # heads 0 and 1 by more than 128 log2 units (query 0)
+    to_log2 = np.log2(np.e) / np.sqrt(w.d)
+    qr = O.rope_rotate(qn[0], np.full((w.h_q,), w.q_pos), w.rope_base)
+    kb = doc_kv[big][0][t_big - int(S.doc_token_offsets(w)[big])]
+    for h in spike_heads:
+        g = h // w.G
+        s_big = float(qr[h] @ kb[g]) * to_log2
+        others = max(float(np.max(doc_kv[n][0][:, g] @ qr[h])) for n in sel[0][:-1]) * to_log2
+        assert s_big - others > 128, (h, s_big, others)
+    for b in range(w.B):
+        ref = M.oracle_attend_decode(w, qn[b], w.q_pos, sel[b], doc_kv, lkn[b], lvn[b], w.P0)
+        for h in spike_heads:
+            assert np.allclose(ref[h], v_big[h // w.G], atol=1e-12)
+        M.check_out(out[b], ref, w.dtype, f"query {b} splits {splits}")
