@@ -536,13 +536,14 @@ def main():
             q, q_route, k_loc, v_loc, L = batches[i % args.batches]
             bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=q_route, ws=ws[0],
                       outputs=outs[i % args.batches], stream=streams[0], splits=args.splits)
-        for i in range(20):
+        for i in range(n1):
             sstep(i)
         torch.cuda.synchronize()
         # the step as a caller sees it: no events on the stream
         t1 = time.perf_counter()
         for i in range(n1):
             sstep(i)
+        hdt = time.perf_counter() - t1  # the host's time to issue the steps
         torch.cuda.synchronize()
         sdt = time.perf_counter() - t1
         # the same steps again with every launch bracketed by events: the
@@ -552,9 +553,11 @@ def main():
         msa.timer_enable(True, 1)
         msa.timer_read(msa.MSA_TIMER_ATTENTION)
         msa.timer_read(msa.MSA_TIMER_ROUTE)
+        t2 = time.perf_counter()
         for i in range(n1):
             sstep(i)
         torch.cuda.synchronize()
+        edt = time.perf_counter() - t2
         s_att_ms, s_att_n = msa.timer_read(msa.MSA_TIMER_ATTENTION)
         s_rt_ms, s_rt_n = msa.timer_read(msa.MSA_TIMER_ROUTE)
         msa.timer_enable(False)
@@ -563,6 +566,8 @@ def main():
                   "decode_avg_launch_us": dec_us,
                   "routing_avg_launch_us": s_rt_ms * 1e3 / max(s_rt_n, 1),
                   "step_over_decode": sdt * 1e6 / n1 / dec_us,
+                  "ms_per_step_with_events": edt * 1e3 / n1,
+                  "host_issue_ms_per_step": hdt * 1e3 / n1,
                   "note": "ms_per_step from a pass with no events; launch durations from a "
                           "second pass of the same steps with every launch event-timed"}
 
