@@ -32,6 +32,12 @@
  *   - Every data array (device, or pinned host for a host-resident store)
  *     starts on a 16-byte boundary, as hipMalloc, hipHostMalloc and torch
  *     allocations do; a misaligned array is MSA_EINVAL.
+ *   - msa_bank_create, msa_build_bank and msa_prepare_local check each
+ *     device array they are given against the allocation that holds it
+ *     (hipMemGetAddressRange): an array that would end past its allocation
+ *     for the shape the call implies is MSA_EINVAL, nothing launched.  Memory
+ *     the runtime cannot place (another allocator's) is not checked; an
+ *     array carved from a larger allocation passes if it ends inside it.
  *   - No call records a memset: the library clears device memory with a
  *     kernel, so the kernel launches of a device-bank call can be captured
  *     into a HIP graph (a host-resident bank's msa_step synchronises and

@@ -248,6 +248,28 @@ bool pinned_host_range(const void* p, size_t bytes) {
   return true;
 }
 
+// Whether [p, p + bytes) lies inside the allocation that holds p, as the
+// runtime records it (hipMemGetAddressRange).  The library sees only
+// pointers, so this is where an array shorter than its stated shape is
+// caught before a kernel runs past its end.  A pointer the runtime cannot
+// place (memory from another allocator) passes: nothing can be checked.
+// A caching allocator's array passes if it ends inside its segment.
+bool extent_ok(const void* p, size_t bytes) {
+  if (!p || bytes == 0) return true;
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, const_cast<void*>(p)) != hipSuccess) {
+    (void)hipGetLastError();  // leave no error behind for the next call to report
+    return true;
+  }
+  return (const char*)p + bytes <= (const char*)base + size;
+}
+
+int extent_fail(const char* what, size_t bytes) {
+  return fail(MSA_EINVAL, std::string(what) + " is shorter than its shape says (" +
+                              std::to_string(bytes) + " bytes, past the end of its allocation)");
+}
+
 }  // namespace msa
 
 using namespace msa;
@@ -479,6 +501,22 @@ int msa_bank_create(const msa_bank_desc* d, msa_bank** out) {
     delete bk;
     return st;
   }
+  {
+    const size_t dsz = dtype_size(d->dtype);
+    const size_t kr_bytes = (size_t)d->h_r * bk->chunk_stride * kD * dsz;
+    const size_t in_bytes = (size_t)d->h_r * bk->chunk_stride * sizeof(float);
+    const size_t kv_bytes = (size_t)d->kv_tokens * d->h_kv * kD * dsz;
+    const char* bad = !extent_ok(d->kr, kr_bytes)         ? "kr"
+                      : !extent_ok(d->inv_norm, in_bytes) ? "inv_norm"
+                      : d->kv_loc == MSA_KV_DEVICE && !extent_ok(d->k_store, kv_bytes) ? "k_store"
+                      : d->kv_loc == MSA_KV_DEVICE && !extent_ok(d->v_store, kv_bytes) ? "v_store"
+                                                                                        : nullptr;
+    if (bad) {
+      msa_bank_destroy(reinterpret_cast<msa_bank*>(bk));
+      return extent_fail(bad, !strcmp(bad, "kr") ? kr_bytes
+                              : !strcmp(bad, "inv_norm") ? in_bytes : kv_bytes);
+    }
+  }
   if (d->kv_loc == MSA_KV_HOST) {
     const size_t store_bytes = (size_t)d->kv_tokens * d->h_kv * kD * dtype_size(d->dtype);
     if (!pinned_host_range(d->k_store, store_bytes) || !pinned_host_range(d->v_store, store_bytes)) {
@@ -571,6 +609,14 @@ int msa_build_bank(const msa_bank* b, int32_t doc0, int32_t doc1, const void* ro
     return fail(MSA_EUNSUPPORTED, "K/V of a host-resident store are not written by the library");
   if (!all_al16(route_vec, k_raw, v_raw))
     return fail(MSA_EINVAL, "route_vec, k_raw and v_raw must be 16-byte aligned");
+  {
+    const size_t rows = (size_t)(bk.tok_off[doc1] - bk.tok_off[doc0]);
+    const size_t dsz = dtype_size(bk.desc.dtype);
+    const size_t rv_bytes = rows * bk.desc.h_r * kD * dsz, kv_bytes = rows * bk.desc.h_kv * kD * dsz;
+    if (!extent_ok(route_vec, rv_bytes)) return extent_fail("route_vec", rv_bytes);
+    if (!extent_ok(k_raw, kv_bytes)) return extent_fail("k_raw", kv_bytes);
+    if (!extent_ok(v_raw, kv_bytes)) return extent_fail("v_raw", kv_bytes);
+  }
   hipStream_t s = (hipStream_t)stream;
   if (route_vec) MSA_CHECK_HIP(launch_pool_keys(bk, doc0, doc1, route_vec, s));
   else MSA_CHECK_HIP(launch_key_norms(bk, doc0, doc1, s));
@@ -586,6 +632,16 @@ int msa_prepare_local(const msa_bank* b, const void* k_raw, const void* v_raw, i
   if (n_seq == 0 || L == 0) return MSA_OK;
   if (!k_loc || !v_loc || !k_raw || !v_raw) return fail(MSA_EINVAL, "NULL pointer");
   if (!all_al16(k_loc, v_loc, k_raw, v_raw)) return fail(MSA_EINVAL, "16-byte alignment");
+  {
+    const Bank& bk = *as_bank(b);
+    const size_t dsz = dtype_size(bk.desc.dtype);
+    const size_t k_bytes = (size_t)n_seq * L * bk.desc.h_kv * kD * dsz;
+    const size_t v_bytes = (size_t)n_seq * bk.desc.h_kv * ((L + 63) / 64) * 64 * kD * dsz;
+    if (!extent_ok(k_raw, k_bytes)) return extent_fail("k_raw", k_bytes);
+    if (!extent_ok(v_raw, k_bytes)) return extent_fail("v_raw", k_bytes);
+    if (!extent_ok(k_loc, k_bytes)) return extent_fail("k_loc", k_bytes);
+    if (!extent_ok(v_loc, v_bytes)) return extent_fail("v_loc", v_bytes);
+  }
   MSA_CHECK_HIP(launch_prepare_local(*as_bank(b), k_raw, v_raw, n_seq, L, pos0, k_loc, v_loc,
                                      (hipStream_t)stream));
   return MSA_OK;
