@@ -3,7 +3,9 @@ computes one by one:
 
 - the 8M-token blocked prefill, in the launch configuration the benchmark
   times (automatic splits);
-- the 100M-token host-resident bank (slot-backed pinned store);
+- the 100M-token host-resident bank (slot-backed pinned store), staged, and
+  through a device document cache filled by a prefetch window on other
+  streams;
 - three interleaved hops over a 32 Mi-token bank of lognormal documents.
 
 For each, routing (top-k and scores) is checked for every query or block, and
@@ -79,16 +81,47 @@ def test_prefill_full_sampled(msa):
         print(f"prefill block {blk} queries {qs.tolist()}: max abs {mx:.3e} rel rms {rel:.3e}")
 
 
+_HOST = {}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def release_host_bank():
+    yield
+    _HOST.clear()
+    torch.cuda.empty_cache()
+
+
+def host_case(msa):
+    """The 100M-token slot-backed host bank (built once for the module) and
+    the oracle's keys and norms."""
+    if not _HOST:
+        w = S.workload("host_100m")
+        slot_len, kv_off = S.host_slot_layout(w)
+        kr = S.keys_direct(w, DEV).to(w.torch_dtype)
+        bank = msa.Bank(w.doc_len, w.h_r, w.h_kv, w.dtype, DEV, kv_loc="host", kv_off=kv_off,
+                        kv_tokens=int(sum(slot_len)), rope_base=w.rope_base,
+                        kr=kr.permute(1, 0, 2).contiguous())
+        bank.build(0, w.n_docs)
+        msa.fill_host_store(bank, slot_len, lambda t0, t1: S.host_kv_raw(w, DEV, t0, t1),
+                            slots_per_pass=32)
+        kr_o = M.np64(kr)
+        del kr
+        _HOST.update(w=w, bank=bank, kv_off=kv_off, kr_o=kr_o, inv_o=O.inverse_norms(kr_o))
+    return _HOST
+
+
+def host_doc_kv(w, kv_off, sel):
+    doc_kv = {}
+    for n in sel:
+        t0, Ln = int(kv_off[n]), int(w.doc_len[n])
+        k_raw, v_raw = S.host_kv_raw(w, DEV, t0, t0 + Ln)
+        doc_kv[n] = (O.bank_keys_rotated(M.np64(k_raw), [Ln], w.rope_base, w.dtype), M.np64(v_raw))
+    return doc_kv
+
+
 def test_host_bank_full_sampled(msa):
-    w = S.workload("host_100m")
-    slot_len, kv_off = S.host_slot_layout(w)
-    kr = S.keys_direct(w, DEV).to(w.torch_dtype)
-    bank = msa.Bank(w.doc_len, w.h_r, w.h_kv, w.dtype, DEV, kv_loc="host", kv_off=kv_off,
-                    kv_tokens=int(sum(slot_len)), rope_base=w.rope_base,
-                    kr=kr.permute(1, 0, 2).contiguous())
-    bank.build(0, w.n_docs)
-    msa.fill_host_store(bank, slot_len, lambda t0, t1: S.host_kv_raw(w, DEV, t0, t1),
-                        slots_per_pass=32)
+    c = host_case(msa)
+    w, bank, kv_off, kr_o, inv_o = c["w"], c["bank"], c["kv_off"], c["kr_o"], c["inv_o"]
     q = S.queries(w, DEV)
     q_route = S.route_queries(w, DEV)
     lk, lv = S.local_raw(w, DEV)
@@ -96,9 +129,6 @@ def test_host_bank_full_sampled(msa):
     ids, scores, out, st = bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=q_route)
     torch.cuda.synchronize()
     ids_np, sc_np, out_np = ids[0].cpu().numpy(), scores[0].cpu().numpy(), out[0].cpu().numpy()
-    kr_o = M.np64(kr)
-    del kr
-    inv_o = O.inverse_norms(kr_o)
     so = O.cosine_doc_scores(M.np64(q_route), kr_o, inv_o, w.doc_len)
     near = M.check_topk(ids_np, sc_np, so, w.k)
     print(f"host bank routing: {w.B} queries over {w.n_docs} documents, {near} near-tie")
@@ -117,15 +147,60 @@ def test_host_bank_full_sampled(msa):
     q64, lk64, lv64 = M.np64(q), M.np64(lk), M.np64(lv)
     for b in M.seeded_subset(w.B, 2, 41):
         sel = pick(ids_np[b], so[b], w.k)
-        doc_kv = {}
-        for n in sel:
-            t0, Ln = int(kv_off[n]), int(w.doc_len[n])
-            k_raw, v_raw = S.host_kv_raw(w, DEV, t0, t0 + Ln)
-            doc_kv[n] = (O.bank_keys_rotated(M.np64(k_raw), [Ln], w.rope_base, w.dtype),
-                         M.np64(v_raw))
+        doc_kv = host_doc_kv(w, kv_off, sel)
         ref = M.oracle_attend_decode(w, q64[b], w.q_pos, sel, doc_kv, lk64[b], lv64[b], w.P0)
         mx, rel = M.check_out(out_np[b][None], ref[None], w.dtype, f"host bank query {b}")
         print(f"host bank query {b}: max abs {mx:.3e} rel rms {rel:.3e}")
+
+
+def test_host_bank_cached_prefetch_full_sampled(msa):
+    """The benchmark's cached leg on the 100M-token host bank: a device
+    document cache, a 4-batch prefetch window on a side stream, steps on a
+    main stream with their copies on a copy stream.  The prefetched steps
+    copy nothing; routing of every query and two sampled queries per step
+    against the oracle.  (A 32 GB cache, not the benchmark's 200 GB: the
+    same kernels and host path with fewer slots, which is still room for
+    every document of the window and the steps.)"""
+    c = host_case(msa)
+    w, bank, kv_off, kr_o, inv_o = c["w"], c["bank"], c["kv_off"], c["kr_o"], c["inv_o"]
+    window, n_steps = 4, 2
+    slot = bank.cache_slot_bytes()
+    slots = (32 << 30) // slot
+    assert slots >= w.B * w.k * (window + n_steps)
+    bank.set_cache(torch.empty(slots * slot, dtype=torch.uint8, device=DEV))
+    try:
+        q = S.queries(w, DEV)
+        lk, lv = S.local_raw(w, DEV)
+        k_loc, v_loc, L = bank.prepare_local(lk, lv, w.P0)
+        main, side, cs = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+        ws = bank.workspace(msa.MSA_DECODE, w.B, w.h_q, w.k)
+        ws_side = bank.workspace(msa.MSA_DECODE, w.B, w.h_q, w.k)
+        qrs = [S.route_queries(w, DEV, batch=i) for i in range(1, 1 + window + n_steps)]
+        torch.cuda.synchronize()
+        for i in range(window):
+            bank.prefetch(qrs[i], w.k, ws=ws_side, stream=side, copy_stream=cs)
+        res = []
+        for i in range(n_steps):
+            bank.prefetch(qrs[i + window], w.k, ws=ws_side, stream=side, copy_stream=cs)
+            res.append(bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=qrs[i], ws=ws,
+                                 stream=main, copy_stream=cs))
+        torch.cuda.synchronize()
+        q64, lk64, lv64 = M.np64(q), M.np64(lk), M.np64(lv)
+        for i, (ids, scores, out, st) in enumerate(res):
+            assert st.docs_copied == 0 and st.docs_cached > 0, (i, st.docs_copied, st.docs_cached)
+            ids_np, sc_np = ids[0].cpu().numpy(), scores[0].cpu().numpy()
+            so = O.cosine_doc_scores(M.np64(qrs[i]), kr_o, inv_o, w.doc_len)
+            M.check_topk(ids_np, sc_np, so, w.k)
+            for b in M.seeded_subset(w.B, 2, 61 + i):
+                sel = pick(ids_np[b], so[b], w.k)
+                ref = M.oracle_attend_decode(w, q64[b], w.q_pos, sel,
+                                             host_doc_kv(w, kv_off, sel), lk64[b], lv64[b], w.P0)
+                mx, rel = M.check_out(out[0][b].cpu().numpy()[None], ref[None], w.dtype,
+                                      f"cached step {i} query {b}")
+                print(f"cached step {i} query {b}: max abs {mx:.3e} rel rms {rel:.3e}")
+    finally:
+        torch.cuda.synchronize()
+        bank.set_cache(None)
 
 
 def test_interleave_full_sampled(msa):
