@@ -319,8 +319,9 @@ int msa_build_pooled(const msa_bank* bank, int32_t doc_begin, int32_t doc_end, v
  * section 5.2: keep frequently used memory in HBM; "MSA" card, "Pułapki
  * implementacyjne": the CPU-GPU link is the bottleneck of large banks).
  *   cache: device memory the caller owns (NULL detaches), cache_bytes of it,
- *     divided into msa_cache_slot_bytes() slots, each holding one document's
- *     K then V in the store layouts.
+ *     divided into n = cache_bytes / msa_cache_slot_bytes() slots, each
+ *     holding one document's K and V in the store layouts: slot s's K at
+ *     s * S and its V at n * S + s * S, with S = msa_cache_slot_bytes() / 2.
  * While a cache is attached, msa_step keeps recently selected documents
  * resident: a selected document already in a slot is read from there, any
  * other is copied from the host store into the least recently used slot
@@ -346,10 +347,16 @@ size_t msa_cache_slot_bytes(const msa_bank* bank);
  * device cache attached, found in the cache or copied into a cache slot --
  * on `copy_stream` (NULL = `stream`), and attention waits, on the device,
  * for the copies it reads (including a cached document's copy that an
- * earlier call or msa_prefetch left in flight).  The call returns once the
- * attention is enqueued; `staging` may be reused by the next call on the
- * same `stream`.  `stats` (host, may be NULL) receives copy and cache-hit
- * counts. */
+ * earlier call or msa_prefetch left in flight).  A document copied into a
+ * cache slot has its K copied on `copy_stream` and its V on a second copy
+ * stream the bank owns (created with a host-resident bank, default
+ * priority), which starts after the work already on `copy_stream` and which
+ * `copy_stream` waits for after the call's last copy: seen from
+ * `copy_stream`, every copy of the call is on it, and two copies in flight
+ * keep the link busy through each copy's start-up.  Copies into `staging`
+ * all run on `copy_stream`.  The call returns once the attention is
+ * enqueued; `staging` may be reused by the next call on the same `stream`.
+ * `stats` (host, may be NULL) receives copy and cache-hit counts. */
 int msa_step(const msa_bank* bank, const msa_step_args* args, void* stream,
              void* copy_stream, msa_step_stats* stats);
 
@@ -380,7 +387,8 @@ int msa_step_static(const msa_bank* bank, const msa_step_args* args, void* strea
  * on `stream`, reads the selection back (blocking once on `stream`), and
  * makes every distinct selected document resident: a document already in
  * the cache is marked recently used, any other is copied into the least
- * recently used slot on `copy_stream` (NULL = `stream`).  The copies are
+ * recently used slot on `copy_stream` (NULL = `stream`; V copies on the
+ * bank's second copy stream, joined back as in msa_step).  The copies are
  * left in flight: a later msa_step that selects these documents finds them
  * in the cache and its attention waits for them on the device.  Running
  * route + prefetch for batch i + W while batch i steps keeps the host link

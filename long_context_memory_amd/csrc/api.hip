@@ -526,6 +526,9 @@ int msa_bank_create(const msa_bank_desc* d, msa_bank** out) {
     }
     hipError_t e = host_buffers_reserve(*bk, kHostIdsInitial);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&bk->tables_done, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&bk->copy_fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&bk->copy_join, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&bk->copy2, hipStreamNonBlocking);
     for (int i = 0; i < Bank::kRing && e == hipSuccess; ++i)
       e = hipEventCreateWithFlags(&bk->ring[i], hipEventDisableTiming);
     if (e != hipSuccess) {
@@ -577,6 +580,12 @@ int msa_bank_destroy(msa_bank* b) {
   if (bk->tables_pending) (void)hipEventSynchronize(bk->tables_done);
   if (bk->tables_done) (void)hipEventDestroy(bk->tables_done);
   if (bk->ring[0]) (void)ring_drain(*bk);
+  if (bk->copy2) {
+    (void)hipStreamSynchronize(bk->copy2);
+    (void)hipStreamDestroy(bk->copy2);
+  }
+  if (bk->copy_fork) (void)hipEventDestroy(bk->copy_fork);
+  if (bk->copy_join) (void)hipEventDestroy(bk->copy_join);
   for (hipEvent_t e : bk->ring)
     if (e) (void)hipEventDestroy(e);
   if (bk->dev_mem) (void)hipFree(bk->dev_mem);
@@ -755,13 +764,39 @@ int make_resident(Bank& bk, const std::vector<int32_t>& docs, void* staging, siz
                   Resident* r) {
   const int32_t n = (int32_t)docs.size();
   const size_t tok_bytes = (size_t)bk.desc.h_kv * kD * dtype_size(bk.desc.dtype);
+  // Copies into cache slots: K on cs, V on the bank's second copy stream,
+  // forked from cs before the first copy (after every wait placed on cs)
+  // and joined back into cs after the last.  Copies into staging stay on cs
+  // alone: there two streams measured slower (a step's copies are issued in
+  // one burst and the attention waits for all of them), while copies into
+  // slots, queued ahead by the prefetch window, gain from two in flight.
+  const bool two = bk.cache != nullptr;
+  bool forked = false;
+  auto fork = [&]() -> hipError_t {
+    if (forked) return hipSuccess;
+    forked = true;
+    hipError_t e = hipEventRecord(bk.copy_fork, cs);
+    return e == hipSuccess ? hipStreamWaitEvent(bk.copy2, bk.copy_fork, 0) : e;
+  };
+  auto join = [&]() -> hipError_t {
+    if (!forked) return hipSuccess;
+    forked = false;
+    hipError_t e = hipEventRecord(bk.copy_join, bk.copy2);
+    return e == hipSuccess ? hipStreamWaitEvent(cs, bk.copy_join, 0) : e;
+  };
+  struct JoinOnExit {  // an early error return still orders cs after the V copies
+    decltype(join)& f;
+    ~JoinOnExit() { (void)f(); }
+  } join_on_exit{join};
   auto copy_doc = [&](int32_t id, char* kdst, char* vdst) -> hipError_t {
     const size_t bytes = (size_t)bk.doc_len[id] * tok_bytes;
     const size_t src_o = (size_t)bk.kv_off[id] * tok_bytes;
-    hipError_t e = hipMemcpyAsync(kdst, (const char*)bk.desc.k_store + src_o, bytes,
-                                  hipMemcpyHostToDevice, cs);
+    hipError_t e = two ? fork() : hipSuccess;
     if (e == hipSuccess)
-      e = hipMemcpyAsync(vdst, (const char*)bk.desc.v_store + src_o, bytes, hipMemcpyHostToDevice, cs);
+      e = hipMemcpyAsync(kdst, (const char*)bk.desc.k_store + src_o, bytes, hipMemcpyHostToDevice, cs);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(vdst, (const char*)bk.desc.v_store + src_o, bytes, hipMemcpyHostToDevice,
+                         two ? bk.copy2 : cs);
     if (stats) {
       stats->docs_copied += 1;
       stats->bytes_copied += (int64_t)(2 * bytes);
@@ -832,6 +867,7 @@ int make_resident(Bank& bk, const std::vector<int32_t>& docs, void* staging, siz
     }
     if (n > 0) filled.push_back(-1);
   }
+  MSA_CHECK_HIP(join());
   if (!filled.empty()) {
     uint64_t tag = 0;
     MSA_CHECK_HIP(ring_record(bk, cs, &tag));

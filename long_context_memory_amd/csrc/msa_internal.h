@@ -56,6 +56,14 @@ struct Bank {
   int64_t* h_src_off = nullptr;
   hipEvent_t tables_done = nullptr;  // remap tables read out of h_src / h_src_off
   bool tables_pending = false;
+  // A second copy stream (default priority) that takes the V copy of each
+  // document copied into a cache slot while the caller's copy stream takes
+  // its K: two copies in flight keep the link busy through each copy's
+  // start-up.  copy_fork orders it after the caller's copy stream,
+  // copy_join orders the copy stream after it, so callers see every copy
+  // of a call on their copy stream.
+  hipStream_t copy2 = nullptr;
+  hipEvent_t copy_fork = nullptr, copy_join = nullptr;
   // Ordering events: a ring of kRing events, recorded in sequence.  An
   // entry is synchronised before it is recorded again, so work tagged with a
   // sequence number older than the ring has completed.  Tags are stored as

@@ -179,6 +179,22 @@ def _stream(stream=None):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
 
 
+def _hold(tensors, *streams):
+    """Tensors the binding allocated (on the current stream) and a call then
+    used on other streams: record those streams, so that torch's caching
+    allocator hands the memory out again only after the work queued there
+    has completed, however soon the tensor is dropped."""
+    for s in streams:
+        if s is None:
+            continue
+        ts = s if isinstance(s, torch.cuda.Stream) else torch.cuda.ExternalStream(int(s))
+        if ts.cuda_stream == torch.cuda.current_stream().cuda_stream:
+            continue
+        for t in tensors:
+            if t is not None:
+                t.record_stream(ts)
+
+
 def _expect(t, shape, dtype, name, device=None):
     """Refuse a tensor whose shape, dtype, layout or device is not what the C
     call will read or write: the library sees only a pointer, so a tensor
@@ -395,14 +411,17 @@ class Bank:
         if exclude is not None:
             _expect(exclude, (B, (self.n_docs + 31) // 32), torch.int32, "exclude", self.device)
         need = self.workspace_bytes(MSA_DECODE, B, self.h_kv, k, 1, 1, 0)
+        own = []
         if ws is None:
             ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
+            own.append(ws)
         _expect_bytes(ws, need, "ws", self.device)
         st = StepStats()
         cs = None if copy_stream is None else _stream(copy_stream)
         _check(lib.msa_prefetch(self.handle, _ptr(q_route), B, int(k), _ptr(exclude), _ptr(ws),
                                 ws.numel() * ws.element_size(), _stream(stream), cs, C.byref(st)),
                "msa_prefetch")
+        _hold(own, stream)
         return st
 
     def staging(self, n_groups, k):
@@ -428,11 +447,14 @@ class Bank:
         _expect(q_route, (B, self.h_r, 128), torch.float32, "q_route", self.device)
         if exclude is not None:
             _expect(exclude, (B, (self.n_docs + 31) // 32), torch.int32, "exclude", self.device)
+        own = []
         if ws is None:
             ws = self.workspace(MSA_DECODE, B, self.h_kv, k)
+            own.append(ws)
         if outputs is None:
             ids = torch.empty((B, k), dtype=torch.int32, device=self.device)
             scores = torch.empty((B, k), dtype=torch.float32, device=self.device)
+            own += [ids, scores]
         else:
             ids, scores = outputs
         _expect(ids, (B, k), torch.int32, "ids", self.device)
@@ -440,6 +462,7 @@ class Bank:
         _check(lib.msa_route(self.handle, _ptr(q_route), B, k, _ptr(exclude), _ptr(ids),
                              _ptr(scores), _ptr(ws), ws.numel() * ws.element_size(),
                              _stream(stream)), "msa_route")
+        _hold(own, stream)
         return ids, scores
 
     def attend(self, q, q_pos: int, ids, k_loc, v_loc, L_loc: int, mode=MSA_DECODE, block: int = 64, splits: int = 0, ws=None, src=None,
@@ -451,10 +474,13 @@ class Bank:
         if ids is not None:
             _expect(ids, (n_groups, k), torch.int32, "ids", self.device)
         self._check_local(k_loc, v_loc, L_loc, 1 if prefill else n_q)
+        own = []
         if ws is None:
             ws = self.workspace(mode, n_q, h_q, k, block, 1, splits)
+            own.append(ws)
         if out is None:
             out = torch.empty((n_q, h_q, 128), dtype=torch.float32, device=self.device)
+            own.append(out)
         _expect(out, (n_q, h_q, 128), torch.float32, "out", self.device)
         sk, sv, so, sl = (None, None, None, None) if src is None else src
         if src is not None:
@@ -469,6 +495,7 @@ class Bank:
                        ws.numel() * ws.element_size(), splits, _ptr(sk), _ptr(sv), _ptr(so), _ptr(sl),
                        0 if sl is None else int(sl.numel()), int(memory))
         _check(lib.msa_attend(self.handle, C.byref(a), _stream(stream)), "msa_attend")
+        _hold(own, stream)
         return out
 
     def step(self, q, q_pos: int, k: int, k_loc, v_loc, L_loc: int, q_route=None, route_tokens=None, mode=MSA_DECODE, block: int = 64, hops: int = 1,
@@ -491,15 +518,19 @@ class Bank:
         if exclude is not None:
             _expect(exclude, (n_groups, (self.n_docs + 31) // 32), torch.int32, "exclude",
                     self.device)
+        own = []
         if ws is None:
             ws = self.workspace(mode, n_q, h_q, k, block, hops, splits)
+            own.append(ws)
         if (self.kv_host and staging is None and getattr(self, "cache", None) is None
                 and memory == MSA_MEMORY_TOKENS):
             staging = self.staging(n_groups, k)
+            own.append(staging)
         if outputs is None:
             ids = torch.empty((hops, n_groups, k), dtype=torch.int32, device=self.device)
             scores = torch.empty((hops, n_groups, k), dtype=torch.float32, device=self.device)
             out = torch.empty((hops, n_q, h_q, 128), dtype=torch.float32, device=self.device)
+            own += [ids, scores, out]
         else:
             ids, scores, out = outputs
         _expect(ids, (hops, n_groups, k), torch.int32, "ids", self.device)
@@ -516,6 +547,7 @@ class Bank:
         cs = None if copy_stream is None else _stream(copy_stream)
         _check(lib.msa_step(self.handle, C.byref(a), _stream(stream), cs, C.byref(st)),
                "msa_step")
+        _hold(own, stream, copy_stream)
         return ids, scores, out, st
 
 

@@ -325,6 +325,49 @@ def test_host_prefetch_window_matches_oracle(msa, window, n_slots):
     assert sum(p.docs_copied for p in pre) > 0
 
 
+def test_host_prefetch_copies_complete_on_the_copy_stream(msa):
+    """Copies into cache slots run two at a time: each document's K on the
+    caller's copy stream and its V on a second copy stream the bank owns,
+    joined back into the caller's stream.  Work queued on the copy stream
+    after msa_prefetch returns -- here, reading the cache back, with no
+    other synchronisation -- sees every copied document whole, K and V
+    (a slot holds a document's K in the cache's first half and its V at the
+    same offset in the second half)."""
+    c = host_case(msa, "host_small")
+    w, bank = c["w"], c["bank"]
+    n_slots = 24
+    slot = bank.cache_slot_bytes()
+    half = slot // 2 // 2  # bf16 elements of a slot's K (or V) part
+    per_tok = w.h_kv * 128
+    qr = S.route_queries(w, DEV, batch=3)
+    ids, _ = bank.route(qr, w.k)
+    docs = sorted(set(ids.cpu().numpy().ravel().tolist()) - {-1})
+    cache = torch.zeros(n_slots * slot, dtype=torch.uint8, device=DEV)
+    torch.cuda.synchronize()
+    bank.set_cache(cache)
+    side, cs = torch.cuda.Stream(), torch.cuda.Stream()
+    try:
+        st = bank.prefetch(qr, w.k, stream=side, copy_stream=cs)
+        with torch.cuda.stream(cs):
+            got = cache.view(torch.bfloat16).cpu()  # queued on cs after the call's copies
+    finally:
+        torch.cuda.synchronize()
+        bank.set_cache(None)
+    assert st.docs_copied == len(docs) and st.docs_cached == 0
+    kpart = got[:n_slots * half].view(n_slots, half)
+    vpart = got[n_slots * half:].view(n_slots, half)
+    for n in docs:
+        a, m = int(c["kv_off"][n]) * per_tok, int(w.doc_len[n]) * per_tok
+        kref, vref = bank.k_store[a:a + m].cpu(), bank.v_store[a:a + m].cpu()
+        # documents that share a slot of the slot-backed host store hold
+        # the same K and V, so K may match several cache slots: each of
+        # them must hold the matching V
+        slots = [i for i in range(n_slots) if torch.equal(kpart[i, :m], kref)]
+        assert slots, f"document {n}: K not found in the cache"
+        for i in slots:
+            assert torch.equal(vpart[i, :m], vref), f"document {n}: V in slot {i} not complete"
+
+
 def test_host_steps_back_to_back_without_syncs(msa):
     """Host-bank steps issued back to back on one stream, with a copy stream
     and distinct outputs, and no device synchronisation between them (the
