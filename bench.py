@@ -630,7 +630,11 @@ def main():
                      # includes time shared with the other stream's launch; the
                      # whole-run rate counts every byte once over the wall clock
                      "aggregate_GBs": kv_bytes * args.steps / dt / 1e9,
-                     "aggregate_frac": kv_bytes * args.steps / dt / 1e9 / HBM_PEAK_GBS},
+                     "aggregate_frac": kv_bytes * args.steps / dt / 1e9 / HBM_PEAK_GBS,
+                     "note": "frac: bytes per launch over the average event-timed launch, "
+                             "each launch overlapped by the other stream's; aggregate_frac: "
+                             "every launch's bytes over the timed wall clock; isolated: the "
+                             "same launches on one stream, none overlapping"},
         # the routing scan streams every routing key and its norm once per step;
         # timed inside the two-stream step, where it overlaps the other
         # stream's attention
