@@ -323,7 +323,14 @@ def host_bank_bench(steps, warmup, cache_gb=200.0, window=4):
     def run(n_warm, n_steps, cached):
         total = n_warm + n_steps
         qrs = [S.route_queries(w, dev, batch=i) for i in range(total + window)]
-        stg = None if cached else bank.staging(w.B, w.k)
+        # staging: steps alternate over two streams, each with its own staging
+        # buffer, so one step's copies queue behind the previous step's while
+        # that step's attention and this step's routing run (one staging
+        # buffer on one stream leaves the link idle for that time); cached:
+        # steps on one stream, the prefetch window on the side stream
+        stg = None if cached else [bank.staging(w.B, w.k) for _ in range(2)]
+        wss = [ws, ws_side]
+        step_streams = [main] if cached else [main, side]
         copied = [0, 0, 0]  # bytes, documents copied, documents found cached
 
         def count(st):
@@ -347,8 +354,10 @@ def host_bank_bench(steps, warmup, cache_gb=200.0, window=4):
             if cached:
                 count(bank.prefetch(qrs[i + window], w.k, ws=ws_side, stream=side,
                                     copy_stream=cs))
-            _, _, _, st = bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=qrs[i], ws=ws,
-                                    staging=stg, stream=main, copy_stream=cs)
+            j = i % len(step_streams)
+            _, _, _, st = bank.step(q, w.q_pos, w.k, k_loc, v_loc, L, q_route=qrs[i], ws=wss[j],
+                                    staging=None if cached else stg[j], stream=step_streams[j],
+                                    copy_stream=cs)
             count(st)
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
