@@ -684,8 +684,11 @@ int msa_bank_set_cache(msa_bank* b, void* cache, size_t cache_bytes) {
   if (bk.desc.kv_loc != MSA_KV_HOST) return fail(MSA_EINVAL, "a device cache needs a host-resident bank");
   if (!al16(cache)) return fail(MSA_EINVAL, "the cache must be 16-byte aligned");
   std::lock_guard<std::mutex> lock(bk.host_mu);
-  // earlier steps' copies and attention may still use the old cache
+  // earlier steps' copies and attention may still use the old cache (the
+  // second copy stream too, should a call have failed before tagging its
+  // copies)
   MSA_CHECK_HIP(ring_drain(bk));
+  if (bk.copy2) MSA_CHECK_HIP(hipStreamSynchronize(bk.copy2));
   bk.cache = nullptr;
   bk.cache_slots = 0;
   bk.cache_doc.clear();
