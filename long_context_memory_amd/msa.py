@@ -187,7 +187,13 @@ def _hold(tensors, *streams):
     for s in streams:
         if s is None:
             continue
-        ts = s if isinstance(s, torch.cuda.Stream) else torch.cuda.ExternalStream(int(s))
+        if isinstance(s, torch.cuda.Stream):
+            ts = s
+        else:  # a raw handle: an int or a ctypes pointer
+            h = int(getattr(s, "value", s) or 0)
+            if h == 0:
+                continue  # the null stream
+            ts = torch.cuda.ExternalStream(h)
         if ts.cuda_stream == torch.cuda.current_stream().cuda_stream:
             continue
         for t in tensors:

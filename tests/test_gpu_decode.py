@@ -279,6 +279,34 @@ def test_decode_step_matches_oracle(msa, name):
     print(f"{name}: max abs {mx:.3e} rel rms {rel:.3e}")
 
 
+@pytest.mark.parametrize("form", ["torch", "int", "ctypes"])
+def test_binding_calls_on_a_side_stream(msa, form):
+    """The binding's route and step on a stream other than the current one,
+    given as a torch stream, an int handle or a ctypes pointer, with the
+    workspace and outputs the binding allocates itself (it records the
+    stream on them, so their memory is not handed out again while the
+    stream still uses it): the same bits as on the current stream."""
+    import ctypes
+    c = decode_case(msa, "decode_small")
+    w, bank = c["w"], c["bank"]
+    ref_ids, ref_sc = bank.route(c["q_route"], w.k)
+    ref = bank.step(c["q"], w.q_pos, w.k, c["k_loc"], c["v_loc"], c["L"], q_route=c["q_route"])
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    s = {"torch": side, "int": side.cuda_stream,
+         "ctypes": ctypes.c_void_p(side.cuda_stream)}[form]
+    for _ in range(3):  # dropped temporaries reallocated while the stream runs
+        ids, sc = bank.route(c["q_route"], w.k, stream=s)
+        got = bank.step(c["q"], w.q_pos, w.k, c["k_loc"], c["v_loc"], c["L"],
+                        q_route=c["q_route"], stream=s)
+        scratch = torch.full((1 << 20,), 7.0, device=DEV)  # on the current stream
+        del scratch
+        side.synchronize()
+        assert torch.equal(ids, ref_ids) and torch.equal(sc, ref_sc)
+        for a, b in zip(got[:3], ref[:3]):
+            assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("h_q,k,n_docs", [(8, 4, 48), (16, 4, 48), (64, 4, 48), (32, 64, 72)])
 def test_decode_gqa_groups_and_max_k(msa, h_q, k, n_docs):
     # one, two and eight query heads per KV head, and the largest k (64
