@@ -514,6 +514,38 @@ def test_interleave_free_running(msa):
         qr = O.interleave_project(ref, M.np64(c["wp"]))
 
 
+@pytest.mark.parametrize("cached", [False, True])
+def test_interleave_on_a_host_resident_bank(msa, tmp_path, cached):
+    """Three interleaved hops on a host-resident copy of the interleave bank
+    (saved, then loaded into pinned host memory): every hop reads its
+    selection back and copies its documents -- into staging, reused from
+    hop to hop, or into a device cache -- before its attention.  Ids,
+    scores and outputs of every hop are bit-identical to the device bank's,
+    with and without exclusion of earlier hops' documents."""
+    c = interleave_case(msa, "interleave_small")
+    w = c["w"]
+    path = str(tmp_path / "interleave_bank.safetensors")
+    msa.save_bank(c["bank"], path)
+    host = msa.load_bank(path, DEV, kv_loc="host")
+    if cached:  # one hop's documents and two more: later hops evict earlier hops' documents
+        host.set_cache(torch.empty((w.B * w.k + 2) * host.cache_slot_bytes(), dtype=torch.uint8,
+                                   device=DEV))
+    args = (c["q"], w.q_pos, w.k, c["k_loc"], c["v_loc"], c["L"])
+    try:
+        for excl in (False, True):
+            kw = dict(q_route=c["q_route"], hops=w.hops, w_proj=c["wp"], exclude_selected=excl)
+            ref = c["bank"].step(*args, **kw)
+            got = host.step(*args, **kw)
+            torch.cuda.synchronize()
+            for name, a, b in zip(("ids", "scores", "out"), got[:3], ref[:3]):
+                assert torch.equal(a, b), f"{name} (exclude_selected={excl})"
+            st = got[3]
+            assert st.docs_copied + st.docs_cached >= w.hops, st
+    finally:
+        if cached:
+            host.set_cache(None)
+
+
 def test_interleave_hop1_equals_single_step(msa):
     """Hop 1 of a multi-hop step is exactly the single-hop step."""
     c = interleave_case(msa, "interleave_small")
