@@ -34,7 +34,8 @@ def run_prefill(msa, w, splits=0):
                                     mode=msa.MSA_PREFILL, block=w.block, splits=splits)
     torch.cuda.synchronize()
     return dict(w=w, r=r, k_raw=k_raw, v_raw=v_raw, q=q, rt=rt, lk=lk, lv=lv, ids=ids[0],
-                scores=scores[0], out=out[0], bank=bank, k_loc=k_loc, v_loc=v_loc)
+                scores=scores[0], out=out[0], bank=bank, k_loc=k_loc, v_loc=v_loc, L=L,
+                q_pos=q_pos)
 
 
 def oracle_block(c, kr_o, inv_o, blk, ids_gpu, queries=None, sel=None):
@@ -117,6 +118,40 @@ def test_prefill_splits_agree(msa):
     for s in (5, 200):
         b = run_prefill(msa, w, splits=s)["out"]
         assert float((a - b).abs().max()) <= 2.0 ** -8 * scale, s
+
+
+@pytest.mark.parametrize("cached", [False, True])
+def test_prefill_on_a_host_resident_bank(msa, tmp_path, cached):
+    """The blocked prefill on a host-resident copy of the bank (saved, then
+    loaded into pinned host memory): the blocks' selections are read back
+    and their documents copied -- into staging, or into a device cache --
+    before the MFMA attention.  Ids, scores and outputs are bit-identical to
+    the device bank's; with a cache, a second step finds every document
+    resident and copies nothing."""
+    w = S.workload("prefill_small")
+    c = run_prefill(msa, w)
+    path = str(tmp_path / "prefill_bank.safetensors")
+    msa.save_bank(c["bank"], path)
+    host = msa.load_bank(path, DEV, kv_loc="host")
+    n_sel = (w.B // w.block) * w.k  # selections of one step
+    if cached:
+        host.set_cache(torch.empty((n_sel + 2) * host.cache_slot_bytes(), dtype=torch.uint8,
+                                   device=DEV))
+    args = (c["q"], c["q_pos"], w.k, c["k_loc"], c["v_loc"], c["L"])
+    kw = dict(route_tokens=c["rt"], mode=msa.MSA_PREFILL, block=w.block)
+    try:
+        for rep in range(2 if cached else 1):
+            ids, scores, out, st = host.step(*args, **kw)
+            torch.cuda.synchronize()
+            assert torch.equal(ids[0], c["ids"]) and torch.equal(scores[0], c["scores"])
+            assert torch.equal(out[0], c["out"]), f"step {rep}"
+            distinct = len(set(c["ids"].cpu().numpy().ravel().tolist()) - {-1})
+            assert st.docs_copied + st.docs_cached == distinct
+            if rep == 1:
+                assert st.docs_copied == 0 and st.docs_cached == distinct
+    finally:
+        if cached:
+            host.set_cache(None)
 
 
 def test_prefill_vector_path_g2(msa):
