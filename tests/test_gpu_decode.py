@@ -307,6 +307,40 @@ def test_binding_calls_on_a_side_stream(msa, form):
             assert torch.equal(a, b)
 
 
+def test_attend_over_a_caller_source(msa):
+    """msa_attend with a source override: the selected documents' K and V
+    blocks copied out of the bank's stores into compact caller-owned arrays
+    (the layout a host-resident bank's staging has), in an order of their
+    own, and the ids remapped to that table: bit-identical to attention
+    over the bank itself."""
+    c = decode_case(msa, "decode_small")
+    w, bank = c["w"], c["bank"]
+    ids, _ = bank.route(c["q_route"], w.k)
+    ref = bank.attend(c["q"], w.q_pos, ids, c["k_loc"], c["v_loc"], c["L"])
+    ids_np = ids.cpu().numpy()
+    docs = sorted(set(ids_np.ravel().tolist()) - {-1}, reverse=True)
+    tok = S.doc_token_offsets(w)
+    per_tok = w.h_kv * 128
+    total = sum(int(w.doc_len[n]) for n in docs)
+    sk = torch.empty(total * per_tok, dtype=w.torch_dtype, device=DEV)
+    sv = torch.empty_like(sk)
+    off, t = [], 0
+    for n in docs:
+        a, m = int(tok[n]) * per_tok, int(w.doc_len[n]) * per_tok
+        sk[t * per_tok:t * per_tok + m] = bank.k_store[a:a + m]
+        sv[t * per_tok:t * per_tok + m] = bank.v_store[a:a + m]
+        off.append(t)
+        t += int(w.doc_len[n])
+    so = torch.tensor(off, dtype=torch.int64, device=DEV)
+    sl = torch.tensor([int(w.doc_len[n]) for n in docs], dtype=torch.int32, device=DEV)
+    slot = {n: i for i, n in enumerate(docs)}
+    ids_c = torch.tensor([[slot.get(int(x), -1) for x in row] for row in ids_np],
+                         dtype=torch.int32, device=DEV)
+    out = bank.attend(c["q"], w.q_pos, ids_c, c["k_loc"], c["v_loc"], c["L"], src=(sk, sv, so, sl))
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
 @pytest.mark.parametrize("h_q,k,n_docs", [(8, 4, 48), (16, 4, 48), (64, 4, 48), (32, 64, 72)])
 def test_decode_gqa_groups_and_max_k(msa, h_q, k, n_docs):
     # one, two and eight query heads per KV head, and the largest k (64
