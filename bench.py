@@ -255,14 +255,18 @@ def prefill_roofline(flops, kv_bytes, att_s):
             "mfma_TFLOPs": tfs, "mfma_frac": tfs / MFMA_PEAK_TFLOPS}
 
 
-def host_bank_bench(steps, warmup, cache_gb=200.0, window=4):
+CACHE_MARGIN_BYTES = 16 << 30  # HBM left free beside an automatically sized document cache
+
+
+def host_bank_bench(steps, warmup, cache_gb=0.0, window=4):
     """The 100M-token host-resident bank (12,207 x 8192 + one 256-token
     document; routing keys in HBM, K/V in pinned host memory backed by 384
     document slots): 8-query decode steps, each reading its selected
     documents' K/V from host memory.  Two runs on one bank: (1) every
     selected document copied into device staging each step; (2) a device
-    document cache of cache_gb with a prefetch window: batch i + window is
-    routed and its documents copied into the cache while batch i steps.
+    document cache of cache_gb (0: all the HBM left free, less a 16 GiB
+    margin) with a prefetch window: batch i + window is routed and its
+    documents copied into the cache while batch i steps.
     Reports queries/s, the host-to-device rate of the copies, a plain pinned
     1 GiB copy's rate in the same run, and the routing scan's HBM rate."""
     import torch
@@ -377,7 +381,15 @@ def host_bank_bench(steps, warmup, cache_gb=200.0, window=4):
     log(f"host bank: staging path, {warmup} + {steps} steps")
     plain = run(warmup, steps, False)
     slot = bank.cache_slot_bytes()
-    slots = int(cache_gb * 1e9) // slot
+    if cache_gb > 0:
+        cache_bytes = int(cache_gb * 1e9)
+    else:  # the HBM left free, less a margin for the leg's own allocations
+        torch.cuda.empty_cache()
+        free, _ = torch.cuda.mem_get_info()
+        cache_bytes = free - CACHE_MARGIN_BYTES
+    slots = min(w.n_docs, max(0, cache_bytes) // slot)
+    if slots < (window + 2) * w.B * w.k:
+        raise RuntimeError(f"host bank: {slots} cache slots cannot hold a {window}-batch window")
     bank.set_cache(torch.empty(slots * slot, dtype=torch.uint8, device=dev))
     # each step routes fresh queries: hits come from the cache holding a share
     # of the bank, so the cache is filled before the timed steps
@@ -491,8 +503,9 @@ def main():
                          "duration); 0 skips it")
     ap.add_argument("--host-bank-steps", type=int, default=8,
                     help="timed steps of each 100M-token host-bank run (0 skips the leg)")
-    ap.add_argument("--host-cache-gb", type=float, default=200.0,
-                    help="device document cache of the host-bank leg's second run, GB")
+    ap.add_argument("--host-cache-gb", type=float, default=0.0,
+                    help="device document cache of the host-bank leg's second run, GB "
+                         "(0: the free HBM less 16 GiB)")
     ap.add_argument("--prefetch-window", type=int, default=4,
                     help="batches routed and prefetched ahead in the cached host-bank run")
     ap.add_argument("--interleave-steps", type=int, default=3,
