@@ -158,7 +158,7 @@ def test_host_bank_cached_prefetch_full_sampled(msa):
     document cache, a 4-batch prefetch window on a side stream, steps on a
     main stream with their copies on a copy stream.  The prefetched steps
     copy nothing; routing of every query and two sampled queries per step
-    against the oracle.  (A 32 GB cache, not the benchmark's 200 GB: the
+    against the oracle.  (A 32 GB cache, not the benchmark's 288 GB: the
     same kernels and host path with fewer slots, which is still room for
     every document of the window and the steps.)"""
     c = host_case(msa)
