@@ -388,9 +388,20 @@ def host_bank_bench(steps, warmup, cache_gb=0.0, window=4):
         free, _ = torch.cuda.mem_get_info()
         cache_bytes = free - CACHE_MARGIN_BYTES
     slots = min(w.n_docs, max(0, cache_bytes) // slot)
-    if slots < (window + 2) * w.B * w.k:
-        raise RuntimeError(f"host bank: {slots} cache slots cannot hold a {window}-batch window")
-    bank.set_cache(torch.empty(slots * slot, dtype=torch.uint8, device=dev))
+    cache = None
+    for _ in range(4):  # an allocation the free-memory figure promised but cannot place
+        if slots < (window + 2) * w.B * w.k:
+            raise RuntimeError(f"host bank: {slots} cache slots cannot hold a {window}-batch window")
+        try:
+            cache = torch.empty(slots * slot, dtype=torch.uint8, device=dev)
+            break
+        except torch.OutOfMemoryError:
+            torch.cuda.empty_cache()
+            slots -= CACHE_MARGIN_BYTES // slot
+    if cache is None:
+        raise RuntimeError("host bank: no room for the document cache")
+    bank.set_cache(cache)
+    del cache
     # each step routes fresh queries: hits come from the cache holding a share
     # of the bank, so the cache is filled before the timed steps
     fill = -(-slots // (w.B * w.k)) + 4
