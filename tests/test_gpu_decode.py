@@ -341,6 +341,35 @@ def test_attend_over_a_caller_source(msa):
     assert torch.equal(out, ref)
 
 
+@pytest.mark.parametrize("name", ["tiny_f32_small", "decode_small"])
+@pytest.mark.parametrize("cached", [False, True])
+def test_host_resident_copy_of_the_bank(msa, tmp_path, name, cached):
+    """A decode step on a host-resident copy of the bank (saved, then loaded
+    into pinned host memory), float32 and bf16 stores: the selected
+    documents are copied (into staging, or into a device cache) and the
+    results are bit-identical to the device bank's."""
+    c = decode_case(msa, name)
+    w = c["w"]
+    path = str(tmp_path / f"{name}.safetensors")
+    msa.save_bank(c["bank"], path)
+    host = msa.load_bank(path, DEV, kv_loc="host")
+    if cached:
+        host.set_cache(torch.empty((w.B * w.k + 1) * host.cache_slot_bytes(), dtype=torch.uint8,
+                                   device=DEV))
+    args = (c["q"], w.q_pos, w.k, c["k_loc"], c["v_loc"], c["L"])
+    try:
+        ref = c["bank"].step(*args, q_route=c["q_route"])
+        got = host.step(*args, q_route=c["q_route"])
+        torch.cuda.synchronize()
+        for name_, a, b in zip(("ids", "scores", "out"), got[:3], ref[:3]):
+            assert torch.equal(a, b), name_
+        distinct = len(set(ref[0].cpu().numpy().ravel().tolist()) - {-1})
+        assert got[3].docs_copied == distinct
+    finally:
+        if cached:
+            host.set_cache(None)
+
+
 @pytest.mark.parametrize("h_q,k,n_docs", [(8, 4, 48), (16, 4, 48), (64, 4, 48), (32, 64, 72)])
 def test_decode_gqa_groups_and_max_k(msa, h_q, k, n_docs):
     # one, two and eight query heads per KV head, and the largest k (64
