@@ -770,9 +770,9 @@ int make_resident(Bank& bk, const std::vector<int32_t>& docs, void* staging, siz
   // Copies into cache slots: K on cs, V on the bank's second copy stream,
   // forked from cs before the first copy (after every wait placed on cs)
   // and joined back into cs after the last.  Copies into staging stay on cs
-  // alone: into staging, two streams measured faster in a process's first
-  // run on a device but slower in later ones (about 95 against 102 queries/s
-  // at 100M tokens), while copies into slots gained in every process.
+  // alone: into staging, two streams measured faster in the first process
+  // to use a device but slower in every later process (about 95 against 102
+  // queries/s at 100M tokens), while copies into slots gained in all of them.
   const bool two = bk.cache != nullptr;
   bool forked = false;
   auto fork = [&]() -> hipError_t {
