@@ -244,6 +244,15 @@ def test_route_exclusion_and_k_equals_n(msa, name):
     ids, scores = c["bank"].route(c["q_route"], N)
     so = oracle_scores(c)
     M.check_topk(ids.cpu().numpy(), scores.cpu().numpy(), so, N)
+    # a query with every document excluded selects nothing; the others are
+    # unaffected
+    words_all = np.zeros_like(words)
+    words_all[0, :] = np.uint32(0xFFFFFFFF)
+    ex_all = torch.from_numpy(words_all.view(np.int32)).to(DEV)
+    ids0, sc0 = c["bank"].route(c["q_route"], w.k)
+    ids, scores = c["bank"].route(c["q_route"], w.k, exclude=ex_all)
+    assert (ids[0] == -1).all() and torch.isinf(scores[0]).all() and (scores[0] < 0).all()
+    assert torch.equal(ids[1:], ids0[1:]) and torch.equal(scores[1:], sc0[1:])
 
 
 def oracle_decode(c, ids_gpu, so):

@@ -5,7 +5,7 @@ beyond).  Routing keys are drawn directly (one
 256-token chunk per document, no K/V needed: every document shares one
 K/V block), so banks just either side of the boundary stay small; the
 selections are checked against the oracle's cosine scores, with exclusion
-masks and the largest k."""
+masks (down to a query that excludes every document) and the largest k."""
 import numpy as np
 import pytest
 import torch
@@ -34,11 +34,13 @@ def test_topk_paths_match_oracle(msa, n_docs, k):
                     kr=kr.permute(1, 0, 2).contiguous())
     bank.build(0, n_docs)  # inverse norms of the given keys
     qr = S.route_queries(w, DEV)
-    # exclusion: query 1 excludes every third document, query 3 all but 70
+    # exclusion: query 1 excludes every third document, query 3 all but 70,
+    # query 4 every document
     W = (n_docs + 31) // 32
     ex = np.zeros((w.B, n_docs), dtype=bool)
     ex[1, ::3] = True
     ex[3, 70:] = True
+    ex[4, :] = True
     words = np.zeros((w.B, W), dtype=np.uint32)
     for b in range(w.B):
         for n in np.nonzero(ex[b])[0]:
@@ -55,3 +57,5 @@ def test_topk_paths_match_oracle(msa, n_docs, k):
         assert not ex[b, ids[b][ids[b] >= 0]].any(), f"query {b} selected an excluded document"
     # query 3 keeps only 70 documents: with k = 64 all of them but 6, else k
     assert (ids[3] >= 0).sum() == min(k, 70)
+    # query 4 keeps none: every slot empty
+    assert (ids[4] == -1).all() and np.isneginf(scores[4]).all()
