@@ -293,7 +293,8 @@ int msa_route(const msa_bank* bank, const float* q_route, int32_t B, int32_t k,
  * hq reads KV head hq / (h_q/h_kv).  Queries are rotated at their global
  * positions.  Decode: each query sees all L_loc local tokens.  Prefill:
  * query i of group g = i / block sees group g's documents and local tokens
- * j <= L_loc - n_q + i (the queries are the last n_q local tokens). */
+ * j <= L_loc - n_q + i (the queries are the last n_q local tokens).  A
+ * query with no key at all (every id slot empty and L_loc = 0) gets 0. */
 int msa_attend(const msa_bank* bank, const msa_attend_args* args, void* stream);
 
 /* Compressed memory (intelliparadigm.com, section 3.1: chunk-mean pooling

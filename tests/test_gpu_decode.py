@@ -519,6 +519,13 @@ def test_decode_local_only_and_docs_only(msa):
         ref = M.oracle_attend_decode(w, q[b], w.q_pos, [n], kv, np.zeros((0, w.h_kv, 128)),
                                      np.zeros((0, w.h_kv, 128)), w.P0)
         M.check_out(out[b].cpu().numpy(), ref, w.dtype, "docs only")
+    # no key at all (every id empty, no local tokens): the output is 0, with
+    # one split and with the most splits
+    ids = torch.full((w.B, 3), -1, dtype=torch.int32, device=DEV)
+    for splits in (4, 256):
+        out = bank.attend(c["q"], w.q_pos, ids, k0, v0, L0, splits=splits)
+        torch.cuda.synchronize()
+        assert torch.equal(out, torch.zeros_like(out)), splits
 
 
 def test_stream_read_probe_reads_every_word(msa):
